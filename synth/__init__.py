@@ -1,0 +1,217 @@
+"""Seeded synthetic inputs for the scaled linear layer.
+
+This module produces the raw byte arrays (bf16/fp16 bit patterns, e4m3 codes,
+int8 values) and fp32 scale arrays that BOTH the HIP library and the CPU oracle
+consume.  It holds none of the layer's arithmetic: it only draws values and
+quantises them into input codes (absmax scaling, saturating round-to-nearest
+casts done by torch's / numpy's CPU casts).
+
+Workloads follow the five problem shapes the library is measured on:
+
+  1  tiny bf16 + GELU          A[64,512]   B[256,512]   bias, GELU(tanh)
+  2  FP8 dynamic decode        A[M,4096]   B[6144,4096] per-token x per-channel, bias
+  3  W8A8 int8 decode          A[M,4096]   B[24576,4096] per-token x per-channel, SiLU
+  4  block-FP8 linear          A[M,12288]  B[4096,12288] 1x128 / 128x128 scales, residual
+  5  prefill decoder block     A[4096,4096] B[4096,4096] bias, GELU(tanh)*0.5 + residual
+
+The (N, K) pairs of 2-4 stand in for the dense-LLM projection shapes that the
+vLLM linear-backend write-up tunes on (its Qwen3 weights and ShareGPT traffic
+are not available); values are Gaussian or uniform stand-ins.
+
+Seeds: numpy PCG64.  Weight-side draws (B, then bias) use seed 1000*cfg so the
+weight is identical across an M sweep; activation-side draws (A, then residual)
+use seed 1000*cfg + M.  Values are drawn in fp32, then quantised or rounded.
+"""
+from dataclasses import dataclass, field
+import functools
+
+import numpy as np
+import torch
+
+E4M3_MAX = 448.0
+INT8_MAX = 127.0
+
+CONFIGS = {
+    1: dict(name="tiny_bf16_gelu", quant="bf16", act="gelu_tanh", N=256, K=512,
+            Ms=(64,), bias=True, residual=False, alpha=1.0, dist="uniform"),
+    2: dict(name="fp8_dynamic_decode", quant="fp8_dynamic", act="none", N=6144, K=4096,
+            Ms=(1, 2, 4, 8, 16, 24, 32), bias=True, residual=False, alpha=1.0, dist="normal"),
+    3: dict(name="w8a8_int8_decode", quant="w8a8_int8", act="silu", N=24576, K=4096,
+            Ms=(1, 2, 4, 8, 16, 24, 32), bias=False, residual=False, alpha=1.0, dist="normal"),
+    4: dict(name="block_fp8", quant="block_fp8", act="none", N=4096, K=12288,
+            Ms=(1, 8, 32, 512, 2048), bias=False, residual=True, alpha=1.0, dist="normal"),
+    5: dict(name="prefill_bf16_fused", quant="bf16", act="gelu_tanh", N=4096, K=4096,
+            Ms=(4096,), bias=True, residual=True, alpha=0.5, dist="normal"),
+}
+
+
+@dataclass
+class Problem:
+    """One layer call's operands, as raw codes (numpy) plus metadata."""
+    quant: str
+    act: str
+    M: int
+    N: int
+    K: int
+    A: np.ndarray                 # [M,K] uint16 (bf16/fp16) | uint8 (e4m3) | int8
+    B: np.ndarray                 # [N,K] same code type
+    sa: np.ndarray = None         # fp32 [M] or [M,K/128]
+    sb: np.ndarray = None         # fp32 [N] or [N/128,K/128]
+    bias: np.ndarray = None       # uint16 [N]
+    residual: np.ndarray = None   # uint16 [M,N]
+    alpha: float = 1.0
+    name: str = ""
+    meta: dict = field(default_factory=dict)
+
+    def operands(self):
+        return dict(A=self.A, B=self.B, sa=self.sa, sb=self.sb, bias=self.bias,
+                    residual=self.residual, alpha=self.alpha)
+
+
+# ------------------------------------------------------------------ casts
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def to_fp16_bits(x: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Saturate to +-448, then round-to-nearest-even to OCP E4M3FN codes."""
+    x = np.clip(np.ascontiguousarray(x, dtype=np.float32), -E4M3_MAX, E4M3_MAX)
+    t = torch.from_numpy(x).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def to_int8_codes(x: np.ndarray) -> np.ndarray:
+    """Round half to even, clamp to [-127, 127] (symmetric)."""
+    return np.clip(np.rint(x), -INT8_MAX, INT8_MAX).astype(np.int8)
+
+
+def _safe_scale(absmax: np.ndarray, qmax: float) -> np.ndarray:
+    s = (absmax / np.float32(qmax)).astype(np.float32)
+    return np.where(absmax > 0, s, np.float32(1.0)).astype(np.float32)
+
+
+# ------------------------------------------------------------ quantisers
+def quant_rows(x: np.ndarray, kind: str):
+    """Per-row (per-token / per-channel) symmetric absmax quantisation."""
+    qmax = E4M3_MAX if kind == "fp8" else INT8_MAX
+    s = _safe_scale(np.abs(x).max(axis=1), qmax)
+    q = x / s[:, None]
+    codes = to_e4m3_codes(q) if kind == "fp8" else to_int8_codes(q)
+    return codes, s
+
+
+def quant_blocks_act(x: np.ndarray):
+    """1x128 blocks along K: scale[M][K/128]."""
+    M, K = x.shape
+    xb = x.reshape(M, K // 128, 128)
+    s = _safe_scale(np.abs(xb).max(axis=2), E4M3_MAX)
+    return to_e4m3_codes((xb / s[:, :, None]).reshape(M, K)), s
+
+
+def quant_blocks_weight(x: np.ndarray):
+    """128x128 blocks: scale[N/128][K/128]."""
+    N, K = x.shape
+    xb = x.reshape(N // 128, 128, K // 128, 128)
+    s = _safe_scale(np.abs(xb).max(axis=(1, 3)), E4M3_MAX)
+    return to_e4m3_codes((xb / s[:, None, :, None]).reshape(N, K)), s
+
+
+def encode(quant: str, x: np.ndarray, side: str):
+    """fp32 values -> (codes, scales) for one operand side ('a' or 'b')."""
+    if quant == "bf16":
+        return to_bf16_bits(x), None
+    if quant == "fp16":
+        return to_fp16_bits(x), None
+    if quant == "fp8_dynamic":
+        return quant_rows(x, "fp8")
+    if quant == "w8a8_int8":
+        return quant_rows(x, "int8")
+    if quant == "block_fp8":
+        return quant_blocks_act(x) if side == "a" else quant_blocks_weight(x)
+    raise ValueError(quant)
+
+
+def encode16(quant: str, x: np.ndarray) -> np.ndarray:
+    """Bias / residual / output codes: fp16 in fp16 mode, else bf16."""
+    return to_fp16_bits(x) if quant == "fp16" else to_bf16_bits(x)
+
+
+# ----------------------------------------------------------------- draws
+def _draw(rng, shape, dist, std):
+    if dist == "uniform":
+        return (rng.random(shape, dtype=np.float32) * 2.0 - 1.0).astype(np.float32)
+    return (rng.standard_normal(shape, dtype=np.float32) * np.float32(std)).astype(np.float32)
+
+
+@functools.lru_cache(maxsize=4)
+def _weight(cfg: int, quant: str):
+    c = CONFIGS[cfg]
+    rng = np.random.Generator(np.random.PCG64(1000 * cfg))
+    w = _draw(rng, (c["N"], c["K"]), c["dist"], 0.02)
+    B, sb = encode(quant, w, "b")
+    del w
+    bias = None
+    if c["bias"]:
+        bias = encode16(quant, (rng.random(c["N"], dtype=np.float32) - np.float32(0.5)))
+    return B, sb, bias
+
+
+def make(cfg: int, M: int = None, quant: str = None) -> Problem:
+    """The seeded problem of workload ``cfg`` at token count ``M``.
+
+    ``quant`` overrides the workload's quant mode (e.g. fp16 instead of bf16)
+    with the same draws.
+    """
+    c = CONFIGS[cfg]
+    M = c["Ms"][0] if M is None else int(M)
+    quant = quant or c["quant"]
+    B, sb, bias = _weight(cfg, quant)
+    rng = np.random.Generator(np.random.PCG64(1000 * cfg + M))
+    a = _draw(rng, (M, c["K"]), c["dist"], 1.0)
+    A, sa = encode(quant, a, "a")
+    residual = None
+    if c["residual"]:
+        residual = encode16(quant, rng.standard_normal((M, c["N"]), dtype=np.float32))
+    return Problem(quant=quant, act=c["act"], M=M, N=c["N"], K=c["K"], A=A, B=B, sa=sa,
+                   sb=sb, bias=bias, residual=residual, alpha=c["alpha"],
+                   name=f"{c['name']}_M{M}", meta=dict(cfg=cfg))
+
+
+def make_custom(quant: str, act: str, M: int, N: int, K: int, seed: int, bias=True,
+                residual=False, alpha=1.0, dist="normal", wstd=0.02) -> Problem:
+    """A seeded problem of arbitrary shape (edge cases, ragged tails)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w = _draw(rng, (N, K), dist, wstd)
+    B, sb = encode(quant, w, "b")
+    bias_c = encode16(quant, rng.random(N, dtype=np.float32) - np.float32(0.5)) if bias else None
+    a = _draw(rng, (M, K), dist, 1.0)
+    A, sa = encode(quant, a, "a")
+    res_c = encode16(quant, rng.standard_normal((M, N), dtype=np.float32)) if residual else None
+    return Problem(quant=quant, act=act, M=M, N=N, K=K, A=A, B=B, sa=sa, sb=sb, bias=bias_c,
+                   residual=res_c, alpha=alpha, name=f"{quant}_{act}_{M}x{N}x{K}_s{seed}")
+
+
+def algorithmic_bytes(quant: str, M: int, N: int, K: int, bias: bool, residual: bool) -> int:
+    """Compulsory HBM bytes of one fused call: operands, scales, bias,
+    residual and the one output write."""
+    e = 2 if quant in ("bf16", "fp16") else 1
+    b = M * K * e + N * K * e
+    if quant in ("fp8_dynamic", "w8a8_int8"):
+        b += 4 * M + 4 * N
+    elif quant == "block_fp8":
+        b += 4 * M * (K // 128) + 4 * (N // 128) * (K // 128)
+    if bias:
+        b += 2 * N
+    if residual:
+        b += 2 * M * N
+    b += 2 * M * N
+    return b
+
+
+def flops(M: int, N: int, K: int) -> int:
+    return 2 * M * N * K

@@ -1,0 +1,24 @@
+"""Shared pytest setup: markers, repo root on sys.path, oracle build."""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: large CPU oracle runs")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _oracle_built():
+    # The oracle is test infrastructure; build it once if nothing is built.
+    import oracle
+    if not os.path.exists(oracle.LIB_PATH):
+        from oracle import build
+        build.build()
+    yield
