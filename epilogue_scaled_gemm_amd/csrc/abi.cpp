@@ -1,0 +1,334 @@
+// abi.cpp -- the extern "C" entry points declared in include/lin_gemm.h.
+//
+// lin_gemm_run plays the part of the custom-op wrapper in the
+// TorchInductor-integration section of "Совместная работа Helion и
+// TorchInductor: слияние операторов" (check the inner dimension, pick the
+// launch shape, launch one kernel), with the per-shape variant choice of
+// "helion-vllm-linear-backend" (sections "Одно ядро вместо трёх вариантов"
+// and "Гибридный диспатч").  Argument checks happen here, on the host, before
+// anything is enqueued; kernels never see a shape they were not built for.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <sstream>
+#include <string>
+#include <vector>
+
+#include "../../include/lin_gemm.h"
+#include "dispatch.hpp"
+#include "launch.hpp"
+
+struct lin_gemm_ctx {
+  std::vector<lg::TableEntry> table;
+  bool forced = false;
+  lg::Variant force;
+  std::string last_error;
+  void* ws = nullptr;         // split-K workspace
+  size_t ws_bytes = 0;
+  bool ws_zero = true;        // workspace all zero (needed by the atomic reduction)
+  int* counters = nullptr;    // per-16-row-group arrival counters (kept at zero between calls)
+  size_t counters_n = 0;
+};
+
+namespace {
+
+int fail(lin_gemm_t h, int status, const std::string& msg) {
+  if (h) h->last_error = msg;
+  return status;
+}
+
+int hip_fail(lin_gemm_t h, hipError_t e, const char* what) {
+  return fail(h, LIN_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int esize(int quant) { return (quant == LIN_Q_BF16 || quant == LIN_Q_FP16) ? 2 : 1; }
+
+int qkind(int quant) {
+  switch (quant) {
+    case LIN_Q_BF16: return lg::QK_BF16;
+    case LIN_Q_FP16: return lg::QK_FP16;
+    case LIN_Q_FP8_DYNAMIC: return lg::QK_FP8;
+    case LIN_Q_W8A8_INT8: return lg::QK_I8;
+    case LIN_Q_BLOCK_FP8: return lg::QK_FP8_BLOCK;
+  }
+  return -1;
+}
+
+bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
+// Shape / pointer checks shared by the fused and unfused entry points.
+int check_shape(lin_gemm_t h, int quant, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return fail(h, LIN_ERR_INVALID_ARG, "negative size");
+  if (quant < LIN_Q_BF16 || quant > LIN_Q_BLOCK_FP8)
+    return fail(h, LIN_ERR_INVALID_ARG, "unknown quant mode " + std::to_string(quant));
+  if (M == 0) return LIN_OK;
+  if (N < 1 || K < 1) return fail(h, LIN_ERR_UNSUPPORTED, "N and K must be >= 1");
+  if ((K * esize(quant)) % 16 != 0)
+    return fail(h, LIN_ERR_UNSUPPORTED, "rows of A and B must be a multiple of 16 bytes "
+                                        "(K % 8 for bf16/fp16, K % 16 for e4m3/int8)");
+  if (quant == LIN_Q_BLOCK_FP8 && (K % 128 != 0 || N % 128 != 0))
+    return fail(h, LIN_ERR_UNSUPPORTED, "block FP8 needs K % 128 == 0 and N % 128 == 0");
+  if (quant == LIN_Q_W8A8_INT8 && K > 131071)
+    return fail(h, LIN_ERR_UNSUPPORTED, "int8 needs K <= 131071 (int32 accumulator range)");
+  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31 || K > (int64_t)1 << 31)
+    return fail(h, LIN_ERR_UNSUPPORTED, "sizes beyond 2^31");
+  return LIN_OK;
+}
+
+int select_variant(lin_gemm_t h, int quant, int64_t M, int64_t N, int64_t K, lg::Variant* v) {
+  if (h->forced) {
+    *v = h->force;
+  } else if (!lg::lookup(h->table, quant, M, N, K, v)) {
+    // No entry: the built-in rule.
+    lg::Variant d;
+    if (M <= 32) { d.kind = lg::V_DECODE; }
+    else { d.kind = lg::V_TILE; d.bm = 128; d.bn = 128; d.wm = 2; d.wn = 2; }
+    *v = d;
+  }
+  if (v->kind == lg::V_DECODE && M > 32) {
+    if (h->forced) return fail(h, LIN_ERR_UNSUPPORTED, "decode variants need M <= 32");
+    v->kind = lg::V_TILE; v->bm = 128; v->bn = 128; v->wm = 2; v->wn = 2;
+  }
+  return LIN_OK;
+}
+
+int resolve_split(const lg::Variant& v, const lg::Call& c) {
+  if (v.kind != lg::V_DECODE) return 1;
+  int split = v.split > 0 ? v.split : lg::decode_auto_split(c, v.waves);
+  const int64_t steps = (c.KB + 127) / 128;
+  while (split > 1 && split > steps) split >>= 1;  // at least one 128-byte step per slice
+  return split;
+}
+
+// Make sure the workspace and counters cover this call.
+int ensure_workspace(lin_gemm_t h, const lg::Variant& v, const lg::Call& c, int split,
+                     hipStream_t s) {
+  const size_t need = lg::decode_ws_bytes(v, c, split);
+  const size_t ncnt = (size_t)((c.N + 15) / 16);
+  const bool grow_ws = need > h->ws_bytes;
+  const bool grow_cnt = split > 1 && ncnt > h->counters_n;
+  if (grow_ws || grow_cnt) {
+    hipError_t e = hipStreamSynchronize(s);  // in-flight calls may still use the old buffers
+    if (e != hipSuccess) return hip_fail(h, e, "hipStreamSynchronize");
+  }
+  if (grow_ws) {
+    if (h->ws) hipFree(h->ws);
+    h->ws = nullptr;
+    h->ws_bytes = 0;
+    size_t bytes = (need + 255) & ~(size_t)255;
+    if (hipMalloc(&h->ws, bytes) != hipSuccess) {
+      h->ws = nullptr;
+      return fail(h, LIN_ERR_OOM, "split-K workspace allocation of " + std::to_string(bytes) + " bytes failed");
+    }
+    h->ws_bytes = bytes;
+    hipError_t e = lg::launch_fill_zero(h->ws, bytes, s);
+    if (e != hipSuccess) return hip_fail(h, e, "workspace zero fill");
+    h->ws_zero = true;
+  }
+  if (grow_cnt) {
+    if (h->counters) hipFree(h->counters);
+    h->counters = nullptr;
+    h->counters_n = 0;
+    size_t n = (ncnt + 63) & ~(size_t)63;
+    if (hipMalloc(&h->counters, n * sizeof(int)) != hipSuccess) {
+      h->counters = nullptr;
+      return fail(h, LIN_ERR_OOM, "split-K counter allocation failed");
+    }
+    h->counters_n = n;
+    hipError_t e = lg::launch_fill_zero(h->counters, n * sizeof(int), s);
+    if (e != hipSuccess) return hip_fail(h, e, "counter zero fill");
+  }
+  if (split > 1) {
+    // The atomic reduction needs a zero accumulator; the others leave
+    // partials behind, so zero again when switching to atomic.
+    if (v.reduce == lg::R_ATOMIC && !h->ws_zero) {
+      hipError_t e = lg::launch_fill_zero(h->ws, h->ws_bytes, s);
+      if (e != hipSuccess) return hip_fail(h, e, "workspace zero fill");
+    }
+    h->ws_zero = (v.reduce == lg::R_ATOMIC);
+  }
+  return LIN_OK;
+}
+
+lg::Epi make_epi(const lin_scales_t* scales, const void* bias, const void* residual, void* C,
+                 int64_t M, int64_t N, int quant, int act) {
+  lg::Epi e;
+  e.sa = scales ? scales->a : nullptr;
+  e.sb = scales ? scales->b : nullptr;
+  e.bias = (const uint16_t*)bias;
+  e.residual = (const uint16_t*)residual;
+  e.C = C;
+  e.alpha = scales ? scales->alpha : 1.0f;
+  e.raw = act == LIN_ACT_RAW_ACC;
+  e.act = e.raw ? 0 : act;
+  e.scale_mode = (quant == LIN_Q_FP8_DYNAMIC || quant == LIN_Q_W8A8_INT8) && !e.raw ? 1 : 0;
+  e.M = M;
+  e.N = N;
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lin_gemm_create(lin_gemm_t* out, const char* config_path) {
+  if (!out) return LIN_ERR_INVALID_ARG;
+  *out = nullptr;
+  lin_gemm_ctx* h = new (std::nothrow) lin_gemm_ctx();
+  if (!h) return LIN_ERR_OOM;
+  std::string text = lg::builtin_table();
+  const char* path = config_path;
+  if (!path) path = std::getenv("LIN_GEMM_CONFIG");
+  if (path && *path) {
+    std::ifstream f(path);
+    if (!f) { delete h; return LIN_ERR_CONFIG; }
+    std::stringstream ss;
+    ss << f.rdbuf();
+    text = ss.str();
+  }
+  std::string err;
+  if (!lg::parse_table(text, &h->table, &err)) {
+    std::fprintf(stderr, "lin_gemm: variant table: %s\n", err.c_str());
+    delete h;
+    return LIN_ERR_CONFIG;
+  }
+  *out = h;
+  return LIN_OK;
+}
+
+int lin_gemm_destroy(lin_gemm_t h) {
+  if (!h) return LIN_OK;
+  if (h->ws) hipFree(h->ws);
+  if (h->counters) hipFree(h->counters);
+  delete h;
+  return LIN_OK;
+}
+
+const char* lin_gemm_strerror(int status) {
+  switch (status) {
+    case LIN_OK: return "ok";
+    case LIN_ERR_INVALID_ARG: return "invalid argument";
+    case LIN_ERR_UNSUPPORTED: return "unsupported shape or mode";
+    case LIN_ERR_HIP: return "HIP runtime error";
+    case LIN_ERR_OOM: return "out of device memory";
+    case LIN_ERR_CONFIG: return "bad variant table or spec";
+  }
+  return "unknown status";
+}
+
+const char* lin_gemm_last_error(lin_gemm_t h) { return h ? h->last_error.c_str() : ""; }
+
+int lin_gemm_set_force(lin_gemm_t h, const char* spec) {
+  if (!h) return LIN_ERR_INVALID_ARG;
+  if (!spec || !*spec) { h->forced = false; return LIN_OK; }
+  lg::Variant v;
+  std::string err;
+  if (!lg::parse_variant(spec, &v, &err)) return fail(h, LIN_ERR_CONFIG, err);
+  h->force = v;
+  h->forced = true;
+  return LIN_OK;
+}
+
+int lin_gemm_describe(lin_gemm_t h, int quant_mode, int64_t M, int64_t N, int64_t K, char* buf,
+                      int buflen) {
+  if (!h || !buf || buflen < 1) return LIN_ERR_INVALID_ARG;
+  int rc = check_shape(h, quant_mode, M, N, K);
+  if (rc != LIN_OK) return rc;
+  lg::Variant v;
+  rc = select_variant(h, quant_mode, M, N, K, &v);
+  if (rc != LIN_OK) return rc;
+  lg::Call c{};
+  c.M = M; c.N = N; c.K = K; c.KB = K * esize(quant_mode);
+  std::string s = lg::format_variant(v, resolve_split(v, c));
+  std::snprintf(buf, (size_t)buflen, "%s", s.c_str());
+  return LIN_OK;
+}
+
+int lin_gemm_run(lin_gemm_t h, const void* A, const void* B, const lin_scales_t* scales,
+                 const void* bias, const void* residual, void* C, int64_t M, int64_t N, int64_t K,
+                 int quant_mode, int activation, void* stream) {
+  if (!h) return LIN_ERR_INVALID_ARG;
+  h->last_error.clear();
+  int rc = check_shape(h, quant_mode, M, N, K);
+  if (rc != LIN_OK || M == 0) return rc;
+  if (!A || !B || !C) return fail(h, LIN_ERR_INVALID_ARG, "A, B and C must be non-null");
+  if (!(activation >= LIN_ACT_NONE && activation <= LIN_ACT_SILU) && activation != LIN_ACT_RAW_ACC)
+    return fail(h, LIN_ERR_INVALID_ARG, "unknown activation " + std::to_string(activation));
+  const bool quantised = quant_mode >= LIN_Q_FP8_DYNAMIC;
+  if (quantised && (!scales || !scales->a || !scales->b))
+    return fail(h, LIN_ERR_INVALID_ARG, "quantised modes need scales->a and scales->b");
+  if (misaligned(A) || misaligned(B) || misaligned(C) || misaligned(bias) || misaligned(residual))
+    return fail(h, LIN_ERR_UNSUPPORTED, "A, B, C, bias and residual must be 16-byte aligned");
+  if (scales && (misaligned(scales->a) || misaligned(scales->b)))
+    return fail(h, LIN_ERR_UNSUPPORTED, "scale arrays must be 16-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  lg::Call c{};
+  c.A = A; c.B = B; c.M = M; c.N = N; c.K = K;
+  c.KB = K * esize(quant_mode);
+  c.qk = qkind(quant_mode);
+  c.epi = make_epi(scales, bias, residual, C, M, N, quant_mode, activation);
+
+  lg::Variant v;
+  rc = select_variant(h, quant_mode, M, N, K, &v);
+  if (rc != LIN_OK) return rc;
+  hipError_t e;
+  if (v.kind == lg::V_TILE) {
+    e = lg::launch_tile(v, c, s);
+  } else {
+    const int split = resolve_split(v, c);
+    rc = ensure_workspace(h, v, c, split, s);
+    if (rc != LIN_OK) return rc;
+    c.ws = h->ws;
+    c.counters = h->counters;
+    e = lg::launch_decode(v, c, split, s);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
+  if (std::getenv("LIN_GEMM_LOG")) {
+    lg::Call cc = c;
+    std::fprintf(stderr, "lin_gemm: quant=%d M=%lld N=%lld K=%lld -> %s\n", quant_mode,
+                 (long long)M, (long long)N, (long long)K,
+                 lg::format_variant(v, resolve_split(v, cc)).c_str());
+  }
+  return LIN_OK;
+}
+
+int lin_gemm_run_unfused(lin_gemm_t h, const void* A, const void* B, const void* bias,
+                         const void* residual, void* C, void* T, void* U, int64_t M, int64_t N,
+                         int64_t K, float alpha, int quant_mode, int activation, void* stream) {
+  if (!h) return LIN_ERR_INVALID_ARG;
+  h->last_error.clear();
+  if (quant_mode != LIN_Q_BF16 && quant_mode != LIN_Q_FP16)
+    return fail(h, LIN_ERR_UNSUPPORTED, "the unfused path is bf16 / fp16 only");
+  int rc = check_shape(h, quant_mode, M, N, K);
+  if (rc != LIN_OK || M == 0) return rc;
+  if (!A || !B || !C || !T || !U) return fail(h, LIN_ERR_INVALID_ARG, "null pointer");
+  if (activation < LIN_ACT_NONE || activation > LIN_ACT_SILU)
+    return fail(h, LIN_ERR_INVALID_ARG, "unknown activation " + std::to_string(activation));
+  if (misaligned(A) || misaligned(B) || misaligned(C) || misaligned(T) || misaligned(U) ||
+      misaligned(bias) || misaligned(residual))
+    return fail(h, LIN_ERR_UNSUPPORTED, "buffers must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const bool f16 = quant_mode == LIN_Q_FP16;
+  lg::Call c{};
+  c.A = A; c.B = B; c.M = M; c.N = N; c.K = K;
+  c.KB = K * 2;
+  c.qk = qkind(quant_mode);
+  c.epi = make_epi(nullptr, nullptr, nullptr, T, M, N, quant_mode, LIN_ACT_NONE);
+  lg::Variant v;
+  rc = select_variant(h, quant_mode, M, N, K, &v);
+  if (rc != LIN_OK) return rc;
+  if (v.kind != lg::V_TILE) { v = lg::Variant(); v.kind = lg::V_TILE; }
+  hipError_t e = lg::launch_tile(v, c, s);
+  if (e != hipSuccess) return hip_fail(h, e, "GEMM launch");
+  e = lg::launch_bias_act(T, bias, U, M, N, activation, f16, s);
+  if (e != hipSuccess) return hip_fail(h, e, "bias+activation launch");
+  e = lg::launch_scale_residual(U, residual, C, M, N, alpha, f16, s);
+  if (e != hipSuccess) return hip_fail(h, e, "scale+residual launch");
+  return LIN_OK;
+}
+
+}  // extern "C"

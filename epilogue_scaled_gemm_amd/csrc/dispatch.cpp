@@ -1,0 +1,174 @@
+// dispatch.cpp -- parser and lookup for the shape-keyed variant table.
+#include "dispatch.hpp"
+
+#include <cstdlib>
+#include <sstream>
+
+namespace lg {
+
+namespace {
+
+const char* kQuantNames[] = {"bf16", "fp16", "fp8_dynamic", "w8a8_int8", "block_fp8"};
+
+int quant_of(const std::string& s) {
+  if (s == "*") return -1;
+  for (int i = 0; i < 5; ++i)
+    if (s == kQuantNames[i]) return i;
+  return -2;
+}
+
+bool to_ll(const std::string& s, long long* v) {
+  if (s == "*") { *v = -1; return true; }
+  char* end = nullptr;
+  long long x = std::strtoll(s.c_str(), &end, 10);
+  if (!end || *end != '\0' || s.empty()) return false;
+  *v = x;
+  return true;
+}
+
+const char* reduce_name(int r) {
+  switch (r) {
+    case R_LASTWG: return "lastwg";
+    case R_ATOMIC: return "atomic";
+    case R_TWOPASS: return "twopass";
+  }
+  return "none";
+}
+
+}  // namespace
+
+bool parse_variant(const std::string& spec, Variant* out, std::string* err) {
+  std::istringstream is(spec);
+  std::string kind;
+  if (!(is >> kind)) { *err = "empty variant spec"; return false; }
+  Variant v;
+  if (kind == "tile") v.kind = V_TILE;
+  else if (kind == "decode") v.kind = V_DECODE;
+  else { *err = "unknown variant kind '" + kind + "'"; return false; }
+  std::string kv;
+  while (is >> kv) {
+    size_t eq = kv.find('=');
+    if (eq == std::string::npos) { *err = "expected key=value, got '" + kv + "'"; return false; }
+    std::string k = kv.substr(0, eq), val = kv.substr(eq + 1);
+    if (k == "reduce") {
+      if (val == "lastwg") v.reduce = R_LASTWG;
+      else if (val == "atomic") v.reduce = R_ATOMIC;
+      else if (val == "twopass") v.reduce = R_TWOPASS;
+      else if (val == "none") v.reduce = R_NONE;
+      else { *err = "unknown reduce '" + val + "'"; return false; }
+      continue;
+    }
+    long long x;
+    if (!to_ll(val, &x) || x < 0) { *err = "bad value in '" + kv + "'"; return false; }
+    int xi = (int)x;
+    if (k == "bm") v.bm = xi;
+    else if (k == "bn") v.bn = xi;
+    else if (k == "wm") v.wm = xi;
+    else if (k == "wn") v.wn = xi;
+    else if (k == "group") v.group_m = xi;
+    else if (k == "swap") v.swap = xi ? 1 : 0;
+    else if (k == "split") v.split = xi;
+    else if (k == "waves") v.waves = xi;
+    else if (k == "unroll") v.unroll = xi;
+    else { *err = "unknown key '" + k + "'"; return false; }
+  }
+  if (v.kind == V_TILE && !tile_supported(0, v.bm, v.bn, v.wm, v.wn)) {
+    *err = "tile shape not compiled: " + spec;
+    return false;
+  }
+  if (v.kind == V_DECODE) {
+    if (!decode_supported(0, 1, v.swap, v.waves, v.unroll)) {
+      *err = "decode waves/unroll not compiled: " + spec;
+      return false;
+    }
+    if (v.split > 256 || (v.split & (v.split - 1)) != 0) {
+      *err = "split must be 0 (auto) or a power of two <= 256: " + spec;
+      return false;
+    }
+  }
+  *out = v;
+  return true;
+}
+
+std::string format_variant(const Variant& v, int split) {
+  std::ostringstream os;
+  if (v.kind == V_TILE) {
+    os << "tile bm=" << v.bm << " bn=" << v.bn << " wm=" << v.wm << " wn=" << v.wn
+       << " group=" << v.group_m;
+  } else {
+    os << "decode swap=" << v.swap << " split=" << split << " reduce=" << reduce_name(v.reduce)
+       << " waves=" << v.waves << " unroll=" << v.unroll;
+  }
+  return os.str();
+}
+
+bool parse_table(const std::string& text, std::vector<TableEntry>* out, std::string* err) {
+  std::istringstream is(text);
+  std::string line;
+  int lineno = 0;
+  std::vector<TableEntry> t;
+  while (std::getline(is, line)) {
+    ++lineno;
+    size_t hash = line.find('#');
+    if (hash != std::string::npos) line = line.substr(0, hash);
+    std::istringstream ls(line);
+    std::string q, mlo, mhi, n, k;
+    if (!(ls >> q)) continue;  // blank
+    if (!(ls >> mlo >> mhi >> n >> k)) {
+      *err = "line " + std::to_string(lineno) + ": expected <quant> <m_lo> <m_hi> <N> <K> <variant>";
+      return false;
+    }
+    TableEntry e;
+    e.quant = quant_of(q);
+    if (e.quant == -2) { *err = "line " + std::to_string(lineno) + ": unknown quant '" + q + "'"; return false; }
+    if (!to_ll(mlo, &e.m_lo) || e.m_lo < 0 || !to_ll(mhi, &e.m_hi) || !to_ll(n, &e.n) ||
+        !to_ll(k, &e.k)) {
+      *err = "line " + std::to_string(lineno) + ": bad number";
+      return false;
+    }
+    std::string rest, tok;
+    while (ls >> tok) rest += (rest.empty() ? "" : " ") + tok;
+    std::string verr;
+    if (!parse_variant(rest, &e.v, &verr)) {
+      *err = "line " + std::to_string(lineno) + ": " + verr;
+      return false;
+    }
+    if (e.v.kind == V_DECODE && (e.m_hi < 0 || e.m_hi > 32)) {
+      *err = "line " + std::to_string(lineno) + ": decode entries must have m_hi <= 32";
+      return false;
+    }
+    t.push_back(e);
+  }
+  *out = std::move(t);
+  return true;
+}
+
+// Built-in default: decode family for up to 32 tokens (swap-AB, split-K
+// chosen from the shape, last-arrival reduction), then tile sizes growing
+// with M.  Tuned entries for the measured shapes come first.
+const char* builtin_table() {
+  return R"TABLE(
+# quant        m_lo m_hi N     K      variant
+*              1    32   *     *      decode swap=1 split=0 reduce=lastwg waves=4 unroll=4
+block_fp8      33   *    *     *      tile bm=128 bn=128 wm=2 wn=2 group=4
+*              33   256  *     *      tile bm=64 bn=128 wm=1 wn=4 group=4
+*              257  1024 *     *      tile bm=128 bn=128 wm=2 wn=2 group=4
+*              1025 *    *     *      tile bm=256 bn=128 wm=2 wn=2 group=4
+)TABLE";
+}
+
+bool lookup(const std::vector<TableEntry>& t, int quant, long long M, long long N, long long K,
+            Variant* out) {
+  for (const TableEntry& e : t) {
+    if (e.quant >= 0 && e.quant != quant) continue;
+    if (M < e.m_lo) continue;
+    if (e.m_hi >= 0 && M > e.m_hi) continue;
+    if (e.n >= 0 && e.n != N) continue;
+    if (e.k >= 0 && e.k != K) continue;
+    *out = e.v;
+    return true;
+  }
+  return false;
+}
+
+}  // namespace lg

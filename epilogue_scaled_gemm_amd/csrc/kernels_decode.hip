@@ -1,0 +1,351 @@
+// kernels_decode.hip -- small-M (decode) family: M <= 32 tokens against a
+// large weight, which is streamed from HBM exactly once.
+//
+// The variants are the two of "helion-vllm-linear-backend" (section "Зачем
+// трогать линейные слои"): split-K -- K divided among several workgroups /
+// waves to add parallelism when M and N cannot fill the GPU -- and swap-AB
+// -- computing (B A^T)^T so that the wide weight dimension takes the tiled
+// side; plus the scale formats of its section "Одно ядро вместо трёх
+// вариантов".  The variant per shape comes from a table (its sections "Одно
+// ядро вместо трёх вариантов" and "Гибридный диспатч").
+//
+// gfx950 design:
+//  * A workgroup owns 16 weight rows (one MFMA tile) and a slice of K; its W
+//    waves split that slice in 128-byte steps (in-workgroup split-K), so each
+//    weight byte is loaded by exactly one lane, straight from HBM into
+//    registers (no LDS staging: there is no reuse to stage for).  Every lane
+//    loads 32 contiguous bytes per step; 4 lanes cover a 128-byte line.
+//  * Loads run one batch of U steps ahead of the MFMAs (register double
+//    buffering), so a wave keeps U * 2 KiB of weight in flight.
+//  * swap = 1 puts the weight on the MFMA row side (tokens are columns): each
+//    lane ends with 4 consecutive output columns of one token (8-byte
+//    stores).  swap = 0 puts tokens on the row side (the direct A*B^T form).
+//  * Tokens past M re-read token M-1 and their outputs are dropped; tokens
+//    use one or two 16-column MFMA tiles (M <= 16 or M <= 32).
+//  * Partial sums of the W waves are reduced in LDS in a fixed order.  With
+//    split > 1 workgroups per row group the cross-workgroup reduction is one
+//    of: lastwg (each writes its partial to workspace [split][M][N]; the last
+//    to arrive on a per-group counter sums them in slice order, runs the
+//    epilogue and resets the counter), atomic (atomic adds into a zeroed
+//    [M][N] accumulator; the last arrival runs the epilogue and re-zeroes
+//    it; exact for int32, order-dependent rounding for fp32) or twopass
+//    (partials, then splitk_reduce sums them in slice order).  The nonlinear
+//    epilogue always runs on the complete sum.
+#include "launch.hpp"
+
+namespace lg {
+namespace {
+
+constexpr int STEPB = 128;  // bytes of K per step
+
+template <typename T> __device__ inline T ld_agent(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T> __device__ inline void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline i32x4 ld16(const uint8_t* p, bool ok) {
+  return ok ? *(const i32x4*)p : i32x4{0, 0, 0, 0};
+}
+__device__ inline i32x8 cat(i32x4 a, i32x4 b) {
+  return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+template <int QK, int NTT, bool SWAP, int W, int U>
+__global__ __launch_bounds__(W * 64) void decode_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int64_t M, int64_t N,
+    int64_t KB, int split, int steps_per_split, int reduce, Epi e, void* __restrict__ ws,
+    int* __restrict__ counters) {
+  using MF = Mfma<QK>;
+  using C = typename MF::C;
+  using AccT = typename QTraits<QK>::Acc;
+  constexpr bool F16 = QTraits<QK>::out_f16;
+  constexpr bool BLOCK = (QK == QK_FP8_BLOCK);
+  constexpr int NS = SWAP ? 1 : 4;  // block scales per token tile per lane
+  __shared__ AccT red[W][NTT * 4][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int sidx = blockIdx.y;
+  const int total_steps = (int)((KB + STEPB - 1) / STEPB);
+  const int beg = sidx * steps_per_split;
+  const int end = min(beg + steps_per_split, total_steps);
+  const int span = end - beg;
+  const int my = span > wave ? (span - wave + W - 1) / W : 0;  // steps of this wave
+
+  const uint8_t* wp = B + min(n0 + l16, N - 1) * KB + g * 32;
+  const uint8_t* xp[NTT];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) xp[tt] = A + min((int64_t)(tt * 16 + l16), M - 1) * KB + g * 32;
+
+  // Block scales: sb[n0/128][kb] is uniform over the workgroup; sa[tok][kb]
+  // per lane (one token per tile with swap, four without).
+  const int64_t KBLK = KB / 128;
+  const float* sa_p[NTT][NS];
+  const float* sb_p = nullptr;
+  if constexpr (BLOCK) {
+    sb_p = e.sb + (n0 / 128) * KBLK;
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int r = 0; r < NS; ++r) {
+        const int64_t tok = SWAP ? (tt * 16 + l16) : (tt * 16 + g * 4 + r);
+        sa_p[tt][r] = e.sa + min(tok, M - 1) * KBLK;
+      }
+  }
+
+  i32x8 wcur[U], xcur[U][NTT], wnxt[U], xnxt[U][NTT];
+  float scur[U][NTT][NS], snxt[U][NTT][NS];
+  auto load_batch = [&](int t0, i32x8* w, i32x8 (*x)[NTT], float (*sc)[NTT][NS]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u;
+      const bool live = t < my;
+      const int st = beg + wave + t * W;
+      const int64_t off = (int64_t)st * STEPB;
+      const bool ok0 = live && (off + g * 32 < KB);
+      const bool ok1 = live && (off + g * 32 + 16 < KB);
+      w[u] = cat(ld16(wp + off, ok0), ld16(wp + off + 16, ok1));
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt)
+        x[u][tt] = cat(ld16(xp[tt] + off, ok0), ld16(xp[tt] + off + 16, ok1));
+      if constexpr (BLOCK) {
+        const float sbv = live ? sb_p[st] : 0.f;
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+          for (int r = 0; r < NS; ++r) sc[u][tt][r] = live ? sa_p[tt][r][st] * sbv : 0.f;
+      }
+    }
+  };
+
+  C acc[NTT];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) acc[tt] = C{0, 0, 0, 0};
+
+  load_batch(0, wcur, xcur, scur);
+  for (int t0 = 0; t0 < my; t0 += U) {
+    if (t0 + U < my) load_batch(t0 + U, wnxt, xnxt, snxt);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const typename MF::Frag w0 = MF::prep(lo16(wcur[u])), w1 = MF::prep(hi16(wcur[u]));
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) {
+        const typename MF::Frag x0 = MF::prep(lo16(xcur[u][tt])), x1 = MF::prep(hi16(xcur[u][tt]));
+        if constexpr (BLOCK) {
+          // One step is one 128-wide K block: scale its exact partial sum.
+          C p = SWAP ? MF::mma(w0, x0, C{0, 0, 0, 0}) : MF::mma(x0, w0, C{0, 0, 0, 0});
+          p = SWAP ? MF::mma(w1, x1, p) : MF::mma(x1, w1, p);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[tt][r] += scur[u][tt][SWAP ? 0 : r] * p[r];
+        } else {
+          acc[tt] = SWAP ? MF::mma(w0, x0, acc[tt]) : MF::mma(x0, w0, acc[tt]);
+          acc[tt] = SWAP ? MF::mma(w1, x1, acc[tt]) : MF::mma(x1, w1, acc[tt]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      wcur[u] = wnxt[u];
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) {
+        xcur[u][tt] = xnxt[u][tt];
+        if constexpr (BLOCK) {
+#pragma unroll
+          for (int r = 0; r < NS; ++r) scur[u][tt][r] = snxt[u][tt][r];
+        }
+      }
+    }
+  }
+
+  // In-workgroup reduction of the W waves' partial tiles, in wave order.
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][tt * 4 + r][lane] = (AccT)acc[tt][r];
+  __syncthreads();
+  if (wave != 0) return;
+  AccT v[NTT * 4];
+#pragma unroll
+  for (int i = 0; i < NTT * 4; ++i) {
+    AccT s = red[0][i][lane];
+#pragma unroll
+    for (int w = 1; w < W; ++w) s += red[w][i][lane];
+    v[i] = s;
+  }
+
+  // Output coordinates of v[tt*4 + r].
+  auto coord = [&](int tt, int r, int64_t& m, int64_t& n) {
+    if (SWAP) { m = tt * 16 + l16; n = n0 + g * 4 + r; }
+    else { m = tt * 16 + g * 4 + r; n = n0 + l16; }
+  };
+  auto finish = [&]() {
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+      if (SWAP) {
+        epilogue_run<4, F16>(e, tt * 16 + l16, n0 + g * 4, &v[tt * 4]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int64_t m, n;
+          coord(tt, r, m, n);
+          epilogue_one<F16>(e, m, n, v[tt * 4 + r]);
+        }
+      }
+    }
+  };
+
+  if (split == 1) {
+    finish();
+    return;
+  }
+
+  AccT* wsa = (AccT*)ws;
+  if (reduce == R_ATOMIC) {
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int64_t m, n;
+        coord(tt, r, m, n);
+        if (m < M && n < N)
+          __hip_atomic_fetch_add(wsa + m * N + n, v[tt * 4 + r], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int64_t m, n;
+        coord(tt, r, m, n);
+        if (m < M && n < N) st_agent(wsa + ((int64_t)sidx * M + m) * N + n, v[tt * 4 + r]);
+      }
+    if (reduce == R_TWOPASS) return;
+  }
+
+  // Arrival: the last of the split workgroups of this row group finishes.
+  int old = 0;
+  if (lane == 0)
+    old = __hip_atomic_fetch_add(counters + blockIdx.x, 1, __ATOMIC_ACQ_REL,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0);
+  if (old != split - 1) return;
+  __atomic_thread_fence(__ATOMIC_ACQUIRE);
+
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int64_t m, n;
+      coord(tt, r, m, n);
+      AccT s = 0;
+      if (m < M && n < N) {
+        if (reduce == R_ATOMIC) {
+          s = ld_agent(wsa + m * N + n);
+          st_agent(wsa + m * N + n, (AccT)0);
+        } else {
+          for (int q = 0; q < split; ++q) s += ld_agent(wsa + ((int64_t)q * M + m) * N + n);
+        }
+      }
+      v[tt * 4 + r] = s;
+    }
+  finish();
+  if (lane == 0) st_agent(counters + blockIdx.x, 0);
+}
+
+// Second pass of the two-pass reduction: sum the split partials of 4
+// consecutive columns in slice order, then the epilogue.
+template <int QK>
+__global__ __launch_bounds__(256) void splitk_reduce(const void* __restrict__ ws, int split,
+                                                     Epi e) {
+  using AccT = typename QTraits<QK>::Acc;
+  const AccT* wsa = (const AccT*)ws;
+  const int64_t nq = (e.N + 3) / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t m = idx / nq;
+  const int64_t n = (idx - m * nq) * 4;
+  if (m >= e.M) return;
+  AccT v[4] = {0, 0, 0, 0};
+  for (int q = 0; q < split; ++q) {
+    const AccT* row = wsa + ((int64_t)q * e.M + m) * e.N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (n + i < e.N) v[i] += row[n + i];
+  }
+  epilogue_run<4, QTraits<QK>::out_f16>(e, m, n, v);
+}
+
+template <int QK, int NTT, bool SWAP, int W, int U>
+hipError_t launch_d(const Variant& v, const Call& c, int split, hipStream_t s) {
+  const int groups = (int)((c.N + 15) / 16);
+  const int total_steps = (int)((c.KB + STEPB - 1) / STEPB);
+  const int sps = (total_steps + split - 1) / split;
+  hipLaunchKernelGGL((decode_kernel<QK, NTT, SWAP, W, U>), dim3(groups, split), dim3(W * 64), 0,
+                     s, (const uint8_t*)c.A, (const uint8_t*)c.B, c.M, c.N, c.KB, split, sps,
+                     v.reduce, c.epi, c.ws, c.counters);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || split == 1 || v.reduce != R_TWOPASS) return err;
+  const int64_t threads = c.M * ((c.N + 3) / 4);
+  hipLaunchKernelGGL((splitk_reduce<QK>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     s, (const void*)c.ws, split, c.epi);
+  return hipGetLastError();
+}
+
+#define LG_DECODE_WAVES(X, QK, NTT, SW) X(QK, NTT, SW, 4, 4) X(QK, NTT, SW, 8, 4) X(QK, NTT, SW, 4, 8) X(QK, NTT, SW, 8, 2)
+
+template <int QK, int NTT, bool SW>
+hipError_t launch_dq(const Variant& v, const Call& c, int split, hipStream_t s) {
+#define LG_TRY(qk, ntt, sw, w, u) \
+  if (v.waves == w && v.unroll == u) return launch_d<qk, ntt, sw, w, u>(v, c, split, s);
+  LG_DECODE_WAVES(LG_TRY, QK, NTT, SW)
+#undef LG_TRY
+  return hipErrorInvalidValue;
+}
+
+template <int QK>
+hipError_t launch_q(const Variant& v, const Call& c, int split, hipStream_t s) {
+  const int ntt = c.M <= 16 ? 1 : 2;
+  if (ntt == 1) return v.swap ? launch_dq<QK, 1, true>(v, c, split, s) : launch_dq<QK, 1, false>(v, c, split, s);
+  return v.swap ? launch_dq<QK, 2, true>(v, c, split, s) : launch_dq<QK, 2, false>(v, c, split, s);
+}
+
+}  // namespace
+
+bool decode_supported(int qk, int ntok_tiles, int swap, int waves, int unroll) {
+  (void)qk;
+  (void)swap;
+  if (ntok_tiles < 1 || ntok_tiles > 2) return false;
+  return (waves == 4 && unroll == 4) || (waves == 8 && unroll == 4) ||
+         (waves == 4 && unroll == 8) || (waves == 8 && unroll == 2);
+}
+
+int decode_auto_split(const Call& c, int waves) {
+  const int64_t groups = (c.N + 15) / 16;
+  const int64_t steps = (c.KB + STEPB - 1) / STEPB;
+  int split = 1;
+  while (groups * split < 768 && (int64_t)split * 2 * waves <= steps && split < 16) split *= 2;
+  return split;
+}
+
+size_t decode_ws_bytes(const Variant& v, const Call& c, int split) {
+  if (split <= 1) return 0;
+  if (v.reduce == R_ATOMIC) return (size_t)c.M * c.N * 4;
+  return (size_t)split * c.M * c.N * 4;
+}
+
+hipError_t launch_decode(const Variant& v, const Call& c, int split, hipStream_t s) {
+  switch (c.qk) {
+    case QK_BF16: return launch_q<QK_BF16>(v, c, split, s);
+    case QK_FP16: return launch_q<QK_FP16>(v, c, split, s);
+    case QK_FP8: return launch_q<QK_FP8>(v, c, split, s);
+    case QK_I8: return launch_q<QK_I8>(v, c, split, s);
+    case QK_FP8_BLOCK: return launch_q<QK_FP8_BLOCK>(v, c, split, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lg

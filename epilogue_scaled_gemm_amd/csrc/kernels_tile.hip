@@ -1,0 +1,300 @@
+// kernels_tile.hip -- LDS-staged MFMA tile GEMM with the fused epilogue, for
+// any M (prefill and medium batches) in every quant mode.
+//
+// What it computes is the layer of the extensible-epilogue listing in
+// "Совместная работа Helion и TorchInductor: слияние операторов" (a 2-D grid
+// of output tiles, an fp32 accumulator over a K loop of masked tile loads,
+// then bias / activation / narrowing on the accumulator and one masked
+// store), extended with the scale formats of "helion-vllm-linear-backend"
+// (section "Одно ядро вместо трёх вариантов"): per-token x per-channel scales
+// applied in the epilogue, and 1x128 / 128x128 block scales applied once per
+// 128-wide K block inside the loop.
+//
+// gfx950 design (not the listing's):
+//  * Weight rows go on the MFMA row side and tokens on the column side, and
+//    MFMA row i of the wave's j-th tile holds weight row i * FN + j.  Each
+//    lane therefore ends the K loop owning 4*FN consecutive output columns of
+//    one row, so bias / scale / residual loads and the store are 16-byte
+//    vectors.
+//  * K advances in 128-byte stages: global -> registers (16-byte coalesced
+//    loads, 8 lanes per row) -> LDS (double buffered, 16-byte chunks XOR
+//    swizzled so the MFMA fragment reads are free of bank conflicts) ->
+//    registers -> MFMA (16x16x32 bf16/fp16, 16x16x64 int8; e4m3 is widened
+//    exactly to bf16 in registers and uses the 16x16x32 bf16 MFMA).
+//  * Workgroup ids are remapped so that each XCD (ids are dealt round-robin
+//    over the 8 XCDs) gets a contiguous, grouped block of tiles, which keeps
+//    the operand panels it shares in its own L2.
+//  * Rows past M / N are clamped on load and masked on store; 16-byte chunks
+//    past the end of K read as zero.
+#include "launch.hpp"
+
+namespace lg {
+namespace {
+
+constexpr int ROWB = 128;  // bytes of K per stage row
+
+template <int BM, int BN, int WM, int WN>
+struct TileShape {
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 16, FN = TN / 16;
+  static constexpr int A_LD = BM * 8 / NT;  // 16-byte chunks per thread per stage
+  static constexpr int B_LD = BN * 8 / NT;
+  static constexpr int STAGE = (BM + BN) * ROWB;
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
+  static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "load split");
+};
+
+__device__ inline int swz_act(int r) { return r & 7; }
+template <int FN> __device__ inline int swz_w(int r) { return (r / FN) & 7; }
+
+template <int QK, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int64_t M, int64_t N,
+    int64_t KB, int tiles_m, int tiles_n, int group_m, Epi e) {
+  using S = TileShape<BM, BN, WM, WN>;
+  using MF = Mfma<QK>;
+  using C = typename MF::C;
+  using AccT = typename QTraits<QK>::Acc;
+  constexpr int FM = S::FM, FN = S::FN, TM = S::TM, TN = S::TN;
+  constexpr bool BLOCK = (QK == QK_FP8_BLOCK);
+  static_assert(!BLOCK || (128 % TN == 0), "a wave's columns must sit in one 128-row scale block");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_m = wave % WM, wave_n = wave / WM;
+  const int g = lane >> 4, l16 = lane & 15;
+
+  // Tile coordinates: XCD-contiguous remap, then a grouped raster.
+  const int nblk = tiles_m * tiles_n;
+  int L = blockIdx.x;
+  if ((nblk & 7) == 0) L = (L & 7) * (nblk >> 3) + (L >> 3);
+  const int gsz = group_m * tiles_n;
+  const int grp = L / gsz;
+  const int first_m = grp * group_m;
+  const int gm = min(tiles_m - first_m, group_m);
+  const int within = L - grp * gsz;
+  const int64_t m0 = (int64_t)(first_m + within % gm) * BM;
+  const int64_t n0 = (int64_t)(within / gm) * BN;
+
+  // Global -> LDS copy slots: thread t copies chunk t % 8 of rows t / 8 + i * NT / 8.
+  const int ck = tid & 7;
+  const int r0 = tid >> 3;
+  constexpr int RSTEP = S::NT / 8;
+  const uint8_t* a_src[S::A_LD];
+  const uint8_t* b_src[S::B_LD];
+  int a_dst[S::A_LD], b_dst[S::B_LD];
+#pragma unroll
+  for (int i = 0; i < S::A_LD; ++i) {
+    const int r = r0 + i * RSTEP;
+    const int64_t gr = min(m0 + r, M - 1);
+    a_src[i] = A + gr * KB + ck * 16;
+    a_dst[i] = r * ROWB + ((ck ^ swz_act(r)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < S::B_LD; ++i) {
+    const int r = r0 + i * RSTEP;
+    const int64_t gr = min(n0 + r, N - 1);
+    b_src[i] = B + gr * KB + ck * 16;
+    b_dst[i] = BM * ROWB + r * ROWB + ((ck ^ swz_w<FN>(r)) << 4);
+  }
+  i32x4 a_reg[S::A_LD], b_reg[S::B_LD];
+
+  auto gload = [&](int kt) {
+    const int64_t off = (int64_t)kt * ROWB;
+    const bool ok = off + ck * 16 < KB;
+#pragma unroll
+    for (int i = 0; i < S::A_LD; ++i)
+      a_reg[i] = ok ? *(const i32x4*)(a_src[i] + off) : i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < S::B_LD; ++i)
+      b_reg[i] = ok ? *(const i32x4*)(b_src[i] + off) : i32x4{0, 0, 0, 0};
+  };
+  auto lstore = [&](int buf) {
+    uint8_t* base = lds + buf * S::STAGE;
+#pragma unroll
+    for (int i = 0; i < S::A_LD; ++i) *(i32x4*)(base + a_dst[i]) = a_reg[i];
+#pragma unroll
+    for (int i = 0; i < S::B_LD; ++i) *(i32x4*)(base + b_dst[i]) = b_reg[i];
+  };
+
+  // Fragment rows (within the stage) of this lane.
+  int fa_row[FM], fw_row[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) fa_row[i] = wave_m * TM + i * 16 + l16;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) fw_row[j] = wave_n * TN + l16 * FN + j;
+  auto a_frag16 = [&](const uint8_t* base, int i, int ch) {
+    const int r = fa_row[i];
+    return *(const i32x4*)(base + r * ROWB + ((ch ^ swz_act(r)) << 4));
+  };
+  auto w_frag16 = [&](const uint8_t* base, int j, int ch) {
+    const int r = fw_row[j];
+    return *(const i32x4*)(base + BM * ROWB + r * ROWB + ((ch ^ swz_w<FN>(r)) << 4));
+  };
+
+  // Block scales: sb is uniform over a wave's columns, sa varies per lane.
+  const int64_t KBLK = KB / 128;
+  const float* sa_ptr[FM];
+  const float* sb_ptr = nullptr;
+  if constexpr (BLOCK) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      sa_ptr[i] = e.sa + min(m0 + fa_row[i], M - 1) * KBLK;
+    // Columns past N (a partial last tile) clamp to the last scale block;
+    // their outputs are never stored.
+    const int64_t nb = min((n0 + wave_n * TN) / 128, (N + 127) / 128 - 1);
+    sb_ptr = e.sb + nb * KBLK;
+  }
+
+  // Block scales of the stage being computed (cur) and of the next one,
+  // fetched together with that stage's tiles.
+  float sa_cur[FM], sa_nxt[FM], sb_cur = 0.f, sb_nxt = 0.f;
+  auto sload = [&](int kt, float* sa_o, float& sb_o) {
+    if constexpr (BLOCK) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sa_o[i] = sa_ptr[i][kt];
+      sb_o = sb_ptr[kt];
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i] = 0.f;
+
+  C acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = C{0, 0, 0, 0};
+
+  const int KT = (int)((KB + ROWB - 1) / ROWB);
+  gload(0);
+  sload(0, sa_cur, sb_cur);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint8_t* base = lds + (kt & 1) * S::STAGE;
+    if (kt + 1 < KT) {
+      gload(kt + 1);
+      sload(kt + 1, sa_nxt, sb_nxt);
+    }
+    if constexpr (!BLOCK) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        typename MF::Frag wf[FN], af[FM];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) wf[j] = MF::prep(w_frag16(base, j, 2 * g + s));
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[i] = MF::prep(a_frag16(base, i, 2 * g + s));
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = MF::mma(wf[j], af[i], acc[i][j]);
+      }
+    } else {
+      // One K stage is one 128-wide scale block: its exact partial sum p is
+      // promoted with sa[m, kb] * sb[n / 128, kb] into the fp32 accumulator.
+      typename MF::Frag wf0[FN], wf1[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        wf0[j] = MF::prep(w_frag16(base, j, 2 * g));
+        wf1[j] = MF::prep(w_frag16(base, j, 2 * g + 1));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const typename MF::Frag a0 = MF::prep(a_frag16(base, i, 2 * g));
+        const typename MF::Frag a1 = MF::prep(a_frag16(base, i, 2 * g + 1));
+        const float sc = sa_cur[i] * sb_cur;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          C p = MF::mma(wf0[j], a0, C{0, 0, 0, 0});
+          p = MF::mma(wf1[j], a1, p);
+          acc[i][j] += sc * p;
+        }
+      }
+    }
+    if (kt + 1 < KT) lstore((kt + 1) & 1);
+    if constexpr (BLOCK) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i];
+      sb_cur = sb_nxt;
+    }
+    __syncthreads();
+  }
+
+  // Fused epilogue straight from the accumulator registers.
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t m = m0 + fa_row[i];
+    const int64_t nb = n0 + wave_n * TN + g * 4 * FN;
+    AccT v[4 * FN];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) v[r * FN + j] = (AccT)acc[i][j][r];
+    epilogue_run<4 * FN, QTraits<QK>::out_f16>(e, m, nb, v);
+  }
+}
+
+template <int QK, int BM, int BN, int WM, int WN>
+hipError_t launch_t(const Variant& v, const Call& c, hipStream_t s) {
+  using S = TileShape<BM, BN, WM, WN>;
+  const int tiles_m = (int)((c.M + BM - 1) / BM);
+  const int tiles_n = (int)((c.N + BN - 1) / BN);
+  const size_t lds = 2 * (size_t)S::STAGE;
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t err = hipFuncSetAttribute((const void*)tile_kernel<QK, BM, BN, WM, WN>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    attr_done = true;
+  }
+  const int group_m = v.group_m > 0 ? v.group_m : 4;
+  hipLaunchKernelGGL((tile_kernel<QK, BM, BN, WM, WN>), dim3(tiles_m * tiles_n), dim3(S::NT),
+                     lds, s, (const uint8_t*)c.A, (const uint8_t*)c.B, c.M, c.N, c.KB, tiles_m,
+                     tiles_n, group_m, c.epi);
+  return hipGetLastError();
+}
+
+// The compiled tile shapes: (BM, BN, WM, WN).
+#define LG_TILE_SHAPES(X) \
+  X(256, 256, 2, 2)       \
+  X(128, 256, 2, 2)       \
+  X(256, 128, 2, 2)       \
+  X(128, 128, 2, 2)       \
+  X(64, 128, 1, 4)        \
+  X(64, 64, 2, 2)
+
+template <int QK>
+hipError_t launch_q(const Variant& v, const Call& c, hipStream_t s) {
+#define LG_TRY(b_m, b_n, w_m, w_n) \
+  if (v.bm == b_m && v.bn == b_n && v.wm == w_m && v.wn == w_n) return launch_t<QK, b_m, b_n, w_m, w_n>(v, c, s);
+  LG_TILE_SHAPES(LG_TRY)
+#undef LG_TRY
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool tile_supported(int qk, int bm, int bn, int wm, int wn) {
+  (void)qk;
+#define LG_HAS(b_m, b_n, w_m, w_n) \
+  if (bm == b_m && bn == b_n && wm == w_m && wn == w_n) return true;
+  LG_TILE_SHAPES(LG_HAS)
+#undef LG_HAS
+  return false;
+}
+
+hipError_t launch_tile(const Variant& v, const Call& c, hipStream_t s) {
+  switch (c.qk) {
+    case QK_BF16: return launch_q<QK_BF16>(v, c, s);
+    case QK_FP16: return launch_q<QK_FP16>(v, c, s);
+    case QK_FP8: return launch_q<QK_FP8>(v, c, s);
+    case QK_I8: return launch_q<QK_I8>(v, c, s);
+    case QK_FP8_BLOCK: return launch_q<QK_FP8_BLOCK>(v, c, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lg

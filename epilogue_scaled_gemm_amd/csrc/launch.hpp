@@ -1,0 +1,55 @@
+// launch.hpp -- host-side view of the kernel families: the variant record the
+// shape-keyed table produces, the call record built by the C ABI, and the
+// launchers each kernel source file provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+namespace lg {
+
+enum VariantKind : int { V_TILE = 0, V_DECODE = 1 };
+// Cross-workgroup split-K reductions of the decode family.
+enum Reduce : int { R_NONE = 0, R_LASTWG = 1, R_ATOMIC = 2, R_TWOPASS = 3 };
+
+struct Variant {
+  int kind = V_TILE;
+  // tile family: workgroup tile BM (tokens) x BN (weight rows), WM x WN waves
+  int bm = 128, bn = 128, wm = 2, wn = 2, group_m = 4;
+  // decode family (M <= 32): swap-AB orientation, split-K factor across
+  // workgroups (0 = choose from the shape), reduction, waves per workgroup
+  // (the in-workgroup K split) and steps of 128 bytes loaded per batch
+  int swap = 1, split = 0, reduce = R_LASTWG, waves = 4, unroll = 4;
+};
+
+struct Call {
+  const void* A;
+  const void* B;
+  int64_t M, N, K;
+  int64_t KB;       // bytes per operand row
+  int qk;           // QKind
+  Epi epi;
+  void* ws;         // split-K workspace (decode family)
+  int* counters;    // arrival counters, one per 16-row weight group
+};
+
+// Tile family (kernels_tile.hip).
+bool tile_supported(int qk, int bm, int bn, int wm, int wn);
+hipError_t launch_tile(const Variant& v, const Call& c, hipStream_t s);
+
+// Decode family (kernels_decode.hip).
+bool decode_supported(int qk, int ntok_tiles, int swap, int waves, int unroll);
+int decode_auto_split(const Call& c, int waves);
+size_t decode_ws_bytes(const Variant& v, const Call& c, int split);
+hipError_t launch_decode(const Variant& v, const Call& c, int split, hipStream_t s);
+
+// Unfused three-kernel path and utilities (kernels_misc.hip).
+hipError_t launch_bias_act(const void* T, const void* bias, void* U, int64_t M, int64_t N,
+                           int act, bool f16, hipStream_t s);
+hipError_t launch_scale_residual(const void* U, const void* residual, void* C, int64_t M,
+                                 int64_t N, float alpha, bool f16, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace lg

@@ -1,0 +1,157 @@
+/*
+ * lin_gemm.h -- C ABI of the MI355X (gfx950) scaled linear layer with a fused
+ * epilogue.
+ *
+ *   C[m,n] = act( s(m,n) * sum_k A[m,k] * B[n,k]  +  bias[n] ) * alpha
+ *            + residual[m,n]
+ *
+ * where s(m,n) is 1 (bf16 / fp16), sa[m] * sb[n] (FP8 dynamic, W8A8 int8),
+ * or applied per 128-wide K block as sa[m,kb] * sb[n/128,kb] (block FP8).
+ * Bias, activation, alpha, residual and the narrowing to a 16-bit float all
+ * happen on the fp32 (or int32) accumulator in registers, before the one
+ * store of C; no intermediate tensor is written to device memory.
+ *
+ * Sources, restated:
+ *  - "Совместная работа Helion и TorchInductor: слияние операторов"
+ *    (gurufy.ru): the epilogue-fusion section (bias, residual, GELU/SiLU and
+ *    the fp32 -> 16-bit narrowing applied to the accumulator before the
+ *    store), the extensible-epilogue kernel listing (fp32 accumulator over
+ *    the K loop; bias broadcast over rows; activation code 1 = ReLU,
+ *    2 = GELU in its tanh form; masked 16-bit store) and the custom-op
+ *    wrapper in the TorchInductor-integration section (checks the inner
+ *    dimension, allocates the output, launches one kernel over a ceil-div
+ *    grid).
+ *  - "helion-vllm-linear-backend" (aixai.ru): the scaled-GEMM formats of the
+ *    section "Одно ядро вместо трёх вариантов" (FP8_Dynamic per-token x
+ *    per-channel, W8A8_INT8 with the same scaling, Block_FP8 with 1x128
+ *    activation and 128x128 weight scale blocks) and the split-K / swap-AB
+ *    variants for small M of the section "Зачем трогать линейные слои",
+ *    chosen per shape from a table (sections "Одно ядро вместо трёх
+ *    вариантов" and "Гибридный диспатч").
+ *
+ * Layouts.  All matrices and scale arrays are dense, row-major, contiguous
+ * and 16-byte aligned device memory owned by the caller:
+ *   A        [M][K]  bf16 | fp16 | e4m3 (OCP E4M3FN) | int8, per quant mode
+ *   B        [N][K]  same element type as A (the weight, K contiguous)
+ *   bias     [N]     bf16 (fp16 in LIN_Q_FP16), or NULL
+ *   residual [M][N]  bf16 (fp16 in LIN_Q_FP16), or NULL
+ *   C        [M][N]  bf16 (fp16 in LIN_Q_FP16); with LIN_ACT_RAW_ACC:
+ *                    int32 (LIN_Q_W8A8_INT8) or fp32 (other modes)
+ *   scales->a  fp32 [M] (FP8 dynamic, int8) or [M][K/128] (block FP8)
+ *   scales->b  fp32 [N] (FP8 dynamic, int8) or [N/128][K/128] (block FP8)
+ *
+ * Streams and errors.  lin_gemm_run enqueues on `stream` (a hipStream_t;
+ * NULL = the null stream) and returns without waiting.  The status it
+ * returns covers argument checks and launch errors only; a fault inside a
+ * kernel surfaces at the next synchronisation.  Nothing throws across this
+ * ABI.  lin_gemm_last_error() gives a human-readable detail for the last
+ * failing call on a handle.
+ *
+ * Handles.  A handle owns its split-K workspace and arrival counters
+ * (device memory, grown on demand, freed by lin_gemm_destroy) and the
+ * shape-keyed variant table.  Calls that share a handle must not run
+ * concurrently on different streams (they share the workspace); use one
+ * handle per stream.  Warm each shape up once before capturing calls into a
+ * hipGraph, so no allocation happens during capture.
+ */
+#ifndef LIN_GEMM_H
+#define LIN_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lin_gemm_ctx *lin_gemm_t;
+
+/* Quant modes (the formats of the linear-backend write-up, plus plain
+ * 16-bit floats). */
+enum lin_quant {
+    LIN_Q_BF16 = 0,
+    LIN_Q_FP16 = 1,
+    LIN_Q_FP8_DYNAMIC = 2, /* e4m3 A, B; sa per token [M], sb per channel [N] */
+    LIN_Q_W8A8_INT8 = 3,   /* int8 A, B; same scaling; int32 accumulator     */
+    LIN_Q_BLOCK_FP8 = 4    /* e4m3; sa [M][K/128], sb [N/128][K/128]         */
+};
+
+/* Activations.  1 and 2 keep the codes of the epilogue listing. */
+enum lin_act {
+    LIN_ACT_NONE = 0,
+    LIN_ACT_RELU = 1,
+    LIN_ACT_GELU_TANH = 2,  /* 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))) */
+    LIN_ACT_SILU = 3,       /* y / (1 + exp(-y)) */
+    LIN_ACT_RAW_ACC = 255   /* test hook: store the raw accumulator (int32 for
+                               int8, fp32 otherwise); no scales, no epilogue */
+};
+
+enum lin_status {
+    LIN_OK = 0,
+    LIN_ERR_INVALID_ARG = -1, /* null pointer, bad code, negative size       */
+    LIN_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels handle   */
+    LIN_ERR_HIP = -3,         /* a HIP runtime call failed                   */
+    LIN_ERR_OOM = -4,         /* workspace allocation failed                 */
+    LIN_ERR_CONFIG = -5       /* variant table file unreadable / malformed   */
+};
+
+typedef struct {
+    const float *a; /* activation scales (see the layouts above)          */
+    const float *b; /* weight scales                                       */
+    float alpha;    /* multiplier applied after the activation (1 = none)  */
+} lin_scales_t;
+
+/* Create a handle.  config_path names a variant-table file (see
+ * lin_gemm_describe for the variant syntax); NULL or "" uses the built-in
+ * table, and the environment variable LIN_GEMM_CONFIG, if set, is read when
+ * config_path is NULL.  Returns LIN_ERR_CONFIG (and no handle) if a named
+ * file cannot be read or parsed. */
+int lin_gemm_create(lin_gemm_t *out, const char *config_path);
+
+/* Run one layer call.  scales may be NULL for LIN_Q_BF16 / LIN_Q_FP16
+ * (alpha = 1); it and scales->a / scales->b are required for the quantised
+ * modes.
+ * Requirements (else LIN_ERR_UNSUPPORTED): N >= 1, K >= 1; K % 8 == 0 for
+ * bf16/fp16 and K % 16 == 0 for e4m3/int8 (16-byte rows); block FP8 also
+ * needs K % 128 == 0 and N % 128 == 0; int8 needs K <= 131071 so that the
+ * int32 accumulator cannot overflow (127 * 127 * K < 2^31).  M == 0 is a
+ * no-op that returns LIN_OK.  Unknown quant / activation codes, a NULL
+ * handle, A, B or C, or negative sizes give LIN_ERR_INVALID_ARG. */
+int lin_gemm_run(lin_gemm_t h, const void *A, const void *B, const lin_scales_t *scales,
+                 const void *bias, const void *residual, void *C, int64_t M, int64_t N,
+                 int64_t K, int quant_mode, int activation, void *stream);
+
+/* Release the handle and its device workspace.  NULL is accepted. */
+int lin_gemm_destroy(lin_gemm_t h);
+
+/* Static text for a status code. */
+const char *lin_gemm_strerror(int status);
+
+/* Detail for the last failing call on h (empty string if none).  The
+ * pointer stays valid until the next call on h. */
+const char *lin_gemm_last_error(lin_gemm_t h);
+
+/* Force a variant for every following lin_gemm_run on h (testing and the
+ * offline sweep); NULL or "" returns to the table.  Spec syntax, e.g.
+ *   "tile bm=128 bn=128"   "decode swap=1 split=4 reduce=lastwg waves=4"
+ * Returns LIN_ERR_CONFIG if the spec does not parse. */
+int lin_gemm_set_force(lin_gemm_t h, const char *spec);
+
+/* Write into buf (NUL-terminated, at most buflen bytes) the variant that
+ * lin_gemm_run would use for this shape, in the spec syntax above. */
+int lin_gemm_describe(lin_gemm_t h, int quant_mode, int64_t M, int64_t N, int64_t K,
+                      char *buf, int buflen);
+
+/* The three-kernel unfused path of the decoder-block example (measurement
+ * only; bf16 / fp16): T = A*B^T, U = act(T + bias), C = alpha*U + residual,
+ * with T and U written to and re-read from the caller's [M][N] buffers.
+ * Same requirements as lin_gemm_run in LIN_Q_BF16 / LIN_Q_FP16. */
+int lin_gemm_run_unfused(lin_gemm_t h, const void *A, const void *B, const void *bias,
+                         const void *residual, void *C, void *T, void *U, int64_t M,
+                         int64_t N, int64_t K, float alpha, int quant_mode, int activation,
+                         void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIN_GEMM_H */

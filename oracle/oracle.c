@@ -141,16 +141,29 @@ typedef struct {
     int quant, act;
 } olayer_t;
 
+/* Lookup tables filled from the closed forms above (every code, once), so
+ * the O(MNK) loops do not call ldexp per element. */
+static double g_e4m3[256];
+static double g_fp16[65536];
+static int g_tables_ready = 0;
+
+static void tables_init(void) {
+    if (g_tables_ready) return;
+    for (int c = 0; c < 256; ++c) g_e4m3[c] = oracle_e4m3_to_f64((uint8_t)c);
+    for (int c = 0; c < 65536; ++c) g_fp16[c] = oracle_fp16_to_f64((uint16_t)c);
+    g_tables_ready = 1;
+}
+
 static double dec16(int quant, uint16_t v) {
-    return quant == OQ_FP16 ? oracle_fp16_to_f64(v) : oracle_bf16_to_f64(v);
+    return quant == OQ_FP16 ? g_fp16[v] : oracle_bf16_to_f64(v);
 }
 
 static double elem(const olayer_t *L, const void *X, int64_t idx) {
     switch (L->quant) {
     case OQ_BF16: return oracle_bf16_to_f64(((const uint16_t *)X)[idx]);
-    case OQ_FP16: return oracle_fp16_to_f64(((const uint16_t *)X)[idx]);
+    case OQ_FP16: return g_fp16[((const uint16_t *)X)[idx]];
     case OQ_FP8_DYNAMIC:
-    case OQ_BLOCK_FP8: return oracle_e4m3_to_f64(((const uint8_t *)X)[idx]);
+    case OQ_BLOCK_FP8: return g_e4m3[((const uint8_t *)X)[idx]];
     default: return NAN;
     }
 }
@@ -203,6 +216,7 @@ static int one(const olayer_t *L, int64_t m, int64_t n, double *r_out, int32_t *
 }
 
 static int check(const olayer_t *L) {
+    tables_init();
     if (L->M < 0 || L->N < 0 || L->K < 0) return O_BAD_ARG;
     if (L->quant < OQ_BF16 || L->quant > OQ_BLOCK_FP8) return O_BAD_ARG;
     if (L->act < OA_NONE || L->act > OA_SILU) return O_BAD_ARG;
@@ -283,6 +297,7 @@ int oracle_linear_at(const void *A, const void *B, const float *sa, const float 
  * outputs are fp64 (the reference value before the final narrowing). */
 int oracle_unfused_stage2(const uint16_t *t, const uint16_t *bias, int64_t M, int64_t N,
                           int quant, int act, double *u) {
+    tables_init();
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n) {
             double y = dec16(quant, t[m * N + n]);
@@ -294,6 +309,7 @@ int oracle_unfused_stage2(const uint16_t *t, const uint16_t *bias, int64_t M, in
 
 int oracle_unfused_stage3(const uint16_t *u, const uint16_t *residual, double alpha,
                           int64_t M, int64_t N, int quant, double *o) {
+    tables_init();
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n) {
             double y = dec16(quant, u[m * N + n]) * alpha;

@@ -87,7 +87,12 @@ def to_e4m3_codes(x: np.ndarray) -> np.ndarray:
 
 def to_int8_codes(x: np.ndarray) -> np.ndarray:
     """Round half to even, clamp to [-127, 127] (symmetric)."""
-    return np.clip(np.rint(x), -INT8_MAX, INT8_MAX).astype(np.int8)
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return torch.round(t).clamp_(-INT8_MAX, INT8_MAX).to(torch.int8).numpy()
+
+
+def _absmax(x: np.ndarray, dims) -> np.ndarray:
+    return torch.from_numpy(x).abs().amax(dim=dims).numpy()
 
 
 def _safe_scale(absmax: np.ndarray, qmax: float) -> np.ndarray:
@@ -99,8 +104,8 @@ def _safe_scale(absmax: np.ndarray, qmax: float) -> np.ndarray:
 def quant_rows(x: np.ndarray, kind: str):
     """Per-row (per-token / per-channel) symmetric absmax quantisation."""
     qmax = E4M3_MAX if kind == "fp8" else INT8_MAX
-    s = _safe_scale(np.abs(x).max(axis=1), qmax)
-    q = x / s[:, None]
+    s = _safe_scale(_absmax(x, 1), qmax)
+    q = (torch.from_numpy(x) / torch.from_numpy(s)[:, None]).numpy()
     codes = to_e4m3_codes(q) if kind == "fp8" else to_int8_codes(q)
     return codes, s
 
@@ -109,16 +114,18 @@ def quant_blocks_act(x: np.ndarray):
     """1x128 blocks along K: scale[M][K/128]."""
     M, K = x.shape
     xb = x.reshape(M, K // 128, 128)
-    s = _safe_scale(np.abs(xb).max(axis=2), E4M3_MAX)
-    return to_e4m3_codes((xb / s[:, :, None]).reshape(M, K)), s
+    s = _safe_scale(_absmax(xb, 2), E4M3_MAX)
+    q = (torch.from_numpy(xb) / torch.from_numpy(s)[:, :, None]).numpy()
+    return to_e4m3_codes(q.reshape(M, K)), s
 
 
 def quant_blocks_weight(x: np.ndarray):
     """128x128 blocks: scale[N/128][K/128]."""
     N, K = x.shape
     xb = x.reshape(N // 128, 128, K // 128, 128)
-    s = _safe_scale(np.abs(xb).max(axis=(1, 3)), E4M3_MAX)
-    return to_e4m3_codes((xb / s[:, None, :, None]).reshape(N, K)), s
+    s = _safe_scale(_absmax(xb, (1, 3)), E4M3_MAX)
+    q = (torch.from_numpy(xb) / torch.from_numpy(s)[:, None, :, None]).numpy()
+    return to_e4m3_codes(q.reshape(N, K)), s
 
 
 def encode(quant: str, x: np.ndarray, side: str):

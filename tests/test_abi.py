@@ -1,0 +1,139 @@
+"""The C ABI: the library loads and exports every symbol include/lin_gemm.h
+declares; the variant table parses; argument errors return the documented
+status codes before anything reaches the GPU.
+
+The CPU tests here never launch a kernel: every call either fails validation
+or has M == 0.  Calls that would pass validation are only made in the GPU
+tests, with real device tensors.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lin_gemm.h")
+
+lg = pytest.importorskip("epilogue_scaled_gemm_amd")
+pytestmark = pytest.mark.skipif(not os.path.exists(lg.LIB_PATH), reason="library not built")
+
+OK, INVALID, UNSUPPORTED, CONFIG = 0, -1, -2, -5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(lin_gemm_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert set(declared_functions()) == set(lg.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", lg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [f for f in declared_functions() if f not in syms]
+    assert not missing, missing
+    lib = ctypes.CDLL(lg.LIB_PATH)
+    for f in declared_functions():
+        assert hasattr(lib, f)
+
+
+def test_strerror():
+    assert lg.strerror(0) == "ok"
+    assert "invalid" in lg.strerror(-1)
+    assert "unsupported" in lg.strerror(-2)
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def _raw_run(h, A=FAKE, B=FAKE, C=FAKE, M=4, N=16, K=64, quant=0, act=0, scales=None,
+             bias=None, residual=None):
+    lib = lg.library()
+    sc = lg._Scales(*(scales if scales else (None, None, 1.0)))
+    return lib.lin_gemm_run(h._h, A, B, ctypes.byref(sc), bias, residual, C, M, N, K, quant, act,
+                            None)
+
+
+@pytest.fixture()
+def cpu_handle():
+    if torch.cuda.is_available():
+        pytest.skip("fake-pointer error paths run on the CPU only")
+    h = lg.Handle()
+    yield h
+    h.close()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(quant=7), INVALID),
+    (dict(act=9), INVALID),
+    (dict(M=-1), INVALID),
+    (dict(A=None), INVALID),
+    (dict(C=None), INVALID),
+    (dict(quant=2), INVALID),                              # fp8 without scales
+    (dict(quant=3, scales=(FAKE, None, 1.0)), INVALID),     # int8 missing sb
+    (dict(K=60), UNSUPPORTED),                             # bf16 rows not 16-byte multiples
+    (dict(quant=2, K=40, scales=(FAKE, FAKE, 1.0)), UNSUPPORTED),
+    (dict(quant=4, N=100, K=256, scales=(FAKE, FAKE, 1.0)), UNSUPPORTED),
+    (dict(quant=4, N=128, K=200, scales=(FAKE, FAKE, 1.0)), UNSUPPORTED),
+    (dict(quant=3, K=131072, scales=(FAKE, FAKE, 1.0)), UNSUPPORTED),
+    (dict(N=0), UNSUPPORTED),
+    (dict(A=FAKE + 4), UNSUPPORTED),                       # misaligned
+])
+def test_argument_errors(cpu_handle, kw, status):
+    assert _raw_run(cpu_handle, **kw) == status
+    if status != OK:
+        assert lg.library().lin_gemm_last_error(cpu_handle._h)
+
+
+def test_zero_m_returns_ok_without_work(cpu_handle):
+    assert _raw_run(cpu_handle, M=0) == OK
+
+
+def test_force_and_describe(cpu_handle):
+    h = cpu_handle
+    assert h.describe("fp8_dynamic", 8, 6144, 4096).startswith("decode")
+    assert h.describe("bf16", 4096, 4096, 4096).startswith("tile")
+    h.set_force("decode swap=0 split=4 reduce=twopass waves=8 unroll=2")
+    assert h.describe("w8a8_int8", 4, 24576, 4096) == \
+        "decode swap=0 split=4 reduce=twopass waves=8 unroll=2"
+    with pytest.raises(lg.LinGemmError):
+        h.describe("bf16", 64, 128, 128)          # forced decode with M > 32
+    with pytest.raises(lg.LinGemmError):
+        h.set_force("tile bm=96 bn=96 wm=2 wn=2")  # not a compiled shape
+    with pytest.raises(lg.LinGemmError):
+        h.set_force("decode split=3")              # not a power of two
+    h.set_force(None)
+    # auto split: 384 row groups of 16 -> 2 slices; 1536 -> 1
+    assert "split=2" in h.describe("fp8_dynamic", 1, 6144, 4096)
+    assert "split=1" in h.describe("w8a8_int8", 1, 24576, 4096)
+
+
+def test_table_file(tmp_path):
+    good = tmp_path / "t.cfg"
+    good.write_text("# test table\nfp8_dynamic 1 32 6144 4096 decode swap=0 split=8 "
+                    "reduce=atomic waves=8 unroll=4\n* 1 * * * tile bm=64 bn=64 wm=2 wn=2\n")
+    h = lg.Handle(str(good))
+    assert h.describe("fp8_dynamic", 3, 6144, 4096) == \
+        "decode swap=0 split=8 reduce=atomic waves=8 unroll=4"
+    assert h.describe("fp8_dynamic", 3, 6144, 8192).startswith("tile bm=64 bn=64")
+    h.close()
+    bad = tmp_path / "bad.cfg"
+    bad.write_text("fp8_dynamic 1 64 * * decode swap=1\n")   # decode beyond 32 tokens
+    with pytest.raises(lg.LinGemmError):
+        lg.Handle(str(bad))
+    with pytest.raises(lg.LinGemmError):
+        lg.Handle(str(tmp_path / "missing.cfg"))
+
+
+def test_shipped_table_parses():
+    path = os.path.join(os.path.dirname(lg.__file__), "configs", "mi355x.cfg")
+    if not os.path.exists(path):
+        pytest.skip("no shipped table yet")
+    h = lg.Handle(path)
+    h.close()

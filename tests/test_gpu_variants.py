@@ -1,0 +1,151 @@
+"""GPU variant invariants: every decode variant (swap-AB on/off, split-K
+factors, the three cross-workgroup reductions, wave / unroll shapes) and
+every compiled tile shape gives the oracle's result; split-K matches the
+unsplit kernel (int8 bit-exact); the deterministic reductions are bitwise
+repeatable; swap-AB equals the direct orientation."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import oracle
+from gpu_util import assert_close, decode_out, reference, run, upload
+
+pytestmark = pytest.mark.gpu
+
+lg = pytest.importorskip("epilogue_scaled_gemm_amd")
+
+
+@pytest.fixture(scope="module")
+def handle():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    h = lg.Handle()
+    yield h
+    h.set_force(None)
+    h.close()
+
+
+DECODE_SPECS = [
+    f"decode swap={sw} split={sp} reduce={rd} waves={w} unroll={u}"
+    for sw in (1, 0)
+    for sp, rd in ((1, "lastwg"), (2, "lastwg"), (4, "atomic"), (8, "twopass"), (16, "lastwg"),
+                   (4, "twopass"), (2, "atomic"))
+    for w, u in ((4, 4), (8, 2))
+] + ["decode swap=1 split=2 reduce=lastwg waves=8 unroll=4",
+     "decode swap=0 split=1 reduce=lastwg waves=4 unroll=8"]
+
+DECODE_PROBLEMS = [
+    ("fp8_dynamic", "none", 1, 6144, 4096, True, False),
+    ("fp8_dynamic", "gelu_tanh", 5, 1040, 4096, True, True),
+    ("w8a8_int8", "silu", 24, 2064, 4096, False, False),
+    ("block_fp8", "none", 17, 512, 3072, False, True),
+    ("bf16", "silu", 9, 272, 1040, True, True),
+    ("fp16", "relu", 32, 144, 528, True, False),
+]
+
+
+@pytest.fixture(scope="module")
+def decode_refs():
+    out = {}
+    for q, a, M, N, K, b, r in DECODE_PROBLEMS:
+        p = synth.make_custom(q, a, M, N, K, seed=7 * M + N, bias=b, residual=r)
+        ref, _ = reference(p)
+        acc = None
+        if q == "w8a8_int8":
+            _, acc = oracle.linear(q, "none", p.A, p.B, p.sa, p.sb)
+        out[(q, M)] = (p, ref, acc)
+    return out
+
+
+@pytest.mark.parametrize("prob", DECODE_PROBLEMS, ids=[f"{p[0]}-M{p[2]}" for p in DECODE_PROBLEMS])
+def test_decode_variants_match_oracle(handle, decode_refs, prob):
+    p, ref, acc = decode_refs[(prob[0], prob[2])]
+    d = upload(p)
+    try:
+        for spec in DECODE_SPECS:
+            handle.set_force(spec)
+            print(f"[variant] {p.name} {spec}", flush=True)
+            C = run(handle, p, d)
+            assert_close(decode_out(C, p.quant), ref, f"{p.name} [{spec}]")
+            if acc is not None:
+                Craw = run(handle, p, d, raw=True)
+                assert np.array_equal(Craw.cpu().numpy(), acc), f"int8 acc [{spec}]"
+    finally:
+        handle.set_force(None)
+
+
+@pytest.mark.parametrize("reduce", ["lastwg", "twopass"])
+def test_deterministic_reductions_repeat_bitwise(handle, reduce):
+    p = synth.make(2, 16)
+    d = upload(p)
+    try:
+        handle.set_force(f"decode swap=1 split=8 reduce={reduce} waves=4 unroll=4")
+        first = run(handle, p, d).cpu()
+        for _ in range(5):
+            assert torch.equal(run(handle, p, d).cpu(), first)
+        # and split-K agrees with the unsplit kernel to fp32 reassociation
+        handle.set_force("decode swap=1 split=1 reduce=lastwg waves=4 unroll=4")
+        unsplit = decode_out(run(handle, p, d), p.quant)
+        assert_close(decode_out(first, p.quant), unsplit, "split vs unsplit")
+    finally:
+        handle.set_force(None)
+
+
+def test_swap_ab_equals_direct(handle):
+    p = synth.make(3, 8)
+    d = upload(p)
+    try:
+        handle.set_force("decode swap=1 split=1 reduce=lastwg waves=4 unroll=4")
+        a = run(handle, p, d, raw=True).cpu()
+        handle.set_force("decode swap=0 split=1 reduce=lastwg waves=4 unroll=4")
+        b = run(handle, p, d, raw=True).cpu()
+        assert torch.equal(a, b)
+    finally:
+        handle.set_force(None)
+
+
+TILE_SPECS = ["tile bm=256 bn=256 wm=2 wn=2", "tile bm=128 bn=256 wm=2 wn=2",
+              "tile bm=256 bn=128 wm=2 wn=2", "tile bm=128 bn=128 wm=2 wn=2",
+              "tile bm=64 bn=128 wm=1 wn=4", "tile bm=64 bn=64 wm=2 wn=2"]
+TILE_PROBLEMS = [
+    ("bf16", "gelu_tanh", 300, 520, 264, True, True, 0.5),
+    ("fp16", "silu", 130, 264, 200, True, False, 1.0),
+    ("fp8_dynamic", "relu", 200, 300, 400, True, True, 1.0),
+    ("w8a8_int8", "silu", 260, 136, 528, False, False, 1.0),
+    ("block_fp8", "none", 270, 512, 384, True, True, 1.0),
+]
+
+
+@pytest.mark.parametrize("prob", TILE_PROBLEMS, ids=[p[0] for p in TILE_PROBLEMS])
+def test_tile_shapes_match_oracle(handle, prob):
+    q, a, M, N, K, b, r, al = prob
+    p = synth.make_custom(q, a, M, N, K, seed=M * 3 + K, bias=b, residual=r, alpha=al)
+    ref, _ = reference(p)
+    acc = oracle.linear(q, "none", p.A, p.B, p.sa, p.sb)[1] if q == "w8a8_int8" else None
+    d = upload(p)
+    try:
+        for spec in TILE_SPECS:
+            handle.set_force(spec)
+            print(f"[variant] {p.name} {spec}", flush=True)
+            assert_close(decode_out(run(handle, p, d), q), ref, f"{p.name} [{spec}]")
+            if acc is not None:
+                assert np.array_equal(run(handle, p, d, raw=True).cpu().numpy(), acc), spec
+    finally:
+        handle.set_force(None)
+
+
+def test_tile_and_decode_agree_on_small_m(handle):
+    # The same M <= 32 problem through both families.
+    p = synth.make(4, 32)
+    d = upload(p)
+    try:
+        handle.set_force("tile bm=64 bn=128 wm=1 wn=4")
+        t = decode_out(run(handle, p, d), p.quant)
+        handle.set_force("decode swap=1 split=4 reduce=lastwg waves=4 unroll=4")
+        dd = decode_out(run(handle, p, d), p.quant)
+        ref, _ = reference(p)
+        assert_close(t, ref, "tile")
+        assert_close(dd, ref, "decode")
+    finally:
+        handle.set_force(None)
