@@ -1,0 +1,361 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X scaled linear layer with a fused epilogue.
+
+Headline workload (one "step"): the FP8-dynamic decode linear, A[M,4096] e4m3
+against a B[6144,4096] e4m3 weight with per-token x per-channel scales and a
+bias, at every token count M in {1, 2, 4, 8, 16, 24, 32}; at each M the step
+runs one call per weight copy of a 16-copy rotation (16 distinct weight
+buffers, 384 MiB in all, so the 256 MB MALL cannot serve repeated reads --
+as 16 layers of a model would).  value = algorithmic HBM bytes of the step /
+its time, in TB/s.
+
+Timing follows the graph-replay discipline of the vLLM linear-backend
+write-up: each M's calls are captured once into a HIP graph and replayed, so
+kernels run back to back without host launch gaps; HIP events on the launch
+stream bracket every replay.  The per-shape table covers all five workloads
+(TFLOP/s, TB/s and their roofline fractions) and the unfused three-kernel
+prefill path.  The CPU oracle is timed on a bounded sample for the
+cpu_baseline field.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-shapes]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12                                     # bytes/s
+MFMA_PEAK = {"bf16": 2.5e15, "fp16": 2.5e15, "fp8_dynamic": 5.0e15, "block_fp8": 5.0e15,
+             "w8a8_int8": 5.0e15}                     # dense, per operand dtype
+RIDGE = {q: MFMA_PEAK[q] / HBM_PEAK for q in MFMA_PEAK}
+HEAD_CFG = 2
+NCOPY_TARGET_BYTES = 384 << 20                        # rotation footprint > 256 MB MALL
+METRIC = "TFLOP/s & HBM TB/s (fraction of roofline) per shape, M∈{1..32} and M=4096"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape table")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--reps", type=int, default=20, help="graph replays per shape in the table")
+    ap.add_argument("--counters", action="store_true",
+                    help="short run for rocprofv3 --pmc passes: the headline graphs for two "
+                         "steps, then a plain 256 MiB device copy that calibrates the counters")
+    return ap.parse_args()
+
+
+def source_digest():
+    """Hash of the kernel sources (to tell whether stored counters still apply)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "epilogue_scaled_gemm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+class Workload:
+    """Device operands of one workload, with a rotation of weight copies."""
+
+    def __init__(self, torch, cfg, Ms, quant=None, ncopy=None):
+        import synth
+        self.torch = torch
+        self.cfg = cfg
+        self.Ms = list(Ms)
+        self.probs = {M: synth.make(cfg, M, quant) for M in self.Ms}
+        p0 = self.probs[self.Ms[0]]
+        self.quant, self.act, self.N, self.K = p0.quant, p0.act, p0.N, p0.K
+        wbytes = p0.B.nbytes
+        self.ncopy = ncopy or max(2, min(32, -(-NCOPY_TARGET_BYTES // wbytes)))
+        B0 = self._dev(p0.B)
+        self.B = [B0] + [B0.clone() for _ in range(self.ncopy - 1)]
+        self.sb = self._dev(p0.sb)
+        self.bias = self._dev(p0.bias)
+        self.dev = {}
+        for M, p in self.probs.items():
+            self.dev[M] = dict(A=self._dev(p.A), sa=self._dev(p.sa), residual=self._dev(p.residual),
+                               C=torch.empty((M, p.N), dtype=torch.int16, device="cuda"),
+                               alpha=p.alpha)
+
+    def _dev(self, a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return self.torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    def call(self, h, M, copy):
+        d = self.dev[M]
+        h.run(d["A"], self.B[copy % self.ncopy], d["C"], quant=self.quant, act=self.act,
+              sa=d["sa"], sb=self.sb, alpha=d["alpha"], bias=self.bias, residual=d["residual"])
+
+    def bytes(self, M):
+        import synth
+        p = self.probs[M]
+        return synth.algorithmic_bytes(self.quant, M, self.N, self.K, p.bias is not None,
+                                       p.residual is not None)
+
+    def flops(self, M):
+        return 2 * M * self.N * self.K
+
+    def graph(self, h, M, reps, offset=0):
+        """A HIP graph of `reps` calls at token count M over rotating copies."""
+        torch = self.torch
+        self.call(h, M, offset)               # warm (workspace allocation)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(reps):
+                self.call(h, M, offset + r)
+        return g
+
+
+def time_graph(torch, g, reps):
+    """Average time (s) of one replay over `reps` replays, by HIP events."""
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        g.replay()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / 1e3 / reps
+
+
+def shape_row(name, quant, M, N, K, t, nbytes, flops, variant, kernel_calls=1):
+    ai = flops / nbytes
+    bound = "mfma" if ai > RIDGE[quant] else "hbm"
+    tbs, tfs = nbytes / t, flops / t
+    return dict(shape=name, quant=quant, M=M, N=N, K=K, variant=variant, us=round(t * 1e6, 3),
+                TBps=round(tbs / 1e12, 4), TFLOPs=round(tfs / 1e12, 3),
+                hbm_frac=round(tbs / HBM_PEAK, 4), mfma_frac=round(tfs / MFMA_PEAK[quant], 4),
+                bound=bound, kernels_per_call=kernel_calls,
+                roof_frac=round((tbs / HBM_PEAK) if bound == "hbm" else (tfs / MFMA_PEAK[quant]), 4))
+
+
+def per_shape_table(torch, h, reps):
+    import synth
+    rows = []
+    for cfg in (1, 2, 3, 4, 5):
+        c = synth.CONFIGS[cfg]
+        wl = Workload(torch, cfg, c["Ms"])
+        for M in c["Ms"]:
+            R = wl.ncopy
+            g = wl.graph(h, M, R)
+            t = time_graph(torch, g, max(2, reps // (1 if M < 512 else 4))) / R
+            rows.append(shape_row(c["name"], wl.quant, M, wl.N, wl.K, t, wl.bytes(M), wl.flops(M),
+                                  h.describe(wl.quant, M, wl.N, wl.K)))
+            print(f"[shape] {rows[-1]}", file=sys.stderr, flush=True)
+            del g
+        if cfg == 5:
+            rows.append(unfused_row(torch, h, wl, reps))
+        del wl
+        torch.cuda.empty_cache()
+    return rows
+
+
+def unfused_row(torch, h, wl, reps):
+    """The three-kernel path on the prefill problem (GEMM -> T, bias+GELU -> U,
+    0.5*U + residual -> C) and its compulsory bytes (T and U each written
+    once and read once on top of the fused traffic)."""
+    M = wl.Ms[0]
+    d = wl.dev[M]
+    T = torch.empty_like(d["C"])
+    U = torch.empty_like(d["C"])
+
+    def call(copy):
+        h.run_unfused(d["A"], wl.B[copy % wl.ncopy], d["C"], T, U, quant=wl.quant, act=wl.act,
+                      alpha=d["alpha"], bias=wl.bias, residual=d["residual"])
+
+    call(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(wl.ncopy):
+            call(r)
+    t = time_graph(torch, g, max(2, reps // 4)) / wl.ncopy
+    nbytes = wl.bytes(M) + 2 * 2 * (2 * M * wl.N)      # + write/read of T and of U
+    row = shape_row("prefill_bf16_unfused_3kernel", wl.quant, M, wl.N, wl.K, t, nbytes,
+                    wl.flops(M), "gemm + bias_act + scale_residual", kernel_calls=3)
+    print(f"[shape] {row}", file=sys.stderr, flush=True)
+    return row
+
+
+def cpu_baseline(target_s):
+    """The oracle, as it stands, on a bounded sample of the headline workload:
+    whole passes of the M sweep, repeated until ~target_s of oracle time."""
+    import oracle
+    import synth
+    c = synth.CONFIGS[HEAD_CFG]
+    probs = [synth.make(HEAD_CFG, M) for M in c["Ms"]]
+    ncols = c["N"]
+    done_bytes, elapsed, passes = 0.0, 0.0, 0
+    while elapsed < target_s and passes < 50:
+        for p in probs:
+            t0 = time.perf_counter()
+            oracle.linear(p.quant, p.act, p.A, p.B[:ncols], p.sa, p.sb[:ncols], p.bias[:ncols],
+                          None, p.alpha)
+            elapsed += time.perf_counter() - t0
+            done_bytes += synth.algorithmic_bytes(p.quant, p.M, ncols, p.K, True, False)
+        passes += 1
+    return dict(value=done_bytes / elapsed / 1e12, unit="TB/s", cores=oracle.num_threads(),
+                kind="oracle",
+                sample=f"fp8_dynamic decode, the full M sweep {list(c['Ms'])} at N={ncols}, "
+                       f"K={c['K']}, repeated {passes} times ({elapsed:.1f} s of oracle time)")
+
+
+def load_traffic(kernel, digest):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    k = t.get("kernels", {}).get(kernel)
+    if not k or t.get("source_digest") != digest:
+        return None
+    return k.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU; collectives and multi-GPU runs are not "
+              f"part of it (asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import epilogue_scaled_gemm_amd as lg
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.init()
+    h = lg.Handle()
+    c = synth.CONFIGS[HEAD_CFG]
+    Ms = list(c["Ms"])
+    wl = Workload(torch, HEAD_CFG, Ms)
+    R = wl.ncopy
+    # Largest M first so the split-K workspace is sized before any capture.
+    graphs = {M: wl.graph(h, M, R) for M in sorted(Ms, reverse=True)}
+    torch.cuda.synchronize()
+    print(f"[bench] workload {c['name']} N={wl.N} K={wl.K} Ms={Ms} copies={R} "
+          f"({R * wl.B[0].numel() / 2**20:.0f} MiB of weights)", file=sys.stderr, flush=True)
+
+    if args.counters:
+        for _ in range(2):
+            for M in Ms:
+                graphs[M].replay()
+        torch.cuda.synchronize()
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": True, "copy_bytes": 256 << 20,
+                          "kernel_bytes": {M: wl.bytes(M) for M in Ms}}), flush=True)
+        return
+
+    for _ in range(args.warmup):
+        for M in Ms:
+            graphs[M].replay()
+    torch.cuda.synchronize()
+
+    ev = [(M, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps) for M in Ms]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()                            # barrier: one rank
+    t_start.record()
+    i = 0
+    for _ in range(args.steps):
+        for M in Ms:
+            ev[i][1].record()
+            graphs[M].replay()
+            ev[i][2].record()
+            i += 1
+    t_end.record()
+    torch.cuda.synchronize()
+    total_s = t_start.elapsed_time(t_end) / 1e3
+    per_M = {M: 0.0 for M in Ms}
+    for M, s, e in ev:
+        per_M[M] += s.elapsed_time(e) / 1e3
+    step_bytes = sum(wl.bytes(M) for M in Ms) * R
+    value = step_bytes * args.steps / total_s / 1e12
+
+    # Dominant kernel: the decode instantiation with the most time (tokens
+    # <= 16 use one 16-column tile, 17..32 use two; the template arguments
+    # are quant kind 2 = e4m3, token tiles, swap-AB, waves, unroll).
+    def kernel_name(M):
+        v = dict(kv.split("=") for kv in h.describe(wl.quant, M, wl.N, wl.K).split()[1:])
+        return (f"decode_kernel<2, {1 if M <= 16 else 2}, {'true' if v['swap'] == '1' else 'false'}"
+                f", {v['waves']}, {v['unroll']}>")
+    groups = {}
+    for M in Ms:
+        groups.setdefault(kernel_name(M), []).append(M)
+    kname, kms = max(groups.items(), key=lambda kv: sum(per_M[M] for M in kv[1]))
+    launches = args.steps * R * len(kms)
+    ktime = sum(per_M[M] for M in kms)
+    avg_dur = ktime / launches
+    avg_bytes = sum(wl.bytes(M) for M in kms) / len(kms)
+    achieved = avg_bytes / avg_dur
+    digest = source_digest()
+    traffic = load_traffic(kname, digest)
+    roofline = dict(bound="hbm", achieved=round(achieved / 1e9, 1), peak=HBM_PEAK / 1e9,
+                    unit="GB/s", frac=round(achieved / HBM_PEAK, 4), traffic=traffic,
+                    kernel=kname, avg_launch_us=round(avg_dur * 1e6, 3),
+                    algorithmic_bytes_per_launch=int(avg_bytes),
+                    variant=h.describe(wl.quant, kms[0], wl.N, wl.K))
+    per_m_rows = [dict(M=M, us_per_call=round(per_M[M] / (args.steps * R) * 1e6, 3),
+                       TBps=round(wl.bytes(M) * R * args.steps / per_M[M] / 1e12, 4),
+                       hbm_frac=round(wl.bytes(M) * R * args.steps / per_M[M] / HBM_PEAK, 4),
+                       variant=h.describe(wl.quant, M, wl.N, wl.K)) for M in Ms]
+    del graphs, wl
+    torch.cuda.empty_cache()
+
+    shapes = None
+    if not args.no_shapes:
+        shapes = per_shape_table(torch, h, args.reps)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_s / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"{c['name']}: A[M,{c['K']}] e4m3 x B[{c['N']},{c['K']}] e4m3, "
+                               f"per-token x per-channel fp32 scales, bf16 bias and output; "
+                               f"M in {Ms}; {R} weight copies per M per step",
+                   "M": Ms, "N": c["N"], "K": c["K"], "weight_copies": R,
+                   "calls_per_step": R * len(Ms), "parallelism": "single GPU"},
+        "roofline": roofline,
+        "per_M": per_m_rows,
+        "cpu_baseline": cpu,
+        "shapes": shapes,
+        "source_digest": digest,
+    }
+    print(json.dumps(out), flush=True)
+    h.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -143,13 +143,24 @@ bool parse_table(const std::string& text, std::vector<TableEntry>* out, std::str
   return true;
 }
 
-// Built-in default: decode family for up to 32 tokens (swap-AB, split-K
-// chosen from the shape, last-arrival reduction), then tile sizes growing
-// with M.  Tuned entries for the measured shapes come first.
+// Built-in default: decode family for up to 32 tokens (swap-AB, K split
+// among the waves of each workgroup), then tile sizes growing with M.
 const char* builtin_table() {
   return R"TABLE(
 # quant        m_lo m_hi N     K      variant
-*              1    32   *     *      decode swap=1 split=0 reduce=lastwg waves=4 unroll=4
+# measured entries (offline sweep on MI355X, graph replay, rotating weights)
+fp8_dynamic    1    8    6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=1
+fp8_dynamic    9    32   6144  4096   decode swap=1 split=1 reduce=twopass waves=4 unroll=8
+w8a8_int8      1    16   24576 4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=2
+w8a8_int8      17   32   24576 4096   decode swap=1 split=1 reduce=twopass waves=16 unroll=1
+block_fp8      1    4    4096  12288  decode swap=1 split=1 reduce=twopass waves=16 unroll=1
+block_fp8      5    16   4096  12288  decode swap=1 split=1 reduce=twopass waves=8 unroll=2
+block_fp8      17   32   4096  12288  decode swap=1 split=1 reduce=twopass waves=16 unroll=2
+block_fp8      33   1024 4096  12288  tile bm=64 bn=64 wm=2 wn=2 group=4
+block_fp8      1025 *    4096  12288  tile bm=64 bn=128 wm=1 wn=4 group=4
+bf16           1025 *    4096  4096   tile bm=128 bn=128 wm=2 wn=2 group=4
+# defaults
+*              1    32   *     *      decode swap=1 split=1 reduce=twopass waves=8 unroll=2
 block_fp8      33   *    *     *      tile bm=128 bn=128 wm=2 wn=2 group=4
 *              33   256  *     *      tile bm=64 bn=128 wm=1 wn=4 group=4
 *              257  1024 *     *      tile bm=128 bn=128 wm=2 wn=2 group=4

@@ -15,8 +15,9 @@
 //    weight byte is loaded by exactly one lane, straight from HBM into
 //    registers (no LDS staging: there is no reuse to stage for).  Every lane
 //    loads 32 contiguous bytes per step; 4 lanes cover a 128-byte line.
-//  * Loads run one batch of U steps ahead of the MFMAs (register double
-//    buffering), so a wave keeps U * 2 KiB of weight in flight.
+//  * A wave issues the loads of up to U steps at once (U * 2 KiB of weight),
+//    then consumes them; with the wave counts used, every weight byte of the
+//    call is requested at kernel start.
 //  * swap = 1 puts the weight on the MFMA row side (tokens are columns): each
 //    lane ends with 4 consecutive output columns of one token (8-byte
 //    stores).  swap = 0 puts tokens on the row side (the direct A*B^T form).
@@ -45,8 +46,13 @@ template <typename T> __device__ inline void st_agent(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16-byte load that is always issued (the address is valid whatever `ok`
+// says) and then zeroed when `ok` is false: straight-line code, so the
+// compiler knows how many loads are outstanding and can wait for one batch
+// while the next is in flight.
 __device__ inline i32x4 ld16(const uint8_t* p, bool ok) {
-  return ok ? *(const i32x4*)p : i32x4{0, 0, 0, 0};
+  const i32x4 v = *(const i32x4*)p;
+  return ok ? v : i32x4{0, 0, 0, 0};
 }
 __device__ inline i32x8 cat(i32x4 a, i32x4 b) {
   return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -97,21 +103,31 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
       }
   }
 
-  i32x8 wcur[U], xcur[U][NTT], wnxt[U], xnxt[U][NTT];
-  float scur[U][NTT][NS], snxt[U][NTT][NS];
-  auto load_batch = [&](int t0, i32x8* w, i32x8 (*x)[NTT], float (*sc)[NTT][NS]) {
+  i32x8 wb[U], xb[U][NTT];
+  float sc[U][NTT][NS];
+  // Issue a whole batch of U steps' loads (straight-line, always in bounds),
+  // then consume it.  A wave's steps usually fit one batch, so every load of
+  // the kernel is in flight at once and each MFMA waits only for its own
+  // step.
+  auto load_batch = [&](int t0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u;
       const bool live = t < my;
-      const int st = beg + wave + t * W;
+      // Steps past this wave's range re-read its first step (valid: my > 0)
+      // and are zeroed; chunks past the end of the row re-read the row's
+      // last 16 bytes and are zeroed.
+      const int st = beg + wave + (live ? t : 0) * W;
       const int64_t off = (int64_t)st * STEPB;
-      const bool ok0 = live && (off + g * 32 < KB);
-      const bool ok1 = live && (off + g * 32 + 16 < KB);
-      w[u] = cat(ld16(wp + off, ok0), ld16(wp + off + 16, ok1));
+      const int64_t o0 = off + g * 32, o1 = o0 + 16;
+      const bool ok0 = live && (o0 < KB);
+      const bool ok1 = live && (o1 < KB);
+      const int64_t c0 = (o0 < KB ? o0 : KB - 16) - g * 32;
+      const int64_t c1 = (o1 < KB ? o1 : KB - 16) - g * 32;
+      wb[u] = cat(ld16(wp + c0, ok0), ld16(wp + c1, ok1));
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt)
-        x[u][tt] = cat(ld16(xp[tt] + off, ok0), ld16(xp[tt] + off + 16, ok1));
+        xb[u][tt] = cat(ld16(xp[tt] + c0, ok0), ld16(xp[tt] + c1, ok1));
       if constexpr (BLOCK) {
         const float sbv = live ? sb_p[st] : 0.f;
 #pragma unroll
@@ -126,36 +142,23 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) acc[tt] = C{0, 0, 0, 0};
 
-  load_batch(0, wcur, xcur, scur);
   for (int t0 = 0; t0 < my; t0 += U) {
-    if (t0 + U < my) load_batch(t0 + U, wnxt, xnxt, snxt);
+    load_batch(t0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const typename MF::Frag w0 = MF::prep(lo16(wcur[u])), w1 = MF::prep(hi16(wcur[u]));
+      const typename MF::Frag w0 = MF::prep(lo16(wb[u])), w1 = MF::prep(hi16(wb[u]));
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
-        const typename MF::Frag x0 = MF::prep(lo16(xcur[u][tt])), x1 = MF::prep(hi16(xcur[u][tt]));
+        const typename MF::Frag x0 = MF::prep(lo16(xb[u][tt])), x1 = MF::prep(hi16(xb[u][tt]));
         if constexpr (BLOCK) {
           // One step is one 128-wide K block: scale its exact partial sum.
           C p = SWAP ? MF::mma(w0, x0, C{0, 0, 0, 0}) : MF::mma(x0, w0, C{0, 0, 0, 0});
           p = SWAP ? MF::mma(w1, x1, p) : MF::mma(x1, w1, p);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[tt][r] += scur[u][tt][SWAP ? 0 : r] * p[r];
+          for (int r = 0; r < 4; ++r) acc[tt][r] += sc[u][tt][SWAP ? 0 : r] * p[r];
         } else {
           acc[tt] = SWAP ? MF::mma(w0, x0, acc[tt]) : MF::mma(x0, w0, acc[tt]);
           acc[tt] = SWAP ? MF::mma(w1, x1, acc[tt]) : MF::mma(x1, w1, acc[tt]);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      wcur[u] = wnxt[u];
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
-        xcur[u][tt] = xnxt[u][tt];
-        if constexpr (BLOCK) {
-#pragma unroll
-          for (int r = 0; r < NS; ++r) scur[u][tt][r] = snxt[u][tt][r];
         }
       }
     }
@@ -295,7 +298,10 @@ hipError_t launch_d(const Variant& v, const Call& c, int split, hipStream_t s) {
   return hipGetLastError();
 }
 
-#define LG_DECODE_WAVES(X, QK, NTT, SW) X(QK, NTT, SW, 4, 4) X(QK, NTT, SW, 8, 4) X(QK, NTT, SW, 4, 8) X(QK, NTT, SW, 8, 2)
+// Compiled (waves, unroll) pairs.
+#define LG_DECODE_WAVES(X, QK, NTT, SW) \
+  X(QK, NTT, SW, 4, 4) X(QK, NTT, SW, 4, 8) X(QK, NTT, SW, 8, 1) X(QK, NTT, SW, 8, 2) \
+  X(QK, NTT, SW, 8, 4) X(QK, NTT, SW, 16, 1) X(QK, NTT, SW, 16, 2)
 
 template <int QK, int NTT, bool SW>
 hipError_t launch_dq(const Variant& v, const Call& c, int split, hipStream_t s) {
@@ -320,7 +326,9 @@ bool decode_supported(int qk, int ntok_tiles, int swap, int waves, int unroll) {
   (void)swap;
   if (ntok_tiles < 1 || ntok_tiles > 2) return false;
   return (waves == 4 && unroll == 4) || (waves == 8 && unroll == 4) ||
-         (waves == 4 && unroll == 8) || (waves == 8 && unroll == 2);
+         (waves == 4 && unroll == 8) || (waves == 8 && unroll == 2) ||
+         (waves == 16 && unroll == 2) || (waves == 16 && unroll == 1) ||
+         (waves == 8 && unroll == 1);
 }
 
 int decode_auto_split(const Call& c, int waves) {

@@ -102,15 +102,23 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
   }
   i32x4 a_reg[S::A_LD], b_reg[S::B_LD];
 
+  // Loads are always issued from a valid address (a chunk past the end of
+  // the row re-reads the row's last 16 bytes) and zeroed afterwards, so the
+  // loop body is straight-line code.
   auto gload = [&](int kt) {
     const int64_t off = (int64_t)kt * ROWB;
     const bool ok = off + ck * 16 < KB;
+    const int64_t c = ok ? off : KB - 16 - ck * 16;
 #pragma unroll
-    for (int i = 0; i < S::A_LD; ++i)
-      a_reg[i] = ok ? *(const i32x4*)(a_src[i] + off) : i32x4{0, 0, 0, 0};
+    for (int i = 0; i < S::A_LD; ++i) {
+      const i32x4 v = *(const i32x4*)(a_src[i] + c);
+      a_reg[i] = ok ? v : i32x4{0, 0, 0, 0};
+    }
 #pragma unroll
-    for (int i = 0; i < S::B_LD; ++i)
-      b_reg[i] = ok ? *(const i32x4*)(b_src[i] + off) : i32x4{0, 0, 0, 0};
+    for (int i = 0; i < S::B_LD; ++i) {
+      const i32x4 v = *(const i32x4*)(b_src[i] + c);
+      b_reg[i] = ok ? v : i32x4{0, 0, 0, 0};
+    }
   };
   auto lstore = [&](int buf) {
     uint8_t* base = lds + buf * S::STAGE;

@@ -1,0 +1,151 @@
+"""Offline sweep: time candidate variants per shape on the GPU and write the
+shape-keyed variant table (configs/mi355x.cfg).
+
+The per-shape search of the vLLM linear-backend write-up (sections "Одно
+ядро вместо трёх вариантов" and "Как автотюнер ищет конфиги") benchmarks
+configurations the way they run in production -- replayed from a graph --
+and keeps the best per shape.  Here the space is small and enumerated
+(swap-AB, split-K factor and reduction, waves, unroll for M <= 32; tile
+shapes otherwise); each candidate is timed as a HIP-graph replay of calls
+over a rotation of weight copies larger than the 256 MB MALL.
+
+    python -m epilogue_scaled_gemm_amd.sweep [--out PATH] [--workloads 2,3,4]
+"""
+import argparse
+import os
+import sys
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+ROTATION_BYTES = 384 << 20
+
+DECODE_CANDIDATES = [
+    f"decode swap={sw} split={sp} reduce={rd} waves={w} unroll={u}"
+    for sw in (1,)
+    for sp, rd in ((1, "twopass"), (2, "twopass"), (4, "twopass"))
+    for w, u in ((4, 4), (4, 8), (8, 1), (8, 2), (8, 4), (16, 1), (16, 2))
+] + ["decode swap=0 split=1 reduce=twopass waves=8 unroll=4",
+     "decode swap=1 split=2 reduce=lastwg waves=8 unroll=2",
+     "decode swap=1 split=2 reduce=atomic waves=8 unroll=2"]
+
+TILE_CANDIDATES = ["tile bm=256 bn=256 wm=2 wn=2", "tile bm=128 bn=256 wm=2 wn=2",
+                   "tile bm=256 bn=128 wm=2 wn=2", "tile bm=128 bn=128 wm=2 wn=2",
+                   "tile bm=64 bn=128 wm=1 wn=4", "tile bm=64 bn=64 wm=2 wn=2"]
+
+
+def _dev(torch, a):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def time_variant(torch, h, p, ops, Bs, spec, reps=10):
+    """Seconds per call of `spec` on problem p (graph replay, rotating B)."""
+    h.set_force(spec)
+    C = torch.empty((p.M, p.N), dtype=torch.int16, device="cuda")
+
+    def call(i):
+        h.run(ops["A"], Bs[i % len(Bs)], C, quant=p.quant, act=p.act, sa=ops["sa"],
+              sb=ops["sb"], alpha=p.alpha, bias=ops["bias"], residual=ops["residual"])
+
+    call(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(len(Bs)):
+            call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        g.replay()
+    e.record()
+    e.synchronize()
+    h.set_force(None)
+    return s.elapsed_time(e) / 1e3 / reps / len(Bs)
+
+
+def sweep(workloads, out_path, reps, log=print):
+    import torch
+    import synth
+    import epilogue_scaled_gemm_amd as lg
+
+    h = lg.Handle()
+    entries = []
+    # Context: a plain device copy (read + write) of 256 MiB and of 24 MiB.
+    for mib in (256, 24):
+        src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(20):
+            dst.copy_(src)
+        e.record()
+        e.synchronize()
+        t = s.elapsed_time(e) / 1e3 / 20
+        log(f"copy {mib} MiB: {t * 1e6:.1f} us, {2 * (mib << 20) / t / 1e12:.2f} TB/s (read+write)")
+        del src, dst
+    for cfg in workloads:
+        c = synth.CONFIGS[cfg]
+        for M in c["Ms"]:
+            p = synth.make(cfg, M)
+            ops = {k: _dev(torch, v) for k, v in p.operands().items() if k != "alpha"}
+            ncopy = max(2, min(32, -(-ROTATION_BYTES // p.B.nbytes)))
+            Bs = [ops["B"]] + [ops["B"].clone() for _ in range(ncopy - 1)]
+            cands = DECODE_CANDIDATES if M <= 32 else TILE_CANDIDATES
+            best = None
+            for spec in cands:
+                try:
+                    t = time_variant(torch, h, p, ops, Bs, spec, reps if M <= 32 else 3)
+                except lg.LinGemmError as ex:
+                    log(f"  skip {spec}: {ex}")
+                    continue
+                log(f"{c['name']} M={M}: {t * 1e6:9.2f} us  {spec}")
+                if best is None or t < best[0]:
+                    best = (t, spec)
+            log(f"BEST {c['name']} M={M}: {best[0] * 1e6:.2f} us  {best[1]}")
+            entries.append((p.quant, M, p.N, p.K, best[1], best[0]))
+            del Bs, ops
+            torch.cuda.empty_cache()
+    h.close()
+    lines = ["# Variant table for MI355X (gfx950), written by epilogue_scaled_gemm_amd.sweep.",
+             "# <quant> <m_lo> <m_hi> <N> <K> <variant>   (first match wins; the",
+             "# built-in defaults follow the measured entries)",
+             "# measured us per call in the trailing comment"]
+    for q, M, N, K, spec, t in entries:
+        lines.append(f"{q:<12} {M:<5} {M:<5} {N:<6} {K:<6} {spec}   # {t * 1e6:.2f} us")
+    lines += ["*            1     32    *      *      decode swap=1 split=1 reduce=twopass waves=8 unroll=2",
+              "block_fp8    33    *     *      *      tile bm=128 bn=128 wm=2 wn=2 group=4",
+              "*            33    256   *      *      tile bm=64 bn=128 wm=1 wn=4 group=4",
+              "*            257   1024  *      *      tile bm=128 bn=128 wm=2 wn=2 group=4",
+              "*            1025  *     *      *      tile bm=256 bn=128 wm=2 wn=2 group=4"]
+    if out_path:
+        os.makedirs(os.path.dirname(out_path), exist_ok=True)
+        with open(out_path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        log(f"wrote {out_path}")
+    return entries
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--workloads", default="1,2,3,4,5")
+    ap.add_argument("--reps", type=int, default=10)
+    a = ap.parse_args()
+    sweep([int(x) for x in a.workloads.split(",")], a.out, a.reps,
+          log=lambda s: print(s, flush=True))
+
+
+if __name__ == "__main__":
+    main()

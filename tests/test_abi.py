@@ -108,10 +108,11 @@ def test_force_and_describe(cpu_handle):
         h.set_force("tile bm=96 bn=96 wm=2 wn=2")  # not a compiled shape
     with pytest.raises(lg.LinGemmError):
         h.set_force("decode split=3")              # not a power of two
-    h.set_force(None)
-    # auto split: 384 row groups of 16 -> 2 slices; 1536 -> 1
+    # auto split (split=0): 384 row groups of 16 -> 2 slices; 1536 -> 1
+    h.set_force("decode swap=1 split=0 reduce=twopass waves=4 unroll=4")
     assert "split=2" in h.describe("fp8_dynamic", 1, 6144, 4096)
     assert "split=1" in h.describe("w8a8_int8", 1, 24576, 4096)
+    h.set_force(None)
 
 
 def test_table_file(tmp_path):
