@@ -150,7 +150,7 @@ def per_shape_table(torch, h, reps):
     import synth
     rows = []
     for cfg in (1, 2, 3, 4, 5):
-        c = synth.CONFIGS[cfg]
+        c = synth.WORKLOADS[cfg]
         wl = Workload(torch, cfg, c["Ms"])
         for M in c["Ms"]:
             R = wl.ncopy
@@ -199,7 +199,7 @@ def cpu_baseline(target_s):
     whole passes of the M sweep, repeated until ~target_s of oracle time."""
     import oracle
     import synth
-    c = synth.CONFIGS[HEAD_CFG]
+    c = synth.WORKLOADS[HEAD_CFG]
     probs = [synth.make(HEAD_CFG, M) for M in c["Ms"]]
     ncols = c["N"]
     done_bytes, elapsed, passes = 0.0, 0.0, 0
@@ -244,7 +244,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.init()
     h = lg.Handle()
-    c = synth.CONFIGS[HEAD_CFG]
+    c = synth.WORKLOADS[HEAD_CFG]
     Ms = list(c["Ms"])
     wl = Workload(torch, HEAD_CFG, Ms)
     R = wl.ncopy

@@ -92,12 +92,19 @@ int select_variant(lin_gemm_t h, int quant, int64_t M, int64_t N, int64_t K, lg:
     if (h->forced) return fail(h, LIN_ERR_UNSUPPORTED, "decode variants need M <= 32");
     v->kind = lg::V_TILE; v->bm = 128; v->bn = 128; v->wm = 2; v->wn = 2;
   }
+  // Block scales are uniform over a decode workgroup's rows only when the
+  // rows sit inside one 128-row scale block.
+  if (v->kind == lg::V_DECODE && quant == LIN_Q_BLOCK_FP8 && 128 % v->rows != 0) {
+    if (h->forced)
+      return fail(h, LIN_ERR_UNSUPPORTED, "block FP8 decode needs rows dividing 128");
+    v->rows = 16;
+  }
   return LIN_OK;
 }
 
 int resolve_split(const lg::Variant& v, const lg::Call& c) {
   if (v.kind != lg::V_DECODE) return 1;
-  int split = v.split > 0 ? v.split : lg::decode_auto_split(c, v.waves);
+  int split = v.split > 0 ? v.split : lg::decode_auto_split(c, v);
   const int64_t steps = (c.KB + 127) / 128;
   while (split > 1 && split > steps) split >>= 1;  // at least one 128-byte step per slice
   return split;
@@ -107,7 +114,7 @@ int resolve_split(const lg::Variant& v, const lg::Call& c) {
 int ensure_workspace(lin_gemm_t h, const lg::Variant& v, const lg::Call& c, int split,
                      hipStream_t s) {
   const size_t need = lg::decode_ws_bytes(v, c, split);
-  const size_t ncnt = (size_t)((c.N + 15) / 16);
+  const size_t ncnt = (size_t)((c.N + v.rows - 1) / v.rows);  // one per row group
   const bool grow_ws = need > h->ws_bytes;
   const bool grow_cnt = split > 1 && ncnt > h->counters_n;
   if (grow_ws || grow_cnt) {

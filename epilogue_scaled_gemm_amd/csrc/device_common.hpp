@@ -271,4 +271,70 @@ __device__ inline void epilogue_one(const Epi& e, int64_t m, int64_t n, AccT v) 
   ((uint16_t*)e.C)[m * e.N + n] = f32_to_h<F16>(y);
 }
 
+// The epilogue operands of a 4-column run C[m][n0 .. n0+4), loaded ahead of
+// time (at kernel start) so the loads' latency overlaps the K loop instead of
+// following it.
+struct EpiPre4 {
+  float sam;
+  float sb[4], bias[4], res[4];
+};
+
+template <bool F16>
+__device__ inline void epilogue_prefetch4(const Epi& e, int64_t m, int64_t n0, EpiPre4& p) {
+  const int64_t mm = m < e.M ? m : e.M - 1;
+  const bool full = (n0 + 4 <= e.N) && (e.N % 4 == 0) && (n0 % 4 == 0);
+  p.sam = 1.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p.sb[i] = 1.f, p.bias[i] = 0.f, p.res[i] = 0.f;
+  if (e.raw) return;
+  if (e.scale_mode == 1) {
+    p.sam = e.sa[mm];
+    if (full) {
+      const f32x4 s = *(const f32x4*)(e.sb + n0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p.sb[i] = s[i];
+    } else {
+      for (int i = 0; i < 4; ++i) if (n0 + i < e.N) p.sb[i] = e.sb[n0 + i];
+    }
+  }
+  if (e.bias) {
+    if (full) load_h<4, F16>(e.bias + n0, p.bias);
+    else for (int i = 0; i < 4; ++i) if (n0 + i < e.N) p.bias[i] = h_to_f32<F16>(e.bias[n0 + i]);
+  }
+  if (e.residual) {
+    const uint16_t* rrow = e.residual + mm * e.N;
+    if (full) load_h<4, F16>(rrow + n0, p.res);
+    else for (int i = 0; i < 4; ++i) if (n0 + i < e.N) p.res[i] = h_to_f32<F16>(rrow[n0 + i]);
+  }
+}
+
+// Epilogue of a 4-column run from prefetched operands (same arithmetic and
+// order as epilogue_run).
+template <bool F16, typename AccT>
+__device__ inline void epilogue_run4_pre(const Epi& e, int64_t m, int64_t n0, const AccT* v,
+                                         const EpiPre4& p) {
+  if (m >= e.M) return;
+  if (e.raw) {
+    AccT* crow = (AccT*)e.C + m * e.N;
+    for (int i = 0; i < 4; ++i)
+      if (n0 + i < e.N) crow[n0 + i] = v[i];
+    return;
+  }
+  float y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    y[i] = (float)v[i];
+    if (e.scale_mode == 1) y[i] *= p.sam * p.sb[i];
+    y[i] += p.bias[i];
+    y[i] = act_apply(e.act, y[i]) * e.alpha + p.res[i];
+  }
+  uint16_t* crow = (uint16_t*)e.C + m * e.N;
+  if ((n0 + 4 <= e.N) && (e.N % 4 == 0) && (n0 % 4 == 0)) {
+    store_h<4, F16>(crow + n0, y);
+  } else {
+    for (int i = 0; i < 4; ++i)
+      if (n0 + i < e.N) crow[n0 + i] = f32_to_h<F16>(y[i]);
+  }
+}
+
 }  // namespace lg

@@ -70,6 +70,7 @@ bool parse_variant(const std::string& spec, Variant* out, std::string* err) {
     else if (k == "split") v.split = xi;
     else if (k == "waves") v.waves = xi;
     else if (k == "unroll") v.unroll = xi;
+    else if (k == "rows") v.rows = xi;
     else { *err = "unknown key '" + k + "'"; return false; }
   }
   if (v.kind == V_TILE && !tile_supported(0, v.bm, v.bn, v.wm, v.wn)) {
@@ -77,8 +78,8 @@ bool parse_variant(const std::string& spec, Variant* out, std::string* err) {
     return false;
   }
   if (v.kind == V_DECODE) {
-    if (!decode_supported(0, 1, v.swap, v.waves, v.unroll)) {
-      *err = "decode waves/unroll not compiled: " + spec;
+    if (!decode_supported(v.swap, v.waves, v.unroll, v.rows)) {
+      *err = "decode swap/waves/unroll/rows not compiled: " + spec;
       return false;
     }
     if (v.split > 256 || (v.split & (v.split - 1)) != 0) {
@@ -97,7 +98,7 @@ std::string format_variant(const Variant& v, int split) {
        << " group=" << v.group_m;
   } else {
     os << "decode swap=" << v.swap << " split=" << split << " reduce=" << reduce_name(v.reduce)
-       << " waves=" << v.waves << " unroll=" << v.unroll;
+       << " waves=" << v.waves << " unroll=" << v.unroll << " rows=" << v.rows;
   }
   return os.str();
 }
@@ -149,16 +150,17 @@ const char* builtin_table() {
   return R"TABLE(
 # quant        m_lo m_hi N     K      variant
 # measured entries (offline sweep on MI355X, graph replay, rotating weights)
-fp8_dynamic    1    8    6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=1
-fp8_dynamic    9    32   6144  4096   decode swap=1 split=1 reduce=twopass waves=4 unroll=8
-w8a8_int8      1    16   24576 4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=2
-w8a8_int8      17   32   24576 4096   decode swap=1 split=1 reduce=twopass waves=16 unroll=1
-block_fp8      1    4    4096  12288  decode swap=1 split=1 reduce=twopass waves=16 unroll=1
-block_fp8      5    16   4096  12288  decode swap=1 split=1 reduce=twopass waves=8 unroll=2
-block_fp8      17   32   4096  12288  decode swap=1 split=1 reduce=twopass waves=16 unroll=2
+fp8_dynamic    1    1    6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=1 rows=12
+fp8_dynamic    2    32   6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=1 rows=24
+w8a8_int8      1    4    24576 4096   decode swap=0 split=1 reduce=twopass waves=8 unroll=2 rows=16
+w8a8_int8      5    16   24576 4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=1 rows=32
+w8a8_int8      17   32   24576 4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=2 rows=32
+block_fp8      1    16   4096  12288  decode swap=1 split=1 reduce=twopass waves=16 unroll=1 rows=16
+block_fp8      17   32   4096  12288  decode swap=1 split=2 reduce=twopass waves=8 unroll=2 rows=32
 block_fp8      33   1024 4096  12288  tile bm=64 bn=64 wm=2 wn=2 group=4
-block_fp8      1025 *    4096  12288  tile bm=64 bn=128 wm=1 wn=4 group=4
+block_fp8      1025 *    4096  12288  tile bm=128 bn=128 wm=2 wn=2 group=4
 bf16           1025 *    4096  4096   tile bm=128 bn=128 wm=2 wn=2 group=4
+bf16           33   256  256   512    tile bm=64 bn=64 wm=2 wn=2 group=4
 # defaults
 *              1    32   *     *      decode swap=1 split=1 reduce=twopass waves=8 unroll=2
 block_fp8      33   *    *     *      tile bm=128 bn=128 wm=2 wn=2 group=4

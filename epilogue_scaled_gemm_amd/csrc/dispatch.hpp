@@ -14,7 +14,7 @@
 // where the variant spec is
 //   tile   bm=<tokens> bn=<weight rows> wm=<waves> wn=<waves> [group=<g>]
 //   decode swap=<0|1> split=<0=auto|1..256> reduce=<lastwg|atomic|twopass>
-//          waves=<w> unroll=<u>
+//          waves=<w> unroll=<u> rows=<weight rows per workgroup, 4..64, 4 | rows>
 // The first matching entry wins.
 #pragma once
 

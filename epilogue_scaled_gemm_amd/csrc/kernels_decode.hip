@@ -10,11 +10,12 @@
 // ядро вместо трёх вариантов" and "Гибридный диспатч").
 //
 // gfx950 design:
-//  * A workgroup owns 16 weight rows (one MFMA tile) and a slice of K; its W
-//    waves split that slice in 128-byte steps (in-workgroup split-K), so each
-//    weight byte is loaded by exactly one lane, straight from HBM into
-//    registers (no LDS staging: there is no reuse to stage for).  Every lane
-//    loads 32 contiguous bytes per step; 4 lanes cover a 128-byte line.
+//  * A workgroup owns 16*rows weight rows and a slice of K; its W waves split
+//    that slice into contiguous runs of 128-byte steps (in-workgroup
+//    split-K), so each weight byte is loaded by exactly one lane, straight
+//    from HBM into registers (no LDS staging: there is no reuse to stage
+//    for).  Every lane loads 32 contiguous bytes per step; 4 lanes cover a
+//    128-byte line; each activation slice feeds all 16*rows weight rows.
 //  * A wave issues the loads of up to U steps at once (U * 2 KiB of weight),
 //    then consumes them; with the wave counts used, every weight byte of the
 //    call is requested at kernel start.
@@ -54,35 +55,53 @@ __device__ inline i32x4 ld16(const uint8_t* p, bool ok) {
   const i32x4 v = *(const i32x4*)p;
   return ok ? v : i32x4{0, 0, 0, 0};
 }
+
 __device__ inline i32x8 cat(i32x4 a, i32x4 b) {
   return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-template <int QK, int NTT, bool SWAP, int W, int U>
+template <int QK, int NTT, bool SWAP, int W, int U, int RT>
 __global__ __launch_bounds__(W * 64) void decode_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int64_t M, int64_t N,
-    int64_t KB, int split, int steps_per_split, int reduce, Epi e, void* __restrict__ ws,
-    int* __restrict__ counters) {
+    int64_t KB, int rpw, int split, int steps_per_split, int reduce, Epi e,
+    void* __restrict__ ws, int* __restrict__ counters) {
   using MF = Mfma<QK>;
   using C = typename MF::C;
   using AccT = typename QTraits<QK>::Acc;
   constexpr bool F16 = QTraits<QK>::out_f16;
   constexpr bool BLOCK = (QK == QK_FP8_BLOCK);
-  constexpr int NS = SWAP ? 1 : 4;  // block scales per token tile per lane
-  __shared__ AccT red[W][NTT * 4][64];
+  constexpr int NS = SWAP ? 1 : 4;    // block scales per token tile per lane
+  constexpr int NTILE = RT * NTT;     // 16x16 output tiles per workgroup
+  __shared__ AccT red[W][NTILE * 4][64];
+  __shared__ int arrival;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  // This workgroup's weight rows are [n0, n0 + rpw) (rpw <= 16 * RT, a
+  // multiple of 4); rows of its MFMA tiles past that are masked.
+  const int64_t n0 = (int64_t)blockIdx.x * rpw;
+  const int64_t nend = min(n0 + rpw, N);
   const int sidx = blockIdx.y;
   const int total_steps = (int)((KB + STEPB - 1) / STEPB);
   const int beg = sidx * steps_per_split;
   const int end = min(beg + steps_per_split, total_steps);
   const int span = end - beg;
-  const int my = span > wave ? (span - wave + W - 1) / W : 0;  // steps of this wave
+  // Wave w takes a contiguous run of steps [first, first + my) of the slice.
+  const int per = (span + W - 1) / W;
+  const int first = beg + wave * per;
+  const int my = max(0, min(per, end - first));  // steps of this wave
 
-  const uint8_t* wp = B + min(n0 + l16, N - 1) * KB + g * 32;
+  // Masked rows load a row this workgroup reads anyway (a cache hit, no
+  // extra HBM traffic) and are zeroed.
+  const uint8_t* wp[RT];
+  bool wrow[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int64_t row = n0 + rt * 16 + l16;
+    wrow[rt] = row < nend;
+    wp[rt] = B + (wrow[rt] ? row : n0) * KB + g * 32;
+  }
   const uint8_t* xp[NTT];
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) xp[tt] = A + min((int64_t)(tt * 16 + l16), M - 1) * KB + g * 32;
@@ -103,12 +122,12 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
       }
   }
 
-  i32x8 wb[U], xb[U][NTT];
+  i32x8 wb[U][RT], xb[U][NTT];
   float sc[U][NTT][NS];
   // Issue a whole batch of U steps' loads (straight-line, always in bounds),
   // then consume it.  A wave's steps usually fit one batch, so every load of
   // the kernel is in flight at once and each MFMA waits only for its own
-  // step.
+  // step.  Each activation slice feeds RT weight tiles.
   auto load_batch = [&](int t0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -117,14 +136,16 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
       // Steps past this wave's range re-read its first step (valid: my > 0)
       // and are zeroed; chunks past the end of the row re-read the row's
       // last 16 bytes and are zeroed.
-      const int st = beg + wave + (live ? t : 0) * W;
+      const int st = first + (live ? t : 0);
       const int64_t off = (int64_t)st * STEPB;
       const int64_t o0 = off + g * 32, o1 = o0 + 16;
       const bool ok0 = live && (o0 < KB);
       const bool ok1 = live && (o1 < KB);
       const int64_t c0 = (o0 < KB ? o0 : KB - 16) - g * 32;
       const int64_t c1 = (o1 < KB ? o1 : KB - 16) - g * 32;
-      wb[u] = cat(ld16(wp + c0, ok0), ld16(wp + c1, ok1));
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        wb[u][rt] = cat(ld16(wp[rt] + c0, ok0 && wrow[rt]), ld16(wp[rt] + c1, ok1 && wrow[rt]));
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt)
         xb[u][tt] = cat(ld16(xp[tt] + c0, ok0), ld16(xp[tt] + c1, ok1));
@@ -138,126 +159,172 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
     }
   };
 
-  C acc[NTT];
+  // Epilogue operands of the tiles this wave will finish (q = wave, wave +
+  // W, ...), fetched now so their latency hides behind the K loop.
+  constexpr int QPW = (NTILE + W - 1) / W;  // tiles per wave, at most
+  EpiPre4 pre[QPW];
+  // (The two-pass reduction with split > 1 runs its epilogue in
+  // splitk_reduce instead.)
+  const bool fin_here = split == 1 || reduce != R_TWOPASS;
+  if (SWAP && fin_here) {
 #pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) acc[tt] = C{0, 0, 0, 0};
+    for (int i = 0; i < QPW; ++i) {
+      const int q = wave + i * W;
+      const int64_t nr = n0 + (q / NTT) * 16 + g * 4;
+      if (q < NTILE && nr < nend) epilogue_prefetch4<F16>(e, (q % NTT) * 16 + l16, nr, pre[i]);
+    }
+  }
+
+  C acc[RT][NTT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) acc[rt][tt] = C{0, 0, 0, 0};
 
   for (int t0 = 0; t0 < my; t0 += U) {
     load_batch(t0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const typename MF::Frag w0 = MF::prep(lo16(wb[u])), w1 = MF::prep(hi16(wb[u]));
+      typename MF::Frag x0[NTT], x1[NTT];
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
-        const typename MF::Frag x0 = MF::prep(lo16(xb[u][tt])), x1 = MF::prep(hi16(xb[u][tt]));
-        if constexpr (BLOCK) {
-          // One step is one 128-wide K block: scale its exact partial sum.
-          C p = SWAP ? MF::mma(w0, x0, C{0, 0, 0, 0}) : MF::mma(x0, w0, C{0, 0, 0, 0});
-          p = SWAP ? MF::mma(w1, x1, p) : MF::mma(x1, w1, p);
+        x0[tt] = MF::prep(lo16(xb[u][tt]));
+        x1[tt] = MF::prep(hi16(xb[u][tt]));
+      }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[tt][r] += sc[u][tt][SWAP ? 0 : r] * p[r];
-        } else {
-          acc[tt] = SWAP ? MF::mma(w0, x0, acc[tt]) : MF::mma(x0, w0, acc[tt]);
-          acc[tt] = SWAP ? MF::mma(w1, x1, acc[tt]) : MF::mma(x1, w1, acc[tt]);
+      for (int rt = 0; rt < RT; ++rt) {
+        const typename MF::Frag w0 = MF::prep(lo16(wb[u][rt])), w1 = MF::prep(hi16(wb[u][rt]));
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) {
+          if constexpr (BLOCK) {
+            // One step is one 128-wide K block: scale its exact partial sum.
+            C p = SWAP ? MF::mma(w0, x0[tt], C{0, 0, 0, 0}) : MF::mma(x0[tt], w0, C{0, 0, 0, 0});
+            p = SWAP ? MF::mma(w1, x1[tt], p) : MF::mma(x1[tt], w1, p);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[rt][tt][r] += sc[u][tt][SWAP ? 0 : r] * p[r];
+          } else {
+            C a = acc[rt][tt];
+            a = SWAP ? MF::mma(w0, x0[tt], a) : MF::mma(x0[tt], w0, a);
+            acc[rt][tt] = SWAP ? MF::mma(w1, x1[tt], a) : MF::mma(x1[tt], w1, a);
+          }
         }
       }
     }
   }
 
-  // In-workgroup reduction of the W waves' partial tiles, in wave order.
+  // In-workgroup reduction, in wave order; wave w then owns tiles
+  // q = w, w + W, ... (q = rt * NTT + tt) for the rest of the kernel.
 #pragma unroll
-  for (int tt = 0; tt < NTT; ++tt)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][tt * 4 + r][lane] = (AccT)acc[tt][r];
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][(rt * NTT + tt) * 4 + r][lane] = (AccT)acc[rt][tt][r];
   __syncthreads();
-  if (wave != 0) return;
-  AccT v[NTT * 4];
-#pragma unroll
-  for (int i = 0; i < NTT * 4; ++i) {
-    AccT s = red[0][i][lane];
-#pragma unroll
-    for (int w = 1; w < W; ++w) s += red[w][i][lane];
-    v[i] = s;
-  }
 
-  // Output coordinates of v[tt*4 + r].
-  auto coord = [&](int tt, int r, int64_t& m, int64_t& n) {
-    if (SWAP) { m = tt * 16 + l16; n = n0 + g * 4 + r; }
-    else { m = tt * 16 + g * 4 + r; n = n0 + l16; }
+  // Output coordinates of value r of tile q.
+  auto coord = [&](int q, int r, int64_t& m, int64_t& n) {
+    const int rt = q / NTT, tt = q % NTT;
+    if (SWAP) { m = tt * 16 + l16; n = n0 + rt * 16 + g * 4 + r; }
+    else { m = tt * 16 + g * 4 + r; n = n0 + rt * 16 + l16; }
   };
-  auto finish = [&]() {
+  auto finish = [&](int q, const AccT* v) {
+    if (SWAP) {
+      int64_t m, n;
+      coord(q, 0, m, n);
+      if (n < nend) epilogue_run<4, F16>(e, m, n, v);
+    } else {
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) {
-      if (SWAP) {
-        epilogue_run<4, F16>(e, tt * 16 + l16, n0 + g * 4, &v[tt * 4]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int64_t m, n;
-          coord(tt, r, m, n);
-          epilogue_one<F16>(e, m, n, v[tt * 4 + r]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        int64_t m, n;
+        coord(q, r, m, n);
+        if (n < nend) epilogue_one<F16>(e, m, n, v[r]);
       }
+    }
+  };
+  auto reduce_tile = [&](int q, AccT* v) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      AccT s = red[0][q * 4 + r][lane];
+#pragma unroll
+      for (int w = 1; w < W; ++w) s += red[w][q * 4 + r][lane];
+      v[r] = s;
     }
   };
 
   if (split == 1) {
-    finish();
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      const int q = wave + i * W;
+      if (q >= NTILE) break;
+      AccT v[4];
+      reduce_tile(q, v);
+      const int64_t nr = n0 + (q / NTT) * 16 + g * 4;
+      if (!SWAP) finish(q, v);
+      else if (nr < nend) epilogue_run4_pre<F16>(e, (q % NTT) * 16 + l16, nr, v, pre[i]);
+    }
     return;
   }
 
   AccT* wsa = (AccT*)ws;
-  if (reduce == R_ATOMIC) {
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int64_t m, n;
-        coord(tt, r, m, n);
-        if (m < M && n < N)
-          __hip_atomic_fetch_add(wsa + m * N + n, v[tt * 4 + r], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-      }
-  } else {
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int64_t m, n;
-        coord(tt, r, m, n);
-        if (m < M && n < N) st_agent(wsa + ((int64_t)sidx * M + m) * N + n, v[tt * 4 + r]);
-      }
-    if (reduce == R_TWOPASS) return;
-  }
-
-  // Arrival: the last of the split workgroups of this row group finishes.
-  int old = 0;
-  if (lane == 0)
-    old = __hip_atomic_fetch_add(counters + blockIdx.x, 1, __ATOMIC_ACQ_REL,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-  old = __shfl(old, 0);
-  if (old != split - 1) return;
-  __atomic_thread_fence(__ATOMIC_ACQUIRE);
-
-#pragma unroll
-  for (int tt = 0; tt < NTT; ++tt)
+  for (int q = wave; q < NTILE; q += W) {
+    AccT v[4];
+    reduce_tile(q, v);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       int64_t m, n;
-      coord(tt, r, m, n);
+      coord(q, r, m, n);
+      if (m < M && n < nend) {
+        if (reduce == R_ATOMIC)
+          __hip_atomic_fetch_add(wsa + m * N + n, v[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          st_agent(wsa + ((int64_t)sidx * M + m) * N + n, v[r]);
+      }
+    }
+  }
+  if (reduce == R_TWOPASS) return;
+
+  // Arrival: the last of the split workgroups of this row group finishes.
+  // Every partial is written, and later read, with agent-scope atomic
+  // stores / loads, which are coherent across the XCDs' L2s by themselves;
+  // what must hold is that a workgroup's partials are complete before its
+  // counter increment is.  Each wave therefore waits for its own stores to
+  // be acknowledged (s_waitcnt 0) before the barrier, and thread 0 then
+  // increments the counter.  A generic agent-scope release / acquire would
+  // also write back and invalidate the whole L2 in every workgroup, which
+  // costs more than the reduction saves.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    arrival = __hip_atomic_fetch_add(counters + blockIdx.x, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (arrival != split - 1) return;
+  for (int q = wave; q < NTILE; q += W) {
+    AccT v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int64_t m, n;
+      coord(q, r, m, n);
       AccT s = 0;
-      if (m < M && n < N) {
+      if (m < M && n < nend) {
         if (reduce == R_ATOMIC) {
           s = ld_agent(wsa + m * N + n);
           st_agent(wsa + m * N + n, (AccT)0);
         } else {
-          for (int q = 0; q < split; ++q) s += ld_agent(wsa + ((int64_t)q * M + m) * N + n);
+          for (int qq = 0; qq < split; ++qq) s += ld_agent(wsa + ((int64_t)qq * M + m) * N + n);
         }
       }
-      v[tt * 4 + r] = s;
+      v[r] = s;
     }
-  finish();
-  if (lane == 0) st_agent(counters + blockIdx.x, 0);
+    const int i = (q - wave) / W;
+    const int64_t nr = n0 + (q / NTT) * 16 + g * 4;
+    if (!SWAP) finish(q, v);
+    else if (nr < nend) epilogue_run4_pre<F16>(e, (q % NTT) * 16 + l16, nr, v, pre[i]);
+  }
+  if (threadIdx.x == 0) st_agent(counters + blockIdx.x, 0);
 }
 
 // Second pass of the two-pass reduction: sum the split partials of 4
@@ -282,14 +349,14 @@ __global__ __launch_bounds__(256) void splitk_reduce(const void* __restrict__ ws
   epilogue_run<4, QTraits<QK>::out_f16>(e, m, n, v);
 }
 
-template <int QK, int NTT, bool SWAP, int W, int U>
+template <int QK, int NTT, bool SWAP, int W, int U, int RT>
 hipError_t launch_d(const Variant& v, const Call& c, int split, hipStream_t s) {
-  const int groups = (int)((c.N + 15) / 16);
+  const int groups = (int)((c.N + v.rows - 1) / v.rows);
   const int total_steps = (int)((c.KB + STEPB - 1) / STEPB);
   const int sps = (total_steps + split - 1) / split;
-  hipLaunchKernelGGL((decode_kernel<QK, NTT, SWAP, W, U>), dim3(groups, split), dim3(W * 64), 0,
-                     s, (const uint8_t*)c.A, (const uint8_t*)c.B, c.M, c.N, c.KB, split, sps,
-                     v.reduce, c.epi, c.ws, c.counters);
+  hipLaunchKernelGGL((decode_kernel<QK, NTT, SWAP, W, U, RT>), dim3(groups, split), dim3(W * 64),
+                     0, s, (const uint8_t*)c.A, (const uint8_t*)c.B, c.M, c.N, c.KB, v.rows, split,
+                     sps, v.reduce, c.epi, c.ws, c.counters);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || split == 1 || v.reduce != R_TWOPASS) return err;
   const int64_t threads = c.M * ((c.N + 3) / 4);
@@ -298,44 +365,49 @@ hipError_t launch_d(const Variant& v, const Call& c, int split, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Compiled (waves, unroll) pairs.
-#define LG_DECODE_WAVES(X, QK, NTT, SW) \
-  X(QK, NTT, SW, 4, 4) X(QK, NTT, SW, 4, 8) X(QK, NTT, SW, 8, 1) X(QK, NTT, SW, 8, 2) \
-  X(QK, NTT, SW, 8, 4) X(QK, NTT, SW, 16, 1) X(QK, NTT, SW, 16, 2)
+// Compiled (waves, unroll, 16-row tiles) triples with swap-AB, and the one
+// direct-orientation variant.  A variant's rows-per-workgroup value picks the
+// tile count: up to 16 rows -> 1 tile, 32 -> 2, 64 -> 4.
+#define LG_DECODE_SWAP(X, QK, NTT) \
+  X(QK, NTT, true, 8, 1, 1) X(QK, NTT, true, 8, 2, 1) X(QK, NTT, true, 4, 4, 1) \
+  X(QK, NTT, true, 16, 1, 1) X(QK, NTT, true, 8, 1, 2) X(QK, NTT, true, 4, 2, 2) \
+  X(QK, NTT, true, 8, 2, 2) X(QK, NTT, true, 4, 1, 4) X(QK, NTT, true, 8, 1, 4) \
+  X(QK, NTT, false, 8, 2, 1)
 
-template <int QK, int NTT, bool SW>
+// Tiles per workgroup for a rows-per-workgroup value: 1, 2 or 4.
+inline int tiles_for(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
+
+#define LG_DECODE_TRY(qk, ntt, sw, w, u, rt)                                             \
+  if (v.swap == (sw ? 1 : 0) && v.waves == w && v.unroll == u && tiles_for(v.rows) == rt) \
+    return launch_d<qk, ntt, sw, w, u, rt>(v, c, split, s);
+
+template <int QK, int NTT>
 hipError_t launch_dq(const Variant& v, const Call& c, int split, hipStream_t s) {
-#define LG_TRY(qk, ntt, sw, w, u) \
-  if (v.waves == w && v.unroll == u) return launch_d<qk, ntt, sw, w, u>(v, c, split, s);
-  LG_DECODE_WAVES(LG_TRY, QK, NTT, SW)
-#undef LG_TRY
+  LG_DECODE_SWAP(LG_DECODE_TRY, QK, NTT)
   return hipErrorInvalidValue;
 }
 
 template <int QK>
 hipError_t launch_q(const Variant& v, const Call& c, int split, hipStream_t s) {
-  const int ntt = c.M <= 16 ? 1 : 2;
-  if (ntt == 1) return v.swap ? launch_dq<QK, 1, true>(v, c, split, s) : launch_dq<QK, 1, false>(v, c, split, s);
-  return v.swap ? launch_dq<QK, 2, true>(v, c, split, s) : launch_dq<QK, 2, false>(v, c, split, s);
+  return c.M <= 16 ? launch_dq<QK, 1>(v, c, split, s) : launch_dq<QK, 2>(v, c, split, s);
 }
 
 }  // namespace
 
-bool decode_supported(int qk, int ntok_tiles, int swap, int waves, int unroll) {
-  (void)qk;
-  (void)swap;
-  if (ntok_tiles < 1 || ntok_tiles > 2) return false;
-  return (waves == 4 && unroll == 4) || (waves == 8 && unroll == 4) ||
-         (waves == 4 && unroll == 8) || (waves == 8 && unroll == 2) ||
-         (waves == 16 && unroll == 2) || (waves == 16 && unroll == 1) ||
-         (waves == 8 && unroll == 1);
+bool decode_supported(int swap, int waves, int unroll, int rows) {
+  if (rows < 4 || rows > 64 || rows % 4 != 0) return false;
+#define LG_DECODE_HAS(qk, ntt, sw, w, u, rt) \
+  if (swap == (sw ? 1 : 0) && waves == w && unroll == u && tiles_for(rows) == rt) return true;
+  LG_DECODE_SWAP(LG_DECODE_HAS, 0, 1)
+#undef LG_DECODE_HAS
+  return false;
 }
 
-int decode_auto_split(const Call& c, int waves) {
-  const int64_t groups = (c.N + 15) / 16;
+int decode_auto_split(const Call& c, const Variant& v) {
+  const int64_t groups = (c.N + v.rows - 1) / v.rows;
   const int64_t steps = (c.KB + STEPB - 1) / STEPB;
   int split = 1;
-  while (groups * split < 768 && (int64_t)split * 2 * waves <= steps && split < 16) split *= 2;
+  while (groups * split < 768 && (int64_t)split * 2 * v.waves <= steps && split < 16) split *= 2;
   return split;
 }
 

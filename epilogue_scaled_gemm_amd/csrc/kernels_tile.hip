@@ -16,16 +16,17 @@
 //    lane therefore ends the K loop owning 4*FN consecutive output columns of
 //    one row, so bias / scale / residual loads and the store are 16-byte
 //    vectors.
-//  * K advances in 128-byte stages: global -> registers (16-byte coalesced
-//    loads, 8 lanes per row) -> LDS (double buffered, 16-byte chunks XOR
-//    swizzled so the MFMA fragment reads are free of bank conflicts) ->
-//    registers -> MFMA (16x16x32 bf16/fp16, 16x16x64 int8; e4m3 is widened
-//    exactly to bf16 in registers and uses the 16x16x32 bf16 MFMA).
+//  * K advances in 128-byte stages: buffer loads straight into LDS (no
+//    staging registers; 8 lanes per 128-byte row), double buffered, with
+//    16-byte chunks XOR swizzled so the MFMA fragment reads are free of bank
+//    conflicts -> registers -> MFMA (16x16x32 bf16/fp16, 16x16x64 int8;
+//    e4m3 is widened exactly to bf16 in registers and uses the 16x16x32 bf16
+//    MFMA).
 //  * Workgroup ids are remapped so that each XCD (ids are dealt round-robin
 //    over the 8 XCDs) gets a contiguous, grouped block of tiles, which keeps
 //    the operand panels it shares in its own L2.
-//  * Rows past M / N are clamped on load and masked on store; 16-byte chunks
-//    past the end of K read as zero.
+//  * Rows past M / N and 16-byte chunks past the end of K read as zero
+//    (buffer bounds); rows past M / N are masked on store.
 #include "launch.hpp"
 
 namespace lg {
@@ -79,53 +80,50 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
   const int64_t m0 = (int64_t)(first_m + within % gm) * BM;
   const int64_t n0 = (int64_t)(within / gm) * BN;
 
-  // Global -> LDS copy slots: thread t copies chunk t % 8 of rows t / 8 + i * NT / 8.
-  const int ck = tid & 7;
-  const int r0 = tid >> 3;
-  constexpr int RSTEP = S::NT / 8;
-  const uint8_t* a_src[S::A_LD];
-  const uint8_t* b_src[S::B_LD];
-  int a_dst[S::A_LD], b_dst[S::B_LD];
+  // Global -> LDS: buffer loads that write straight into LDS (no staging
+  // registers).  One instruction moves 8 rows x 128 bytes: lane i lands at
+  // LDS row i / 8, 16-byte position i % 8, and fetches the global chunk
+  // that the swizzle puts there.  The buffer resources cover only this
+  // tile's valid rows, and chunks past the end of K get an out-of-range
+  // offset, so both read as zero.
+  constexpr int NW = WM * WN;
+  constexpr int A_OCT = BM / 8 / NW, B_OCT = BN / 8 / NW;  // 8-row groups per wave per stage
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "direct-load split");
+  const int a_rows = (int)min((int64_t)BM, M - m0), b_rows = (int)min((int64_t)BN, N - n0);
+  const __amdgpu_buffer_rsrc_t rsrc_a =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * KB), (short)0, (int)(a_rows * KB), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc_b =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(B + n0 * KB), (short)0, (int)(b_rows * KB), 0x00020000);
+  int a_off[A_OCT], b_off[B_OCT], a_chk[A_OCT], b_chk[B_OCT];
 #pragma unroll
-  for (int i = 0; i < S::A_LD; ++i) {
-    const int r = r0 + i * RSTEP;
-    const int64_t gr = min(m0 + r, M - 1);
-    a_src[i] = A + gr * KB + ck * 16;
-    a_dst[i] = r * ROWB + ((ck ^ swz_act(r)) << 4);
+  for (int i = 0; i < A_OCT; ++i) {
+    const int r = (wave * A_OCT + i) * 8 + (lane >> 3);
+    a_chk[i] = ((lane & 7) ^ swz_act(r)) << 4;
+    a_off[i] = r * (int)KB + a_chk[i];
   }
 #pragma unroll
-  for (int i = 0; i < S::B_LD; ++i) {
-    const int r = r0 + i * RSTEP;
-    const int64_t gr = min(n0 + r, N - 1);
-    b_src[i] = B + gr * KB + ck * 16;
-    b_dst[i] = BM * ROWB + r * ROWB + ((ck ^ swz_w<FN>(r)) << 4);
+  for (int i = 0; i < B_OCT; ++i) {
+    const int r = (wave * B_OCT + i) * 8 + (lane >> 3);
+    b_chk[i] = ((lane & 7) ^ swz_w<FN>(r)) << 4;
+    b_off[i] = r * (int)KB + b_chk[i];
   }
-  i32x4 a_reg[S::A_LD], b_reg[S::B_LD];
-
-  // Loads are always issued from a valid address (a chunk past the end of
-  // the row re-reads the row's last 16 bytes) and zeroed afterwards, so the
-  // loop body is straight-line code.
-  auto gload = [&](int kt) {
-    const int64_t off = (int64_t)kt * ROWB;
-    const bool ok = off + ck * 16 < KB;
-    const int64_t c = ok ? off : KB - 16 - ck * 16;
-#pragma unroll
-    for (int i = 0; i < S::A_LD; ++i) {
-      const i32x4 v = *(const i32x4*)(a_src[i] + c);
-      a_reg[i] = ok ? v : i32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < S::B_LD; ++i) {
-      const i32x4 v = *(const i32x4*)(b_src[i] + c);
-      b_reg[i] = ok ? v : i32x4{0, 0, 0, 0};
-    }
-  };
-  auto lstore = [&](int buf) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto dload = [&](int kt, int buf) {
     uint8_t* base = lds + buf * S::STAGE;
+    const int koff = kt * ROWB;
 #pragma unroll
-    for (int i = 0; i < S::A_LD; ++i) *(i32x4*)(base + a_dst[i]) = a_reg[i];
+    for (int i = 0; i < A_OCT; ++i) {
+      const int off = (koff + a_chk[i] < KB) ? a_off[i] + koff : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_void*)(base + (wave * A_OCT + i) * 1024),
+                                               16, off, 0, 0, 0);
+    }
 #pragma unroll
-    for (int i = 0; i < S::B_LD; ++i) *(i32x4*)(base + b_dst[i]) = b_reg[i];
+    for (int i = 0; i < B_OCT; ++i) {
+      const int off = (koff + b_chk[i] < KB) ? b_off[i] + koff : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b,
+                                               (lds_void*)(base + BM * ROWB + (wave * B_OCT + i) * 1024),
+                                               16, off, 0, 0, 0);
+    }
   };
 
   // Fragment rows (within the stage) of this lane.
@@ -177,14 +175,14 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
     for (int j = 0; j < FN; ++j) acc[i][j] = C{0, 0, 0, 0};
 
   const int KT = (int)((KB + ROWB - 1) / ROWB);
-  gload(0);
+  dload(0, 0);
   sload(0, sa_cur, sb_cur);
-  lstore(0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
     const uint8_t* base = lds + (kt & 1) * S::STAGE;
     if (kt + 1 < KT) {
-      gload(kt + 1);
+      dload(kt + 1, (kt + 1) & 1);
       sload(kt + 1, sa_nxt, sb_nxt);
     }
     if constexpr (!BLOCK) {
@@ -222,7 +220,9 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
         }
       }
     }
-    if (kt + 1 < KT) lstore((kt + 1) & 1);
+    // This wave's loads of the next stage have landed in LDS; the barrier
+    // then covers every wave's loads and every wave's reads of this stage.
+    __builtin_amdgcn_s_waitcnt(0);
     if constexpr (BLOCK) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i];

@@ -20,8 +20,10 @@ struct Variant {
   int bm = 128, bn = 128, wm = 2, wn = 2, group_m = 4;
   // decode family (M <= 32): swap-AB orientation, split-K factor across
   // workgroups (0 = choose from the shape), reduction, waves per workgroup
-  // (the in-workgroup K split) and steps of 128 bytes loaded per batch
-  int swap = 1, split = 0, reduce = R_LASTWG, waves = 4, unroll = 4;
+  // (the in-workgroup K split), steps of 128 bytes loaded per batch, and
+  // weight rows per workgroup (4..64, a multiple of 4; each activation load
+  // feeds all of them)
+  int swap = 1, split = 0, reduce = R_TWOPASS, waves = 8, unroll = 2, rows = 16;
 };
 
 struct Call {
@@ -32,7 +34,7 @@ struct Call {
   int qk;           // QKind
   Epi epi;
   void* ws;         // split-K workspace (decode family)
-  int* counters;    // arrival counters, one per 16-row weight group
+  int* counters;    // arrival counters, one per workgroup row group
 };
 
 // Tile family (kernels_tile.hip).
@@ -40,8 +42,8 @@ bool tile_supported(int qk, int bm, int bn, int wm, int wn);
 hipError_t launch_tile(const Variant& v, const Call& c, hipStream_t s);
 
 // Decode family (kernels_decode.hip).
-bool decode_supported(int qk, int ntok_tiles, int swap, int waves, int unroll);
-int decode_auto_split(const Call& c, int waves);
+bool decode_supported(int swap, int waves, int unroll, int rows);
+int decode_auto_split(const Call& c, const Variant& v);
 size_t decode_ws_bytes(const Variant& v, const Call& c, int split);
 hipError_t launch_decode(const Variant& v, const Call& c, int split, hipStream_t s);
 

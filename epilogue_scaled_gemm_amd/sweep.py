@@ -24,14 +24,16 @@ if ROOT not in sys.path:
 
 ROTATION_BYTES = 384 << 20
 
+# (waves, unroll, rows per workgroup)
+DECODE_SHAPES = [(8, 1, 16), (8, 2, 16), (4, 4, 16), (16, 1, 16), (8, 1, 8), (8, 1, 12),
+                 (16, 1, 12), (16, 1, 8), (8, 2, 8), (8, 1, 32), (4, 2, 32), (8, 2, 32),
+                 (8, 1, 24), (4, 1, 64), (8, 1, 64)]
 DECODE_CANDIDATES = [
-    f"decode swap={sw} split={sp} reduce={rd} waves={w} unroll={u}"
-    for sw in (1,)
-    for sp, rd in ((1, "twopass"), (2, "twopass"), (4, "twopass"))
-    for w, u in ((4, 4), (4, 8), (8, 1), (8, 2), (8, 4), (16, 1), (16, 2))
-] + ["decode swap=0 split=1 reduce=twopass waves=8 unroll=4",
-     "decode swap=1 split=2 reduce=lastwg waves=8 unroll=2",
-     "decode swap=1 split=2 reduce=atomic waves=8 unroll=2"]
+    f"decode swap=1 split={sp} reduce=twopass waves={w} unroll={u} rows={r}"
+    for sp in (1, 2) for w, u, r in DECODE_SHAPES
+] + ["decode swap=0 split=1 reduce=twopass waves=8 unroll=2",
+     "decode swap=1 split=2 reduce=lastwg waves=8 unroll=1 rows=32",
+     "decode swap=1 split=2 reduce=atomic waves=8 unroll=1 rows=32"]
 
 TILE_CANDIDATES = ["tile bm=256 bn=256 wm=2 wn=2", "tile bm=128 bn=256 wm=2 wn=2",
                    "tile bm=256 bn=128 wm=2 wn=2", "tile bm=128 bn=128 wm=2 wn=2",
@@ -73,7 +75,7 @@ def time_variant(torch, h, p, ops, Bs, spec, reps=10):
     return s.elapsed_time(e) / 1e3 / reps / len(Bs)
 
 
-def sweep(workloads, out_path, reps, log=print):
+def sweep(workloads, out_path, reps, log=print, max_m=None):
     import torch
     import synth
     import epilogue_scaled_gemm_amd as lg
@@ -96,8 +98,10 @@ def sweep(workloads, out_path, reps, log=print):
         log(f"copy {mib} MiB: {t * 1e6:.1f} us, {2 * (mib << 20) / t / 1e12:.2f} TB/s (read+write)")
         del src, dst
     for cfg in workloads:
-        c = synth.CONFIGS[cfg]
+        c = synth.WORKLOADS[cfg]
         for M in c["Ms"]:
+            if max_m is not None and M > max_m:
+                continue
             p = synth.make(cfg, M)
             ops = {k: _dev(torch, v) for k, v in p.operands().items() if k != "alpha"}
             ncopy = max(2, min(32, -(-ROTATION_BYTES // p.B.nbytes)))
@@ -105,6 +109,8 @@ def sweep(workloads, out_path, reps, log=print):
             cands = DECODE_CANDIDATES if M <= 32 else TILE_CANDIDATES
             best = None
             for spec in cands:
+                if p.quant == "block_fp8" and "rows=" in spec and 128 % int(spec.split("rows=")[1]):
+                    continue
                 try:
                     t = time_variant(torch, h, p, ops, Bs, spec, reps if M <= 32 else 3)
                 except lg.LinGemmError as ex:
@@ -124,7 +130,7 @@ def sweep(workloads, out_path, reps, log=print):
              "# measured us per call in the trailing comment"]
     for q, M, N, K, spec, t in entries:
         lines.append(f"{q:<12} {M:<5} {M:<5} {N:<6} {K:<6} {spec}   # {t * 1e6:.2f} us")
-    lines += ["*            1     32    *      *      decode swap=1 split=1 reduce=twopass waves=8 unroll=2",
+    lines += ["*            1     32    *      *      decode swap=1 split=1 reduce=twopass waves=8 unroll=2 rows=16",
               "block_fp8    33    *     *      *      tile bm=128 bn=128 wm=2 wn=2 group=4",
               "*            33    256   *      *      tile bm=64 bn=128 wm=1 wn=4 group=4",
               "*            257   1024  *      *      tile bm=128 bn=128 wm=2 wn=2 group=4",
@@ -142,9 +148,10 @@ def main():
     ap.add_argument("--out", default=None)
     ap.add_argument("--workloads", default="1,2,3,4,5")
     ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--max-m", type=int, default=None, help="only token counts up to this")
     a = ap.parse_args()
     sweep([int(x) for x in a.workloads.split(",")], a.out, a.reps,
-          log=lambda s: print(s, flush=True))
+          log=lambda s: print(s, flush=True), max_m=a.max_m)
 
 
 if __name__ == "__main__":

@@ -31,7 +31,7 @@ import torch
 E4M3_MAX = 448.0
 INT8_MAX = 127.0
 
-CONFIGS = {
+WORKLOADS = {
     1: dict(name="tiny_bf16_gelu", quant="bf16", act="gelu_tanh", N=256, K=512,
             Ms=(64,), bias=True, residual=False, alpha=1.0, dist="uniform"),
     2: dict(name="fp8_dynamic_decode", quant="fp8_dynamic", act="none", N=6144, K=4096,
@@ -157,7 +157,7 @@ def _draw(rng, shape, dist, std):
 
 @functools.lru_cache(maxsize=4)
 def _weight(cfg: int, quant: str):
-    c = CONFIGS[cfg]
+    c = WORKLOADS[cfg]
     rng = np.random.Generator(np.random.PCG64(1000 * cfg))
     w = _draw(rng, (c["N"], c["K"]), c["dist"], 0.02)
     B, sb = encode(quant, w, "b")
@@ -174,7 +174,7 @@ def make(cfg: int, M: int = None, quant: str = None) -> Problem:
     ``quant`` overrides the workload's quant mode (e.g. fp16 instead of bf16)
     with the same draws.
     """
-    c = CONFIGS[cfg]
+    c = WORKLOADS[cfg]
     M = c["Ms"][0] if M is None else int(M)
     quant = quant or c["quant"]
     B, sb, bias = _weight(cfg, quant)

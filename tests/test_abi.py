@@ -101,7 +101,7 @@ def test_force_and_describe(cpu_handle):
     assert h.describe("bf16", 4096, 4096, 4096).startswith("tile")
     h.set_force("decode swap=0 split=4 reduce=twopass waves=8 unroll=2")
     assert h.describe("w8a8_int8", 4, 24576, 4096) == \
-        "decode swap=0 split=4 reduce=twopass waves=8 unroll=2"
+        "decode swap=0 split=4 reduce=twopass waves=8 unroll=2 rows=16"
     with pytest.raises(lg.LinGemmError):
         h.describe("bf16", 64, 128, 128)          # forced decode with M > 32
     with pytest.raises(lg.LinGemmError):
@@ -109,7 +109,7 @@ def test_force_and_describe(cpu_handle):
     with pytest.raises(lg.LinGemmError):
         h.set_force("decode split=3")              # not a power of two
     # auto split (split=0): 384 row groups of 16 -> 2 slices; 1536 -> 1
-    h.set_force("decode swap=1 split=0 reduce=twopass waves=4 unroll=4")
+    h.set_force("decode swap=1 split=0 reduce=twopass waves=4 unroll=4 rows=16")
     assert "split=2" in h.describe("fp8_dynamic", 1, 6144, 4096)
     assert "split=1" in h.describe("w8a8_int8", 1, 24576, 4096)
     h.set_force(None)
@@ -117,11 +117,11 @@ def test_force_and_describe(cpu_handle):
 
 def test_table_file(tmp_path):
     good = tmp_path / "t.cfg"
-    good.write_text("# test table\nfp8_dynamic 1 32 6144 4096 decode swap=0 split=8 "
-                    "reduce=atomic waves=8 unroll=4\n* 1 * * * tile bm=64 bn=64 wm=2 wn=2\n")
+    good.write_text("# test table\nfp8_dynamic 1 32 6144 4096 decode swap=1 split=8 "
+                    "reduce=atomic waves=8 unroll=1 rows=64\n* 1 * * * tile bm=64 bn=64 wm=2 wn=2\n")
     h = lg.Handle(str(good))
     assert h.describe("fp8_dynamic", 3, 6144, 4096) == \
-        "decode swap=0 split=8 reduce=atomic waves=8 unroll=4"
+        "decode swap=1 split=8 reduce=atomic waves=8 unroll=1 rows=64"
     assert h.describe("fp8_dynamic", 3, 6144, 8192).startswith("tile bm=64 bn=64")
     h.close()
     bad = tmp_path / "bad.cfg"

@@ -29,8 +29,8 @@ def handle():
     h.close()
 
 
-CASES = [(1, 64)] + [(2, m) for m in synth.CONFIGS[2]["Ms"]] + \
-        [(3, m) for m in synth.CONFIGS[3]["Ms"]] + [(4, m) for m in synth.CONFIGS[4]["Ms"]] + \
+CASES = [(1, 64)] + [(2, m) for m in synth.WORKLOADS[2]["Ms"]] + \
+        [(3, m) for m in synth.WORKLOADS[3]["Ms"]] + [(4, m) for m in synth.WORKLOADS[4]["Ms"]] + \
         [(5, 4096)]
 SAMPLED = {(4, 2048), (5, 4096)}
 
@@ -50,7 +50,7 @@ def test_workload_parity(handle, cfg, M):
         assert_close(g, r, p.name)
 
 
-@pytest.mark.parametrize("M", synth.CONFIGS[3]["Ms"])
+@pytest.mark.parametrize("M", synth.WORKLOADS[3]["Ms"])
 def test_int8_accumulator_bit_exact(handle, M):
     p = synth.make(3, M)
     C = run(handle, p, raw=True)
@@ -88,7 +88,7 @@ def test_zero_m_is_noop(handle):
 
 
 @pytest.mark.parametrize("spec", [None, "tile bm=64 bn=128 wm=1 wn=4",
-                                  "decode swap=0 split=2 reduce=twopass waves=4 unroll=4"])
+                                  "decode swap=0 split=2 reduce=twopass waves=8 unroll=2"])
 def test_e4m3_every_code_through_the_path(handle, spec):
     # A holds every finite e4m3 code; B is the identity (1.0 = 0x38), unit
     # scales, raw accumulator: C must equal the exact decoded codes.

@@ -26,14 +26,17 @@ def handle():
     h.close()
 
 
-DECODE_SPECS = [
-    f"decode swap={sw} split={sp} reduce={rd} waves={w} unroll={u}"
-    for sw in (1, 0)
-    for sp, rd in ((1, "lastwg"), (2, "lastwg"), (4, "atomic"), (8, "twopass"), (16, "lastwg"),
-                   (4, "twopass"), (2, "atomic"))
-    for w, u in ((4, 4), (8, 2))
-] + ["decode swap=1 split=2 reduce=lastwg waves=8 unroll=4",
-     "decode swap=0 split=1 reduce=lastwg waves=4 unroll=8"]
+# Every compiled (swap, waves, unroll, rows) combination, with the split-K
+# factors and cross-workgroup reductions spread over them.
+# (rows = weight rows per workgroup; 8, 12 and 24 leave tile rows masked)
+DECODE_SHAPES = [(1, 8, 1, 16), (1, 8, 2, 8), (1, 4, 4, 12), (1, 16, 1, 16), (1, 8, 1, 32),
+                 (1, 4, 2, 24), (1, 8, 2, 32), (1, 4, 1, 64), (1, 8, 1, 64), (0, 8, 2, 16),
+                 (0, 8, 2, 12)]
+SPLITS = [(1, "twopass"), (2, "lastwg"), (4, "atomic"), (8, "twopass"), (16, "lastwg"),
+          (4, "twopass"), (2, "atomic")]
+DECODE_SPECS = [f"decode swap={sw} split={sp} reduce={rd} waves={w} unroll={u} rows={r}"
+                for i, (sw, w, u, r) in enumerate(DECODE_SHAPES)
+                for sp, rd in (SPLITS[i % len(SPLITS)], SPLITS[(i + 3) % len(SPLITS)], (1, "twopass"))]
 
 DECODE_PROBLEMS = [
     ("fp8_dynamic", "none", 1, 6144, 4096, True, False),
@@ -64,6 +67,12 @@ def test_decode_variants_match_oracle(handle, decode_refs, prob):
     d = upload(p)
     try:
         for spec in DECODE_SPECS:
+            rows = int(spec.split("rows=")[1])
+            if p.quant == "block_fp8" and 128 % rows:
+                with pytest.raises(lg.LinGemmError):
+                    handle.set_force(spec)
+                    run(handle, p, d)
+                continue
             handle.set_force(spec)
             print(f"[variant] {p.name} {spec}", flush=True)
             C = run(handle, p, d)
@@ -80,12 +89,12 @@ def test_deterministic_reductions_repeat_bitwise(handle, reduce):
     p = synth.make(2, 16)
     d = upload(p)
     try:
-        handle.set_force(f"decode swap=1 split=8 reduce={reduce} waves=4 unroll=4")
+        handle.set_force(f"decode swap=1 split=8 reduce={reduce} waves=8 unroll=1 rows=32")
         first = run(handle, p, d).cpu()
         for _ in range(5):
             assert torch.equal(run(handle, p, d).cpu(), first)
         # and split-K agrees with the unsplit kernel to fp32 reassociation
-        handle.set_force("decode swap=1 split=1 reduce=lastwg waves=4 unroll=4")
+        handle.set_force("decode swap=1 split=1 reduce=twopass waves=8 unroll=1 rows=32")
         unsplit = decode_out(run(handle, p, d), p.quant)
         assert_close(decode_out(first, p.quant), unsplit, "split vs unsplit")
     finally:
@@ -96,9 +105,9 @@ def test_swap_ab_equals_direct(handle):
     p = synth.make(3, 8)
     d = upload(p)
     try:
-        handle.set_force("decode swap=1 split=1 reduce=lastwg waves=4 unroll=4")
+        handle.set_force("decode swap=1 split=1 reduce=twopass waves=8 unroll=2")
         a = run(handle, p, d, raw=True).cpu()
-        handle.set_force("decode swap=0 split=1 reduce=lastwg waves=4 unroll=4")
+        handle.set_force("decode swap=0 split=1 reduce=twopass waves=8 unroll=2")
         b = run(handle, p, d, raw=True).cpu()
         assert torch.equal(a, b)
     finally:
@@ -142,7 +151,7 @@ def test_tile_and_decode_agree_on_small_m(handle):
     try:
         handle.set_force("tile bm=64 bn=128 wm=1 wn=4")
         t = decode_out(run(handle, p, d), p.quant)
-        handle.set_force("decode swap=1 split=4 reduce=lastwg waves=4 unroll=4")
+        handle.set_force("decode swap=1 split=4 reduce=lastwg waves=8 unroll=1 rows=64")
         dd = decode_out(run(handle, p, d), p.quant)
         ref, _ = reference(p)
         assert_close(t, ref, "tile")

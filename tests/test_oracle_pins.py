@@ -288,8 +288,8 @@ def test_printed_sizes():
 
 
 def test_synth_workload_shapes_follow_pages():
-    assert list(synth.CONFIGS[2]["Ms"]) == FACTS["num_tokens_tuned"]["value"]
-    assert list(synth.CONFIGS[3]["Ms"]) == FACTS["num_tokens_tuned"]["value"]
+    assert list(synth.WORKLOADS[2]["Ms"]) == FACTS["num_tokens_tuned"]["value"]
+    assert list(synth.WORKLOADS[3]["Ms"]) == FACTS["num_tokens_tuned"]["value"]
     p = synth.make(4, 1)
     assert p.sa.shape == (1, p.K // FACTS["scale_blocks"]["value"]["activation"][1])
     assert p.sb.shape == (p.N // 128, p.K // 128)
