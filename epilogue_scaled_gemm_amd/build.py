@@ -23,6 +23,9 @@ SOURCES = ["kernels_tile.hip", "kernels_decode.hip", "kernels_misc.hip", "dispat
 # Packed fp32 instructions are disabled for all device code.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # let the fully unrolled tile epilogues unroll (keeps accumulators
+         # in registers instead of a dynamically indexed scratch array)
+         "-mllvm", "-pragma-unroll-threshold=100000",
          "-I", os.path.join(ROOT, "include")]
 
 

@@ -159,14 +159,14 @@ block_fp8      1    16   4096  12288  decode swap=1 split=1 reduce=twopass waves
 block_fp8      17   32   4096  12288  decode swap=1 split=2 reduce=twopass waves=8 unroll=2 rows=32
 block_fp8      33   1024 4096  12288  tile bm=64 bn=64 wm=2 wn=2 group=4
 block_fp8      1025 *    4096  12288  tile bm=128 bn=128 wm=2 wn=2 group=4
-bf16           1025 *    4096  4096   tile bm=128 bn=128 wm=2 wn=2 group=4
+bf16           1025 *    4096  4096   tile bm=256 bn=256 wm=2 wn=4 group=4
 bf16           33   256  256   512    tile bm=64 bn=64 wm=2 wn=2 group=4
 # defaults
 *              1    32   *     *      decode swap=1 split=1 reduce=twopass waves=8 unroll=2
 block_fp8      33   *    *     *      tile bm=128 bn=128 wm=2 wn=2 group=4
 *              33   256  *     *      tile bm=64 bn=128 wm=1 wn=4 group=4
-*              257  1024 *     *      tile bm=128 bn=128 wm=2 wn=2 group=4
-*              1025 *    *     *      tile bm=256 bn=128 wm=2 wn=2 group=4
+*              257  1024 *     *      tile bm=128 bn=128 wm=2 wn=4 group=4
+*              1025 *    *     *      tile bm=256 bn=256 wm=2 wn=4 group=4
 )TABLE";
 }
 

@@ -18,8 +18,8 @@
 //    vectors.
 //  * K advances in 128-byte stages: buffer loads straight into LDS (no
 //    staging registers; 8 lanes per 128-byte row), double buffered, with
-//    16-byte chunks XOR swizzled so the MFMA fragment reads are free of bank
-//    conflicts -> registers -> MFMA (16x16x32 bf16/fp16, 16x16x64 int8;
+//    16-byte chunks XOR swizzled and weight rows stored in fragment order so
+//    the MFMA fragment reads are free of bank conflicts -> registers -> MFMA (16x16x32 bf16/fp16, 16x16x64 int8;
 //    e4m3 is widened exactly to bf16 in registers and uses the 16x16x32 bf16
 //    MFMA).
 //  * Workgroup ids are remapped so that each XCD (ids are dealt round-robin
@@ -46,8 +46,11 @@ struct TileShape {
   static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "load split");
 };
 
-__device__ inline int swz_act(int r) { return r & 7; }
-template <int FN> __device__ inline int swz_w(int r) { return (r / FN) & 7; }
+// 16-byte chunk swizzle of LDS row R: chunk c of row R is stored at position
+// c ^ swz(R).  Distinct for any 16 consecutive rows, so the 16 lanes that
+// read one chunk of 16 consecutive rows in a pass hit 16 different
+// 16-byte bank groups (64 banks x 4 bytes = two 128-byte rows).
+__device__ inline int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 template <int QK, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
@@ -94,17 +97,21 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
       __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * KB), (short)0, (int)(a_rows * KB), 0x00020000);
   const __amdgpu_buffer_rsrc_t rsrc_b =
       __builtin_amdgcn_make_buffer_rsrc((void*)(B + n0 * KB), (short)0, (int)(b_rows * KB), 0x00020000);
+  // Weight rows sit in LDS in the order the fragments read them: within a
+  // wave's TN-row section, LDS row j*16 + l holds weight row l*FN + j.
   int a_off[A_OCT], b_off[B_OCT], a_chk[A_OCT], b_chk[B_OCT];
 #pragma unroll
   for (int i = 0; i < A_OCT; ++i) {
     const int r = (wave * A_OCT + i) * 8 + (lane >> 3);
-    a_chk[i] = ((lane & 7) ^ swz_act(r)) << 4;
+    a_chk[i] = ((lane & 7) ^ swz(r)) << 4;
     a_off[i] = r * (int)KB + a_chk[i];
   }
 #pragma unroll
   for (int i = 0; i < B_OCT; ++i) {
-    const int r = (wave * B_OCT + i) * 8 + (lane >> 3);
-    b_chk[i] = ((lane & 7) ^ swz_w<FN>(r)) << 4;
+    const int R = (wave * B_OCT + i) * 8 + (lane >> 3);  // LDS row in the tile
+    const int sec = R / TN, Rs = R % TN;
+    const int r = sec * TN + (Rs % 16) * FN + Rs / 16;    // weight row in the tile
+    b_chk[i] = ((lane & 7) ^ swz(R)) << 4;
     b_off[i] = r * (int)KB + b_chk[i];
   }
   typedef __attribute__((address_space(3))) void lds_void;
@@ -127,18 +134,20 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
   };
 
   // Fragment rows (within the stage) of this lane.
+  // MFMA row l16 of weight tile j is weight row l16 * FN + j, i.e. LDS row
+  // j * 16 + l16 of the wave's section.
   int fa_row[FM], fw_row[FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) fa_row[i] = wave_m * TM + i * 16 + l16;
 #pragma unroll
-  for (int j = 0; j < FN; ++j) fw_row[j] = wave_n * TN + l16 * FN + j;
+  for (int j = 0; j < FN; ++j) fw_row[j] = wave_n * TN + j * 16 + l16;
   auto a_frag16 = [&](const uint8_t* base, int i, int ch) {
     const int r = fa_row[i];
-    return *(const i32x4*)(base + r * ROWB + ((ch ^ swz_act(r)) << 4));
+    return *(const i32x4*)(base + r * ROWB + ((ch ^ swz(r)) << 4));
   };
   auto w_frag16 = [&](const uint8_t* base, int j, int ch) {
     const int r = fw_row[j];
-    return *(const i32x4*)(base + BM * ROWB + r * ROWB + ((ch ^ swz_w<FN>(r)) << 4));
+    return *(const i32x4*)(base + BM * ROWB + r * ROWB + ((ch ^ swz(r)) << 4));
   };
 
   // Block scales: sb is uniform over a wave's columns, sa varies per lane.
@@ -242,6 +251,10 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
 #pragma unroll
       for (int j = 0; j < FN; ++j) v[r * FN + j] = (AccT)acc[i][j][r];
     epilogue_run<4 * FN, QTraits<QK>::out_f16>(e, m, nb, v);
+    // One accumulator row group at a time: keeps the scheduler from hoisting
+    // every row's residual loads (which would not fit beside the
+    // accumulators).
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -272,7 +285,10 @@ hipError_t launch_t(const Variant& v, const Call& c, hipStream_t s) {
   X(256, 128, 2, 2)       \
   X(128, 128, 2, 2)       \
   X(64, 128, 1, 4)        \
-  X(64, 64, 2, 2)
+  X(64, 64, 2, 2)         \
+  X(256, 256, 2, 4)       \
+  X(256, 128, 2, 4)       \
+  X(128, 128, 2, 4)
 
 template <int QK>
 hipError_t launch_q(const Variant& v, const Call& c, hipStream_t s) {

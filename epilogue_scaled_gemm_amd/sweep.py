@@ -37,7 +37,9 @@ DECODE_CANDIDATES = [
 
 TILE_CANDIDATES = ["tile bm=256 bn=256 wm=2 wn=2", "tile bm=128 bn=256 wm=2 wn=2",
                    "tile bm=256 bn=128 wm=2 wn=2", "tile bm=128 bn=128 wm=2 wn=2",
-                   "tile bm=64 bn=128 wm=1 wn=4", "tile bm=64 bn=64 wm=2 wn=2"]
+                   "tile bm=64 bn=128 wm=1 wn=4", "tile bm=64 bn=64 wm=2 wn=2",
+                   "tile bm=256 bn=256 wm=2 wn=4", "tile bm=256 bn=128 wm=2 wn=4",
+                   "tile bm=128 bn=128 wm=2 wn=4"]
 
 
 def _dev(torch, a):

@@ -116,7 +116,9 @@ def test_swap_ab_equals_direct(handle):
 
 TILE_SPECS = ["tile bm=256 bn=256 wm=2 wn=2", "tile bm=128 bn=256 wm=2 wn=2",
               "tile bm=256 bn=128 wm=2 wn=2", "tile bm=128 bn=128 wm=2 wn=2",
-              "tile bm=64 bn=128 wm=1 wn=4", "tile bm=64 bn=64 wm=2 wn=2"]
+              "tile bm=64 bn=128 wm=1 wn=4", "tile bm=64 bn=64 wm=2 wn=2",
+              "tile bm=256 bn=256 wm=2 wn=4", "tile bm=256 bn=128 wm=2 wn=4",
+              "tile bm=128 bn=128 wm=2 wn=4"]
 TILE_PROBLEMS = [
     ("bf16", "gelu_tanh", 300, 520, 264, True, True, 0.5),
     ("fp16", "silu", 130, 264, 200, True, False, 1.0),
