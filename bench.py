@@ -53,7 +53,40 @@ def parse():
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 --pmc passes: the headline graphs for two "
                          "steps, then a plain 256 MiB device copy that calibrates the counters")
+    ap.add_argument("--counters-prefill", action="store_true",
+                    help="short run for rocprofv3 --pmc passes on the 4096^3 bf16 prefill: two "
+                         "fused calls, two unfused three-kernel calls, then the 256 MiB copy")
     return ap.parse_args()
+
+
+def counters_copy(torch):
+    """A plain 256 MiB device-to-device copy whose counter readings calibrate
+    FETCH_SIZE / WRITE_SIZE (bytes moved are known)."""
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def counters_prefill(torch, h):
+    import synth
+    c = synth.WORKLOADS[5]
+    wl = Workload(torch, 5, c["Ms"], ncopy=2)
+    M = c["Ms"][0]
+    d = wl.dev[M]
+    T = torch.empty_like(d["C"])
+    U = torch.empty_like(d["C"])
+    for r in range(2):
+        wl.call(h, M, r)
+    torch.cuda.synchronize()
+    for r in range(2):
+        h.run_unfused(d["A"], wl.B[r], d["C"], T, U, quant=wl.quant, act=wl.act,
+                      alpha=d["alpha"], bias=wl.bias, residual=d["residual"])
+    torch.cuda.synchronize()
+    counters_copy(torch)
+    print(json.dumps({"counters_run": "prefill", "copy_bytes": 256 << 20,
+                      "fused_algorithmic_bytes": wl.bytes(M),
+                      "tensor_bytes": 2 * M * wl.N, "M": M, "N": wl.N, "K": wl.K}), flush=True)
 
 
 def source_digest():
@@ -122,17 +155,23 @@ class Workload:
         return g
 
 
-def time_graph(torch, g, reps):
-    """Average time (s) of one replay over `reps` replays, by HIP events."""
-    g.replay()
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(reps):
+def time_graphs(torch, graphs, reps):
+    """Median time (s) of one replay of each graph over `reps` rounds of
+    replays, the graphs interleaved within a round so they see the same
+    clock and power state; HIP events bracket every replay."""
+    for g in graphs:
         g.replay()
-    e.record()
-    e.synchronize()
-    return s.elapsed_time(e) / 1e3 / reps
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in graphs] for _ in range(reps)]
+    for r in range(reps):
+        for g, (s, e) in zip(graphs, ev[r]):
+            s.record()
+            g.replay()
+            e.record()
+    torch.cuda.synchronize()
+    return [float(np.median([ev[r][i][0].elapsed_time(ev[r][i][1]) for r in range(reps)])) / 1e3
+            for i in range(len(graphs))]
 
 
 def shape_row(name, quant, M, N, K, t, nbytes, flops, variant, kernel_calls=1):
@@ -154,24 +193,31 @@ def per_shape_table(torch, h, reps):
         wl = Workload(torch, cfg, c["Ms"])
         for M in c["Ms"]:
             R = wl.ncopy
-            g = wl.graph(h, M, R)
-            t = time_graph(torch, g, max(2, reps // (1 if M < 512 else 4))) / R
-            rows.append(shape_row(c["name"], wl.quant, M, wl.N, wl.K, t, wl.bytes(M), wl.flops(M),
-                                  h.describe(wl.quant, M, wl.N, wl.K)))
+            graphs = [wl.graph(h, M, R)]
+            keep = None
+            if cfg == 5:
+                gu, keep = unfused_graph(torch, h, wl, M)
+                graphs.append(gu)
+            ts = time_graphs(torch, graphs, max(3, reps // (1 if M < 512 else 4)))
+            rows.append(shape_row(c["name"], wl.quant, M, wl.N, wl.K, ts[0] / R, wl.bytes(M),
+                                  wl.flops(M), h.describe(wl.quant, M, wl.N, wl.K)))
             print(f"[shape] {rows[-1]}", file=sys.stderr, flush=True)
-            del g
-        if cfg == 5:
-            rows.append(unfused_row(torch, h, wl, reps))
+            if cfg == 5:
+                # compulsory bytes: the fused traffic plus a write and a read of T and of U
+                nbytes = wl.bytes(M) + 2 * 2 * (2 * M * wl.N)
+                rows.append(shape_row("prefill_bf16_unfused_3kernel", wl.quant, M, wl.N, wl.K,
+                                      ts[1] / R, nbytes, wl.flops(M),
+                                      "gemm + bias_act + scale_residual", kernel_calls=3))
+                print(f"[shape] {rows[-1]}", file=sys.stderr, flush=True)
+            del graphs, keep
         del wl
         torch.cuda.empty_cache()
     return rows
 
 
-def unfused_row(torch, h, wl, reps):
-    """The three-kernel path on the prefill problem (GEMM -> T, bias+GELU -> U,
-    0.5*U + residual -> C) and its compulsory bytes (T and U each written
-    once and read once on top of the fused traffic)."""
-    M = wl.Ms[0]
+def unfused_graph(torch, h, wl, M):
+    """A HIP graph of the three-kernel path on the prefill problem (GEMM -> T,
+    bias+GELU -> U, 0.5*U + residual -> C) over the weight rotation."""
     d = wl.dev[M]
     T = torch.empty_like(d["C"])
     U = torch.empty_like(d["C"])
@@ -186,12 +232,7 @@ def unfused_row(torch, h, wl, reps):
     with torch.cuda.graph(g):
         for r in range(wl.ncopy):
             call(r)
-    t = time_graph(torch, g, max(2, reps // 4)) / wl.ncopy
-    nbytes = wl.bytes(M) + 2 * 2 * (2 * M * wl.N)      # + write/read of T and of U
-    row = shape_row("prefill_bf16_unfused_3kernel", wl.quant, M, wl.N, wl.K, t, nbytes,
-                    wl.flops(M), "gemm + bias_act + scale_residual", kernel_calls=3)
-    print(f"[shape] {row}", file=sys.stderr, flush=True)
-    return row
+    return g, (T, U)
 
 
 def cpu_baseline(target_s):
@@ -244,6 +285,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.init()
     h = lg.Handle()
+    if args.counters_prefill:
+        counters_prefill(torch, h)
+        h.close()
+        return
     c = synth.WORKLOADS[HEAD_CFG]
     Ms = list(c["Ms"])
     wl = Workload(torch, HEAD_CFG, Ms)
@@ -259,10 +304,7 @@ def main():
             for M in Ms:
                 graphs[M].replay()
         torch.cuda.synchronize()
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
+        counters_copy(torch)
         print(json.dumps({"counters_run": True, "copy_bytes": 256 << 20,
                           "kernel_bytes": {M: wl.bytes(M) for M in Ms}}), flush=True)
         return
@@ -294,13 +336,16 @@ def main():
     step_bytes = sum(wl.bytes(M) for M in Ms) * R
     value = step_bytes * args.steps / total_s / 1e12
 
-    # Dominant kernel: the decode instantiation with the most time (tokens
-    # <= 16 use one 16-column tile, 17..32 use two; the template arguments
-    # are quant kind 2 = e4m3, token tiles, swap-AB, waves, unroll).
+    # Dominant kernel: the decode instantiation with the most time.  The
+    # template arguments are quant kind (2 = e4m3), token tiles (one 16-token
+    # tile up to M = 16, two up to 32), swap-AB, waves, unroll and 16-row
+    # weight tiles per workgroup (1 up to 16 rows, 2 up to 32, else 4).
     def kernel_name(M):
         v = dict(kv.split("=") for kv in h.describe(wl.quant, M, wl.N, wl.K).split()[1:])
+        rows = int(v["rows"])
+        rt = 1 if rows <= 16 else (2 if rows <= 32 else 4)
         return (f"decode_kernel<2, {1 if M <= 16 else 2}, {'true' if v['swap'] == '1' else 'false'}"
-                f", {v['waves']}, {v['unroll']}>")
+                f", {v['waves']}, {v['unroll']}, {rt}>")
     groups = {}
     for M in Ms:
         groups.setdefault(kernel_name(M), []).append(M)
