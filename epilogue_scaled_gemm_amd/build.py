@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "liblingemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["kernels_tile.hip", "kernels_decode.hip", "kernels_misc.hip", "dispatch.cpp",
+SOURCES = ["kernels_tile.hip", "kernels_pp.hip", "kernels_decode.hip", "kernels_misc.hip", "dispatch.cpp",
            "abi.cpp"]
 
 # Packed fp32 instructions are disabled for all device code.

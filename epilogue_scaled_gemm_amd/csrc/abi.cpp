@@ -75,6 +75,9 @@ int check_shape(lin_gemm_t h, int quant, int64_t M, int64_t N, int64_t K) {
     return fail(h, LIN_ERR_UNSUPPORTED, "int8 needs K <= 131071 (int32 accumulator range)");
   if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31 || K > (int64_t)1 << 31)
     return fail(h, LIN_ERR_UNSUPPORTED, "sizes beyond 2^31");
+  // Tile kernels address a 256-row operand panel with 32-bit buffer offsets.
+  if (K * esize(quant) > ((int64_t)1 << 31) / 256 - 256)
+    return fail(h, LIN_ERR_UNSUPPORTED, "operand rows longer than 8 MiB");
   return LIN_OK;
 }
 
@@ -92,6 +95,18 @@ int select_variant(lin_gemm_t h, int quant, int64_t M, int64_t N, int64_t K, lg:
     if (h->forced) return fail(h, LIN_ERR_UNSUPPORTED, "decode variants need M <= 32");
     v->kind = lg::V_TILE; v->bm = 128; v->bn = 128; v->wm = 2; v->wn = 2;
   }
+  // The ping-pong family covers bf16 / fp16 / int8 and block FP8; split-K
+  // only for block FP8.
+  if (v->kind == lg::V_PP) {
+    const bool ok = lg::pp_supported(qkind(quant)) &&
+                    (quant == LIN_Q_BLOCK_FP8 || v->split <= 1);
+    if (!ok) {
+      if (h->forced)
+        return fail(h, LIN_ERR_UNSUPPORTED,
+                    "pp variants cover bf16, fp16, int8 and block FP8 (split-K for block FP8 only)");
+      v->kind = lg::V_TILE; v->bm = 128; v->bn = 128; v->wm = 2; v->wn = 2;
+    }
+  }
   // Block scales are uniform over a decode workgroup's rows only when the
   // rows sit inside one 128-row scale block.
   if (v->kind == lg::V_DECODE && quant == LIN_Q_BLOCK_FP8 && 128 % v->rows != 0) {
@@ -103,6 +118,12 @@ int select_variant(lin_gemm_t h, int quant, int64_t M, int64_t N, int64_t K, lg:
 }
 
 int resolve_split(const lg::Variant& v, const lg::Call& c) {
+  if (v.kind == lg::V_PP) {
+    int split = v.split > 0 ? v.split : lg::pp_auto_split(c);
+    const int64_t blocks = c.KB / 128;
+    while (split > 1 && split > blocks) split >>= 1;  // at least one scale block per slice
+    return c.qk == lg::QK_FP8_BLOCK ? split : 1;
+  }
   if (v.kind != lg::V_DECODE) return 1;
   int split = v.split > 0 ? v.split : lg::decode_auto_split(c, v);
   const int64_t steps = (c.KB + 127) / 128;
@@ -113,10 +134,11 @@ int resolve_split(const lg::Variant& v, const lg::Call& c) {
 // Make sure the workspace and counters cover this call.
 int ensure_workspace(lin_gemm_t h, const lg::Variant& v, const lg::Call& c, int split,
                      hipStream_t s) {
-  const size_t need = lg::decode_ws_bytes(v, c, split);
+  const bool pp = v.kind == lg::V_PP;
+  const size_t need = pp ? lg::pp_ws_bytes(c, split) : lg::decode_ws_bytes(v, c, split);
   const size_t ncnt = (size_t)((c.N + v.rows - 1) / v.rows);  // one per row group
   const bool grow_ws = need > h->ws_bytes;
-  const bool grow_cnt = split > 1 && ncnt > h->counters_n;
+  const bool grow_cnt = !pp && split > 1 && ncnt > h->counters_n;
   if (grow_ws || grow_cnt) {
     hipError_t e = hipStreamSynchronize(s);  // in-flight calls may still use the old buffers
     if (e != hipSuccess) return hip_fail(h, e, "hipStreamSynchronize");
@@ -148,7 +170,7 @@ int ensure_workspace(lin_gemm_t h, const lg::Variant& v, const lg::Call& c, int 
     hipError_t e = lg::launch_fill_zero(h->counters, n * sizeof(int), s);
     if (e != hipSuccess) return hip_fail(h, e, "counter zero fill");
   }
-  if (split > 1) {
+  if (split > 1 && !pp) {
     // The atomic reduction needs a zero accumulator; the others leave
     // partials behind, so zero again when switching to atomic.
     if (v.reduce == lg::R_ATOMIC && !h->ws_zero) {
@@ -157,6 +179,7 @@ int ensure_workspace(lin_gemm_t h, const lg::Variant& v, const lg::Call& c, int 
     }
     h->ws_zero = (v.reduce == lg::R_ATOMIC);
   }
+  if (split > 1 && pp) h->ws_zero = false;  // slices overwrite the workspace
   return LIN_OK;
 }
 
@@ -249,6 +272,7 @@ int lin_gemm_describe(lin_gemm_t h, int quant_mode, int64_t M, int64_t N, int64_
   if (rc != LIN_OK) return rc;
   lg::Call c{};
   c.M = M; c.N = N; c.K = K; c.KB = K * esize(quant_mode);
+  c.qk = qkind(quant_mode);
   std::string s = lg::format_variant(v, resolve_split(v, c));
   std::snprintf(buf, (size_t)buflen, "%s", s.c_str());
   return LIN_OK;
@@ -285,6 +309,12 @@ int lin_gemm_run(lin_gemm_t h, const void* A, const void* B, const lin_scales_t*
   hipError_t e;
   if (v.kind == lg::V_TILE) {
     e = lg::launch_tile(v, c, s);
+  } else if (v.kind == lg::V_PP) {
+    const int split = resolve_split(v, c);
+    rc = ensure_workspace(h, v, c, split, s);
+    if (rc != LIN_OK) return rc;
+    c.ws = h->ws;
+    e = lg::launch_pp(v, c, split, s);
   } else {
     const int split = resolve_split(v, c);
     rc = ensure_workspace(h, v, c, split, s);
@@ -328,8 +358,13 @@ int lin_gemm_run_unfused(lin_gemm_t h, const void* A, const void* B, const void*
   lg::Variant v;
   rc = select_variant(h, quant_mode, M, N, K, &v);
   if (rc != LIN_OK) return rc;
-  if (v.kind != lg::V_TILE) { v = lg::Variant(); v.kind = lg::V_TILE; }
-  hipError_t e = lg::launch_tile(v, c, s);
+  hipError_t e;
+  if (v.kind == lg::V_PP) {
+    e = lg::launch_pp(v, c, 1, s);
+  } else {
+    if (v.kind != lg::V_TILE) { v = lg::Variant(); v.kind = lg::V_TILE; }
+    e = lg::launch_tile(v, c, s);
+  }
   if (e != hipSuccess) return hip_fail(h, e, "GEMM launch");
   e = lg::launch_bias_act(T, bias, U, M, N, activation, f16, s);
   if (e != hipSuccess) return hip_fail(h, e, "bias+activation launch");

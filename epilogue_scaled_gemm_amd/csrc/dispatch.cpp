@@ -44,6 +44,7 @@ bool parse_variant(const std::string& spec, Variant* out, std::string* err) {
   Variant v;
   if (kind == "tile") v.kind = V_TILE;
   else if (kind == "decode") v.kind = V_DECODE;
+  else if (kind == "pp") v.kind = V_PP;
   else { *err = "unknown variant kind '" + kind + "'"; return false; }
   std::string kv;
   while (is >> kv) {
@@ -77,6 +78,10 @@ bool parse_variant(const std::string& spec, Variant* out, std::string* err) {
     *err = "tile shape not compiled: " + spec;
     return false;
   }
+  if (v.kind == V_PP && (v.split > 16 || (v.split & (v.split - 1)) != 0)) {
+    *err = "pp split must be 0 (auto) or a power of two <= 16: " + spec;
+    return false;
+  }
   if (v.kind == V_DECODE) {
     if (!decode_supported(v.swap, v.waves, v.unroll, v.rows)) {
       *err = "decode swap/waves/unroll/rows not compiled: " + spec;
@@ -96,6 +101,8 @@ std::string format_variant(const Variant& v, int split) {
   if (v.kind == V_TILE) {
     os << "tile bm=" << v.bm << " bn=" << v.bn << " wm=" << v.wm << " wn=" << v.wn
        << " group=" << v.group_m;
+  } else if (v.kind == V_PP) {
+    os << "pp split=" << split << " group=" << v.group_m;
   } else {
     os << "decode swap=" << v.swap << " split=" << split << " reduce=" << reduce_name(v.reduce)
        << " waves=" << v.waves << " unroll=" << v.unroll << " rows=" << v.rows;
@@ -157,15 +164,19 @@ w8a8_int8      5    16   24576 4096   decode swap=1 split=1 reduce=twopass waves
 w8a8_int8      17   32   24576 4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=2 rows=32
 block_fp8      1    16   4096  12288  decode swap=1 split=1 reduce=twopass waves=16 unroll=1 rows=16
 block_fp8      17   32   4096  12288  decode swap=1 split=2 reduce=twopass waves=8 unroll=2 rows=32
-block_fp8      33   1024 4096  12288  tile bm=64 bn=64 wm=2 wn=2 group=4
-block_fp8      1025 *    4096  12288  tile bm=128 bn=128 wm=2 wn=2 group=4
-bf16           1025 *    4096  4096   tile bm=256 bn=256 wm=2 wn=4 group=4
+block_fp8      257  *    4096  12288  pp split=0 group=4
+block_fp8      33   256  4096  12288  tile bm=64 bn=64 wm=2 wn=2 group=4
+bf16           1025 *    4096  4096   pp group=4
 bf16           33   256  256   512    tile bm=64 bn=64 wm=2 wn=2 group=4
 # defaults
 *              1    32   *     *      decode swap=1 split=1 reduce=twopass waves=8 unroll=2
+block_fp8      257  *    *     *      pp split=0 group=4
 block_fp8      33   *    *     *      tile bm=128 bn=128 wm=2 wn=2 group=4
 *              33   256  *     *      tile bm=64 bn=128 wm=1 wn=4 group=4
 *              257  1024 *     *      tile bm=128 bn=128 wm=2 wn=4 group=4
+bf16           1025 *    *     *      pp group=4
+fp16           1025 *    *     *      pp group=4
+w8a8_int8      1025 *    *     *      pp group=4
 *              1025 *    *     *      tile bm=256 bn=256 wm=2 wn=4 group=4
 )TABLE";
 }

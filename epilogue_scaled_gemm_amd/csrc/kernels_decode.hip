@@ -417,6 +417,22 @@ size_t decode_ws_bytes(const Variant& v, const Call& c, int split) {
   return (size_t)split * c.M * c.N * 4;
 }
 
+hipError_t launch_splitk_reduce(int qk, const void* ws, int split, const Epi& e, hipStream_t s) {
+  const int64_t threads = e.M * ((e.N + 3) / 4);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  switch (qk) {
+    case QK_BF16: hipLaunchKernelGGL((splitk_reduce<QK_BF16>), grid, dim3(256), 0, s, ws, split, e); break;
+    case QK_FP16: hipLaunchKernelGGL((splitk_reduce<QK_FP16>), grid, dim3(256), 0, s, ws, split, e); break;
+    case QK_FP8: hipLaunchKernelGGL((splitk_reduce<QK_FP8>), grid, dim3(256), 0, s, ws, split, e); break;
+    case QK_I8: hipLaunchKernelGGL((splitk_reduce<QK_I8>), grid, dim3(256), 0, s, ws, split, e); break;
+    case QK_FP8_BLOCK:
+      hipLaunchKernelGGL((splitk_reduce<QK_FP8_BLOCK>), grid, dim3(256), 0, s, ws, split, e);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const Variant& v, const Call& c, int split, hipStream_t s) {
   switch (c.qk) {
     case QK_BF16: return launch_q<QK_BF16>(v, c, split, s);

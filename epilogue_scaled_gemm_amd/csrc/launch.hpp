@@ -10,13 +10,15 @@
 
 namespace lg {
 
-enum VariantKind : int { V_TILE = 0, V_DECODE = 1 };
+enum VariantKind : int { V_TILE = 0, V_DECODE = 1, V_PP = 2 };
 // Cross-workgroup split-K reductions of the decode family.
 enum Reduce : int { R_NONE = 0, R_LASTWG = 1, R_ATOMIC = 2, R_TWOPASS = 3 };
 
 struct Variant {
   int kind = V_TILE;
   // tile family: workgroup tile BM (tokens) x BN (weight rows), WM x WN waves
+  // (the ping-pong family has a fixed tile per quant mode and uses only
+  // group_m and split; split = 0 picks the split-K factor from the shape)
   int bm = 128, bn = 128, wm = 2, wn = 2, group_m = 4;
   // decode family (M <= 32): swap-AB orientation, split-K factor across
   // workgroups (0 = choose from the shape), reduction, waves per workgroup
@@ -41,11 +43,21 @@ struct Call {
 bool tile_supported(int qk, int bm, int bn, int wm, int wn);
 hipError_t launch_tile(const Variant& v, const Call& c, hipStream_t s);
 
+// Ping-pong family (kernels_pp.hip): bf16 / fp16 / int8 256x256 tiles and
+// block FP8 256x128 tiles with optional split-K over the scale blocks.
+bool pp_supported(int qk);
+int pp_auto_split(const Call& c);
+size_t pp_ws_bytes(const Call& c, int split);
+hipError_t launch_pp(const Variant& v, const Call& c, int split, hipStream_t s);
+
 // Decode family (kernels_decode.hip).
 bool decode_supported(int swap, int waves, int unroll, int rows);
 int decode_auto_split(const Call& c, const Variant& v);
 size_t decode_ws_bytes(const Variant& v, const Call& c, int split);
 hipError_t launch_decode(const Variant& v, const Call& c, int split, hipStream_t s);
+// Second pass of a two-pass split-K reduction: sums the fp32 / int32 slices
+// [split][M][N] in slice order and applies the epilogue.
+hipError_t launch_splitk_reduce(int qk, const void* ws, int split, const Epi& e, hipStream_t s);
 
 // Unfused three-kernel path and utilities (kernels_misc.hip).
 hipError_t launch_bias_act(const void* T, const void* bias, void* U, int64_t M, int64_t N,

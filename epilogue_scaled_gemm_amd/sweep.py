@@ -39,7 +39,8 @@ TILE_CANDIDATES = ["tile bm=256 bn=256 wm=2 wn=2", "tile bm=128 bn=256 wm=2 wn=2
                    "tile bm=256 bn=128 wm=2 wn=2", "tile bm=128 bn=128 wm=2 wn=2",
                    "tile bm=64 bn=128 wm=1 wn=4", "tile bm=64 bn=64 wm=2 wn=2",
                    "tile bm=256 bn=256 wm=2 wn=4", "tile bm=256 bn=128 wm=2 wn=4",
-                   "tile bm=128 bn=128 wm=2 wn=4"]
+                   "tile bm=128 bn=128 wm=2 wn=4", "pp split=1 group=4", "pp split=2 group=4",
+                   "pp split=4 group=4", "pp split=8 group=4"]
 
 
 def _dev(torch, a):
@@ -50,31 +51,50 @@ def _dev(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def time_variant(torch, h, p, ops, Bs, spec, reps=10):
-    """Seconds per call of `spec` on problem p (graph replay, rotating B)."""
+def capture_variant(torch, h, p, ops, Bs, spec):
+    """A HIP graph of one call of `spec` per weight copy (rotating B), and its
+    output buffer.  Raises LinGemmError if the variant does not apply."""
     h.set_force(spec)
-    C = torch.empty((p.M, p.N), dtype=torch.int16, device="cuda")
+    try:
+        C = torch.empty((p.M, p.N), dtype=torch.int16, device="cuda")
 
-    def call(i):
-        h.run(ops["A"], Bs[i % len(Bs)], C, quant=p.quant, act=p.act, sa=ops["sa"],
-              sb=ops["sb"], alpha=p.alpha, bias=ops["bias"], residual=ops["residual"])
+        def call(i):
+            h.run(ops["A"], Bs[i % len(Bs)], C, quant=p.quant, act=p.act, sa=ops["sa"],
+                  sb=ops["sb"], alpha=p.alpha, bias=ops["bias"], residual=ops["residual"])
 
-    call(0)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(len(Bs)):
-            call(i)
-    g.replay()
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(reps):
+        call(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(len(Bs)):
+                call(i)
+    finally:
+        h.set_force(None)
+    return g, C
+
+
+def time_interleaved(torch, graphs, rounds):
+    """Median seconds per replay of each graph.  Every round replays all the
+    graphs once, so the candidates see the same clock and power state."""
+    for g in graphs:
         g.replay()
-    e.record()
-    e.synchronize()
-    h.set_force(None)
-    return s.elapsed_time(e) / 1e3 / reps / len(Bs)
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in graphs] for _ in range(rounds)]
+    for r in range(rounds):
+        for g, (s, e) in zip(graphs, ev[r]):
+            s.record()
+            g.replay()
+            e.record()
+    torch.cuda.synchronize()
+    return [float(np.median([ev[r][i][0].elapsed_time(ev[r][i][1]) for r in range(rounds)])) / 1e3
+            for i in range(len(graphs))]
+
+
+def time_variant(torch, h, p, ops, Bs, spec, reps=10):
+    """Seconds per call of one variant (graph replay, rotating B)."""
+    g, _ = capture_variant(torch, h, p, ops, Bs, spec)
+    return time_interleaved(torch, [g], reps)[0] / len(Bs)
 
 
 def sweep(workloads, out_path, reps, log=print, max_m=None):
@@ -109,18 +129,33 @@ def sweep(workloads, out_path, reps, log=print, max_m=None):
             ncopy = max(2, min(32, -(-ROTATION_BYTES // p.B.nbytes)))
             Bs = [ops["B"]] + [ops["B"].clone() for _ in range(ncopy - 1)]
             cands = DECODE_CANDIDATES if M <= 32 else TILE_CANDIDATES
-            best = None
+            # Warm every candidate first (the handle's split-K workspace only
+            # grows, so it reaches its final size before any graph is
+            # captured), then time them in interleaved rounds.
+            ok = []
             for spec in cands:
                 if p.quant == "block_fp8" and "rows=" in spec and 128 % int(spec.split("rows=")[1]):
                     continue
+                h.set_force(spec)
                 try:
-                    t = time_variant(torch, h, p, ops, Bs, spec, reps if M <= 32 else 3)
+                    C = torch.empty((p.M, p.N), dtype=torch.int16, device="cuda")
+                    h.run(ops["A"], Bs[0], C, quant=p.quant, act=p.act, sa=ops["sa"],
+                          sb=ops["sb"], alpha=p.alpha, bias=ops["bias"], residual=ops["residual"])
+                    ok.append(spec)
                 except lg.LinGemmError as ex:
                     log(f"  skip {spec}: {ex}")
-                    continue
+                finally:
+                    h.set_force(None)
+            torch.cuda.synchronize()
+            caps = [capture_variant(torch, h, p, ops, Bs, spec) for spec in ok]
+            ts = time_interleaved(torch, [g for g, _ in caps], reps if M <= 32 else max(3, reps // 2))
+            best = None
+            for spec, t in zip(ok, ts):
+                t /= len(Bs)
                 log(f"{c['name']} M={M}: {t * 1e6:9.2f} us  {spec}")
                 if best is None or t < best[0]:
                     best = (t, spec)
+            del caps
             log(f"BEST {c['name']} M={M}: {best[0] * 1e6:.2f} us  {best[1]}")
             entries.append((p.quant, M, p.N, p.K, best[1], best[0]))
             del Bs, ops
@@ -133,10 +168,14 @@ def sweep(workloads, out_path, reps, log=print, max_m=None):
     for q, M, N, K, spec, t in entries:
         lines.append(f"{q:<12} {M:<5} {M:<5} {N:<6} {K:<6} {spec}   # {t * 1e6:.2f} us")
     lines += ["*            1     32    *      *      decode swap=1 split=1 reduce=twopass waves=8 unroll=2 rows=16",
+              "block_fp8    257   *     *      *      pp split=0 group=4",
               "block_fp8    33    *     *      *      tile bm=128 bn=128 wm=2 wn=2 group=4",
               "*            33    256   *      *      tile bm=64 bn=128 wm=1 wn=4 group=4",
-              "*            257   1024  *      *      tile bm=128 bn=128 wm=2 wn=2 group=4",
-              "*            1025  *     *      *      tile bm=256 bn=128 wm=2 wn=2 group=4"]
+              "*            257   1024  *      *      tile bm=128 bn=128 wm=2 wn=4 group=4",
+              "bf16         1025  *     *      *      pp group=4",
+              "fp16         1025  *     *      *      pp group=4",
+              "w8a8_int8    1025  *     *      *      pp group=4",
+              "*            1025  *     *      *      tile bm=256 bn=256 wm=2 wn=4 group=4"]
     if out_path:
         os.makedirs(os.path.dirname(out_path), exist_ok=True)
         with open(out_path, "w") as f:

@@ -98,7 +98,7 @@ def test_zero_m_returns_ok_without_work(cpu_handle):
 def test_force_and_describe(cpu_handle):
     h = cpu_handle
     assert h.describe("fp8_dynamic", 8, 6144, 4096).startswith("decode")
-    assert h.describe("bf16", 4096, 4096, 4096).startswith("tile")
+    assert h.describe("bf16", 4096, 4096, 4096).startswith("pp")
     h.set_force("decode swap=0 split=4 reduce=twopass waves=8 unroll=2")
     assert h.describe("w8a8_int8", 4, 24576, 4096) == \
         "decode swap=0 split=4 reduce=twopass waves=8 unroll=2 rows=16"
@@ -112,6 +112,30 @@ def test_force_and_describe(cpu_handle):
     h.set_force("decode swap=1 split=0 reduce=twopass waves=4 unroll=4 rows=16")
     assert "split=2" in h.describe("fp8_dynamic", 1, 6144, 4096)
     assert "split=1" in h.describe("w8a8_int8", 1, 24576, 4096)
+    h.set_force(None)
+
+
+def test_pp_force_and_split(cpu_handle):
+    h = cpu_handle
+    # block FP8 auto split: 256x128 tiles, slices doubled while the grid is
+    # under 256 workgroups and each slice keeps >= 8 of the 96 scale blocks
+    h.set_force("pp")
+    assert h.describe("block_fp8", 512, 4096, 12288) == "pp split=4 group=4"
+    assert h.describe("block_fp8", 2048, 4096, 12288) == "pp split=1 group=4"
+    assert h.describe("block_fp8", 40, 4096, 12288) == "pp split=8 group=4"
+    assert h.describe("bf16", 4096, 4096, 4096) == "pp split=1 group=4"
+    assert h.describe("w8a8_int8", 300, 512, 1024) == "pp split=1 group=4"
+    with pytest.raises(lg.LinGemmError):
+        h.describe("fp8_dynamic", 512, 4096, 4096)   # no ping-pong kernel for per-channel e4m3
+    # an explicit split is clamped to the number of scale blocks
+    h.set_force("pp split=16")
+    assert h.describe("block_fp8", 256, 512, 512) == "pp split=4 group=4"
+    with pytest.raises(lg.LinGemmError):
+        h.describe("bf16", 4096, 4096, 4096)         # split-K is for block FP8 only
+    with pytest.raises(lg.LinGemmError):
+        h.set_force("pp split=3")                    # not a power of two
+    with pytest.raises(lg.LinGemmError):
+        h.set_force("pp split=32")                   # beyond 16
     h.set_force(None)
 
 

@@ -1,8 +1,9 @@
 """GPU variant invariants: every decode variant (swap-AB on/off, split-K
-factors, the three cross-workgroup reductions, wave / unroll shapes) and
-every compiled tile shape gives the oracle's result; split-K matches the
-unsplit kernel (int8 bit-exact); the deterministic reductions are bitwise
-repeatable; swap-AB equals the direct orientation."""
+factors, the three cross-workgroup reductions, wave / unroll shapes), every
+compiled tile shape and the ping-pong family (with block-FP8 split-K) gives
+the oracle's result; split-K matches the unsplit kernel (int8 bit-exact); the
+deterministic reductions are bitwise repeatable; swap-AB equals the direct
+orientation."""
 import numpy as np
 import pytest
 import torch
@@ -158,5 +159,47 @@ def test_tile_and_decode_agree_on_small_m(handle):
         ref, _ = reference(p)
         assert_close(t, ref, "tile")
         assert_close(dd, ref, "decode")
+    finally:
+        handle.set_force(None)
+
+
+# Ping-pong family: ragged M / N, K tails inside a 64-byte stage (bf16, fp16,
+# int8) and block-FP8 split-K factors (an explicit split above the number of
+# scale blocks is clamped; 0 = chosen from the shape).
+PP_PROBLEMS = [
+    ("bf16", "gelu_tanh", 300, 520, 264, True, True, 0.5, [1]),
+    ("fp16", "silu", 130, 264, 200, True, False, 1.0, [1]),
+    ("w8a8_int8", "silu", 260, 136, 528, False, False, 1.0, [1]),
+    ("block_fp8", "none", 270, 512, 384, True, True, 1.0, [1, 2, 4]),
+    ("block_fp8", "gelu_tanh", 600, 1024, 2048, True, False, 1.0, [0, 1, 4, 16]),
+]
+
+
+@pytest.mark.parametrize("prob", PP_PROBLEMS, ids=[f"{p[0]}-M{p[2]}" for p in PP_PROBLEMS])
+def test_pp_variants_match_oracle(handle, prob):
+    q, a, M, N, K, b, r, al, splits = prob
+    p = synth.make_custom(q, a, M, N, K, seed=M * 5 + N, bias=b, residual=r, alpha=al)
+    ref, _ = reference(p)
+    acc = oracle.linear(q, "none", p.A, p.B, p.sa, p.sb)[1] if q == "w8a8_int8" else None
+    d = upload(p)
+    try:
+        for sp in splits:
+            spec = f"pp split={sp} group=4"
+            handle.set_force(spec)
+            print(f"[variant] {p.name} {spec} -> {handle.describe(q, M, N, K)}", flush=True)
+            assert_close(decode_out(run(handle, p, d), q), ref, f"{p.name} [{spec}]")
+            if acc is not None:
+                assert np.array_equal(run(handle, p, d, raw=True).cpu().numpy(), acc), spec
+    finally:
+        handle.set_force(None)
+
+
+def test_pp_rejects_per_channel_fp8(handle):
+    p = synth.make_custom("fp8_dynamic", "none", 64, 256, 512, seed=3, bias=False, residual=False)
+    d = upload(p)
+    try:
+        handle.set_force("pp")
+        with pytest.raises(lg.LinGemmError):
+            run(handle, p, d)
     finally:
         handle.set_force(None)
