@@ -133,10 +133,10 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u;
       const bool live = t < my;
-      // Steps past this wave's range re-read its first step (valid: my > 0)
-      // and are zeroed; chunks past the end of the row re-read the row's
-      // last 16 bytes and are zeroed.
-      const int st = first + (live ? t : 0);
+      // Steps past this wave's range re-read a step inside the row (its
+      // first, clamped to the last step of K) and are zeroed; chunks past the
+      // end of the row re-read the row's last 16 bytes and are zeroed.
+      const int st = min(first + (live ? t : 0), total_steps - 1);
       const int64_t off = (int64_t)st * STEPB;
       const int64_t o0 = off + g * 32, o1 = o0 + 16;
       const bool ok0 = live && (o0 < KB);
@@ -159,30 +159,13 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
     }
   };
 
-  // Epilogue operands of the tiles this wave will finish (q = wave, wave +
-  // W, ...), fetched now so their latency hides behind the K loop.
-  constexpr int QPW = (NTILE + W - 1) / W;  // tiles per wave, at most
-  EpiPre4 pre[QPW];
-  // (The two-pass reduction with split > 1 runs its epilogue in
-  // splitk_reduce instead.)
-  const bool fin_here = split == 1 || reduce != R_TWOPASS;
-  if (SWAP && fin_here) {
-#pragma unroll
-    for (int i = 0; i < QPW; ++i) {
-      const int q = wave + i * W;
-      const int64_t nr = n0 + (q / NTT) * 16 + g * 4;
-      if (q < NTILE && nr < nend) epilogue_prefetch4<F16>(e, (q % NTT) * 16 + l16, nr, pre[i]);
-    }
-  }
-
   C acc[RT][NTT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) acc[rt][tt] = C{0, 0, 0, 0};
 
-  for (int t0 = 0; t0 < my; t0 += U) {
-    load_batch(t0);
+  auto compute_batch = [&]() {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       typename MF::Frag x0[NTT], x1[NTT];
@@ -210,6 +193,34 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
         }
       }
     }
+  };
+
+  // The first batch is issued before anything else, so the weight stream
+  // starts at once (a wave with no steps loads zeroed re-reads, which add
+  // nothing).
+  load_batch(0);
+
+  // Epilogue operands of the tiles this wave will finish (q = wave, wave +
+  // W, ...), fetched behind the first batch so their latency hides behind
+  // the K loop.
+  constexpr int QPW = (NTILE + W - 1) / W;  // tiles per wave, at most
+  EpiPre4 pre[QPW];
+  // (The two-pass reduction with split > 1 runs its epilogue in
+  // splitk_reduce instead.)
+  const bool fin_here = split == 1 || reduce != R_TWOPASS;
+  if (SWAP && fin_here) {
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      const int q = wave + i * W;
+      const int64_t nr = n0 + (q / NTT) * 16 + g * 4;
+      if (q < NTILE && nr < nend) epilogue_prefetch4<F16>(e, (q % NTT) * 16 + l16, nr, pre[i]);
+    }
+  }
+
+  compute_batch();
+  for (int t0 = U; t0 < my; t0 += U) {
+    load_batch(t0);
+    compute_batch();
   }
 
   // In-workgroup reduction, in wave order; wave w then owns tiles
