@@ -172,6 +172,11 @@ PP_PROBLEMS = [
     ("w8a8_int8", "silu", 260, 136, 528, False, False, 1.0, [1]),
     ("block_fp8", "none", 270, 512, 384, True, True, 1.0, [1, 2, 4]),
     ("block_fp8", "gelu_tanh", 600, 1024, 2048, True, False, 1.0, [0, 1, 4, 16]),
+    # degenerate sizes: one partial stage, tiles almost empty, one scale block
+    ("bf16", "none", 5, 12, 8, True, True, 1.0, [1]),
+    ("fp16", "gelu_tanh", 3, 20, 40, False, True, 2.0, [1]),
+    ("w8a8_int8", "relu", 17, 40, 16, True, False, 1.0, [1]),
+    ("block_fp8", "silu", 3, 128, 128, True, True, 1.0, [1, 2]),
 ]
 
 
