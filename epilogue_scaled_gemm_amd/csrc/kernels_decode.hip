@@ -76,7 +76,7 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
   __shared__ int arrival;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   // This workgroup's weight rows are [n0, n0 + rpw) (rpw <= 16 * RT, a
   // multiple of 4); rows of its MFMA tiles past that are masked.
@@ -383,7 +383,7 @@ hipError_t launch_d(const Variant& v, const Call& c, int split, hipStream_t s) {
   X(QK, NTT, true, 8, 1, 1) X(QK, NTT, true, 8, 2, 1) X(QK, NTT, true, 4, 4, 1) \
   X(QK, NTT, true, 16, 1, 1) X(QK, NTT, true, 8, 1, 2) X(QK, NTT, true, 4, 2, 2) \
   X(QK, NTT, true, 8, 2, 2) X(QK, NTT, true, 4, 1, 4) X(QK, NTT, true, 8, 1, 4) \
-  X(QK, NTT, false, 8, 2, 1)
+  X(QK, NTT, true, 8, 4, 1) X(QK, NTT, true, 8, 4, 2) X(QK, NTT, false, 8, 2, 1)
 
 // Tiles per workgroup for a rows-per-workgroup value: 1, 2 or 4.
 inline int tiles_for(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
