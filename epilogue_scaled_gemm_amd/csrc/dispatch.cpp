@@ -157,14 +157,11 @@ const char* builtin_table() {
   return R"TABLE(
 # quant        m_lo m_hi N     K      variant
 # measured entries (offline sweep on MI355X, graph replay, rotating weights)
-fp8_dynamic    1    4    6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=1 rows=12
-fp8_dynamic    5    16   6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=1 rows=24
-fp8_dynamic    17   32   6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=4 rows=24
+fp8_dynamic    1    2    6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=1 rows=12
+fp8_dynamic    3    32   6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=4 rows=24
 w8a8_int8      1    4    24576 4096   decode swap=1 split=1 reduce=twopass waves=4 unroll=4 rows=16
-w8a8_int8      5    16   24576 4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=4 rows=24
-w8a8_int8      17   32   24576 4096   decode swap=1 split=1 reduce=twopass waves=4 unroll=2 rows=32
-block_fp8      1    4    4096  12288  decode swap=1 split=1 reduce=twopass waves=16 unroll=1 rows=16
-block_fp8      5    16   4096  12288  decode swap=1 split=1 reduce=twopass waves=8 unroll=2 rows=16
+w8a8_int8      5    32   24576 4096   decode swap=1 split=1 reduce=twopass waves=4 unroll=2 rows=32
+block_fp8      1    16   4096  12288  decode swap=1 split=1 reduce=twopass waves=12 unroll=1 rows=16
 block_fp8      17   32   4096  12288  decode swap=1 split=2 reduce=twopass waves=8 unroll=2 rows=32
 block_fp8      257  *    4096  12288  pp split=0 group=4
 block_fp8      33   256  4096  12288  tile bm=64 bn=64 wm=2 wn=2 group=4

@@ -22,6 +22,9 @@
 //  * swap = 1 puts the weight on the MFMA row side (tokens are columns): each
 //    lane ends with 4 consecutive output columns of one token (8-byte
 //    stores).  swap = 0 puts tokens on the row side (the direct A*B^T form).
+//  * With swap and W = 8 or 12, one more wave loads the epilogue operands (scales, bias,
+//    residual) into LDS while the others stream the weight, so no wave that
+//    loads weights waits on them, and the epilogue reads them from LDS.
 //  * Tokens past M re-read token M-1 and their outputs are dropped; tokens
 //    use one or two 16-column MFMA tiles (M <= 16 or M <= 32).
 //  * Partial sums of the W waves are reduced in LDS in a fixed order.  With
@@ -60,8 +63,14 @@ __device__ inline i32x8 cat(i32x4 a, i32x4 b) {
   return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Whether a variant has the operand wave: with swap and 8 or 12 K waves.  A
+// workgroup holds at most 16 waves; with 4 K waves the extra wave's share of
+// the CU's wave slots cost more than it saved, and those variants prefetch
+// the operands in the owning waves instead.
+constexpr bool op_wave(bool swap, int w) { return swap && w >= 8 && w < 16; }
+
 template <int QK, int NTT, bool SWAP, int W, int U, int RT>
-__global__ __launch_bounds__(W * 64) void decode_kernel(
+__global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int64_t M, int64_t N,
     int64_t KB, int rpw, int split, int steps_per_split, int reduce, Epi e,
     void* __restrict__ ws, int* __restrict__ counters) {
@@ -73,10 +82,19 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
   constexpr int NS = SWAP ? 1 : 4;    // block scales per token tile per lane
   constexpr int NTILE = RT * NTT;     // 16x16 output tiles per workgroup
   __shared__ AccT red[W][NTILE * 4][64];
+  // Epilogue operands per tile and lane: sa, sb[4], bias[4], residual[4],
+  // staged by the operand wave.
+  constexpr bool OPW = op_wave(SWAP, W);
+  constexpr int NOP = 13;
+  __shared__ float opnd[OPW ? NTILE : 1][NOP][64];
   __shared__ int arrival;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Wave W (one past the K waves), if present, is the operand wave: it loads
+  // no weights, only the epilogue operands of the workgroup's tiles, which
+  // it stages in LDS while the K waves stream the weight.
+  const bool opw = OPW && wave == W;
   const int g = lane >> 4, l16 = lane & 15;
   // This workgroup's weight rows are [n0, n0 + rpw) (rpw <= 16 * RT, a
   // multiple of 4); rows of its MFMA tiles past that are masked.
@@ -198,39 +216,61 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
   // The first batch is issued before anything else, so the weight stream
   // starts at once (a wave with no steps loads zeroed re-reads, which add
   // nothing).
-  load_batch(0);
-
-  // Epilogue operands of the tiles this wave will finish (q = wave, wave +
-  // W, ...), fetched behind the first batch so their latency hides behind
-  // the K loop.
-  constexpr int QPW = (NTILE + W - 1) / W;  // tiles per wave, at most
-  EpiPre4 pre[QPW];
-  // (The two-pass reduction with split > 1 runs its epilogue in
-  // splitk_reduce instead.)
+  // Without the operand wave, each swap wave prefetches the operands of the
+  // tiles it will finish (q = wave, wave + W, ...) right behind its first
+  // batch.
   const bool fin_here = split == 1 || reduce != R_TWOPASS;
-  if (SWAP && fin_here) {
+  constexpr int QPW = (NTILE + W - 1) / W;  // tiles per wave, at most
+  EpiPre4 pre[SWAP && !OPW ? QPW : 1];
+  if (!opw) {
+    load_batch(0);
+    if constexpr (SWAP && !OPW) {
+      if (fin_here) {
 #pragma unroll
-    for (int i = 0; i < QPW; ++i) {
-      const int q = wave + i * W;
-      const int64_t nr = n0 + (q / NTT) * 16 + g * 4;
-      if (q < NTILE && nr < nend) epilogue_prefetch4<F16>(e, (q % NTT) * 16 + l16, nr, pre[i]);
+        for (int i = 0; i < QPW; ++i) {
+          const int q = wave + i * W;
+          const int64_t nr = n0 + (q / NTT) * 16 + g * 4;
+          if (q < NTILE && nr < nend) epilogue_prefetch4<F16>(e, (q % NTT) * 16 + l16, nr, pre[i]);
+        }
+      }
     }
-  }
-
-  compute_batch();
-  for (int t0 = U; t0 < my; t0 += U) {
-    load_batch(t0);
     compute_batch();
+    for (int t0 = U; t0 < my; t0 += U) {
+      load_batch(t0);
+      compute_batch();
+    }
+  } else if (fin_here) {
+    // The operand wave: the loads' latency overlaps the weight stream of the
+    // K waves, and the waves that own the tiles read the operands from LDS
+    // at the end.  (The two-pass reduction with split > 1 runs its epilogue
+    // in splitk_reduce instead.)
+#pragma unroll
+    for (int q = 0; q < NTILE; ++q) {
+      const int64_t nr = n0 + (q / NTT) * 16 + g * 4;
+      if (nr < nend) {
+        EpiPre4 p;
+        epilogue_prefetch4<F16>(e, (q % NTT) * 16 + l16, nr, p);
+        opnd[q][0][lane] = p.sam;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          opnd[q][1 + i][lane] = p.sb[i];
+          opnd[q][5 + i][lane] = p.bias[i];
+          opnd[q][9 + i][lane] = p.res[i];
+        }
+      }
+    }
   }
 
   // In-workgroup reduction, in wave order; wave w then owns tiles
   // q = w, w + W, ... (q = rt * NTT + tt) for the rest of the kernel.
+  if (!opw) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
+      for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave][(rt * NTT + tt) * 4 + r][lane] = (AccT)acc[rt][tt][r];
+        for (int r = 0; r < 4; ++r) red[wave][(rt * NTT + tt) * 4 + r][lane] = (AccT)acc[rt][tt][r];
+  }
   __syncthreads();
 
   // Output coordinates of value r of tile q.
@@ -253,6 +293,25 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
       }
     }
   };
+  // Swap-orientation epilogue of tile q (the i-th tile of this wave) from the
+  // operands staged in LDS, or prefetched by this wave.
+  auto finish_swap = [&](int q, int i, const AccT* v) {
+    const int64_t nr = n0 + (q / NTT) * 16 + g * 4;
+    if (nr >= nend) return;
+    if constexpr (!OPW) {
+      epilogue_run4_pre<F16>(e, (q % NTT) * 16 + l16, nr, v, pre[SWAP && !OPW ? i : 0]);
+      return;
+    }
+    EpiPre4 p;
+    p.sam = opnd[q][0][lane];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p.sb[j] = opnd[q][1 + j][lane];
+      p.bias[j] = opnd[q][5 + j][lane];
+      p.res[j] = opnd[q][9 + j][lane];
+    }
+    epilogue_run4_pre<F16>(e, (q % NTT) * 16 + l16, nr, v, p);
+  };
   auto reduce_tile = [&](int q, AccT* v) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -264,21 +323,21 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
   };
 
   if (split == 1) {
+    if (opw) return;
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
       const int q = wave + i * W;
       if (q >= NTILE) break;
       AccT v[4];
       reduce_tile(q, v);
-      const int64_t nr = n0 + (q / NTT) * 16 + g * 4;
-      if (!SWAP) finish(q, v);
-      else if (nr < nend) epilogue_run4_pre<F16>(e, (q % NTT) * 16 + l16, nr, v, pre[i]);
+      if (SWAP) finish_swap(q, i, v);
+      else finish(q, v);
     }
     return;
   }
 
   AccT* wsa = (AccT*)ws;
-  for (int q = wave; q < NTILE; q += W) {
+  for (int q = opw ? NTILE : wave; q < NTILE; q += W) {
     AccT v[4];
     reduce_tile(q, v);
 #pragma unroll
@@ -312,8 +371,11 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
     arrival = __hip_atomic_fetch_add(counters + blockIdx.x, 1, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (arrival != split - 1) return;
-  for (int q = wave; q < NTILE; q += W) {
+  if (arrival != split - 1 || opw) return;
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    const int q = wave + i * W;
+    if (q >= NTILE) break;
     AccT v[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -330,10 +392,8 @@ __global__ __launch_bounds__(W * 64) void decode_kernel(
       }
       v[r] = s;
     }
-    const int i = (q - wave) / W;
-    const int64_t nr = n0 + (q / NTT) * 16 + g * 4;
-    if (!SWAP) finish(q, v);
-    else if (nr < nend) epilogue_run4_pre<F16>(e, (q % NTT) * 16 + l16, nr, v, pre[i]);
+    if (SWAP) finish_swap(q, i, v);
+    else finish(q, v);
   }
   if (threadIdx.x == 0) st_agent(counters + blockIdx.x, 0);
 }
@@ -365,7 +425,8 @@ hipError_t launch_d(const Variant& v, const Call& c, int split, hipStream_t s) {
   const int groups = (int)((c.N + v.rows - 1) / v.rows);
   const int total_steps = (int)((c.KB + STEPB - 1) / STEPB);
   const int sps = (total_steps + split - 1) / split;
-  hipLaunchKernelGGL((decode_kernel<QK, NTT, SWAP, W, U, RT>), dim3(groups, split), dim3(W * 64),
+  hipLaunchKernelGGL((decode_kernel<QK, NTT, SWAP, W, U, RT>), dim3(groups, split),
+                     dim3((W + (op_wave(SWAP, W) ? 1 : 0)) * 64),
                      0, s, (const uint8_t*)c.A, (const uint8_t*)c.B, c.M, c.N, c.KB, v.rows, split,
                      sps, v.reduce, c.epi, c.ws, c.counters);
   hipError_t err = hipGetLastError();
@@ -383,7 +444,8 @@ hipError_t launch_d(const Variant& v, const Call& c, int split, hipStream_t s) {
   X(QK, NTT, true, 8, 1, 1) X(QK, NTT, true, 8, 2, 1) X(QK, NTT, true, 4, 4, 1) \
   X(QK, NTT, true, 16, 1, 1) X(QK, NTT, true, 8, 1, 2) X(QK, NTT, true, 4, 2, 2) \
   X(QK, NTT, true, 8, 2, 2) X(QK, NTT, true, 4, 1, 4) X(QK, NTT, true, 8, 1, 4) \
-  X(QK, NTT, true, 8, 4, 1) X(QK, NTT, true, 8, 4, 2) X(QK, NTT, false, 8, 2, 1)
+  X(QK, NTT, true, 8, 4, 1) X(QK, NTT, true, 8, 4, 2) X(QK, NTT, true, 12, 1, 1) \
+  X(QK, NTT, false, 8, 2, 1)
 
 // Tiles per workgroup for a rows-per-workgroup value: 1, 2 or 4.
 inline int tiles_for(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }

@@ -27,7 +27,7 @@ ROTATION_BYTES = 384 << 20
 # (waves, unroll, rows per workgroup)
 DECODE_SHAPES = [(8, 1, 16), (8, 2, 16), (4, 4, 16), (16, 1, 16), (8, 1, 8), (8, 1, 12),
                  (16, 1, 12), (16, 1, 8), (8, 2, 8), (8, 1, 32), (4, 2, 32), (8, 2, 32),
-                 (8, 1, 24), (4, 1, 64), (8, 1, 64), (8, 4, 12), (8, 4, 24)]
+                 (8, 1, 24), (4, 1, 64), (8, 1, 64), (8, 4, 12), (8, 4, 24), (12, 1, 12), (12, 1, 16)]
 DECODE_CANDIDATES = [
     f"decode swap=1 split={sp} reduce=twopass waves={w} unroll={u} rows={r}"
     for sp in (1, 2) for w, u, r in DECODE_SHAPES
