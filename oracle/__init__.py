@@ -15,7 +15,11 @@ CPU cast, bf16/fp16 decode and bf16 rounding against torch/numpy casts, exact
 Fraction brute force on tiny shapes for every quant mode, the GELU-tanh and
 SiLU closed forms and their odd-part identity, identity and permutation
 weights, the block-scale closed form, the transpose (swap-AB) identity, and
-the 32 MiB size of a 4096x4096 16-bit intermediate.  Unpinned: nothing in the
+the 32 MiB size of a 4096x4096 16-bit intermediate; for the dynamic
+quantization, every e4m3 code and every midpoint between neighbours against
+torch's CPU cast, int8 ties-to-even on exact halves, the group maximum mapping
+to the format's maximum, the half-step error bound, and the block kind equal to
+the per-token kind over 128-wide rows.  Unpinned: nothing in the
 oracle itself; the GPU's fp32 accumulation order is covered only by the
 stated tolerance.
 """
@@ -65,6 +69,10 @@ def _load():
     lib.oracle_unfused_stage3.restype = ctypes.c_int
     lib.oracle_unfused_stage3.argtypes = [P, P, ctypes.c_double, I64, I64, ctypes.c_int, P]
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_f32_to_e4m3_rne.restype = ctypes.c_uint8
+    lib.oracle_f32_to_e4m3_rne.argtypes = [ctypes.c_float]
+    lib.oracle_dynamic_quant.restype = ctypes.c_int
+    lib.oracle_dynamic_quant.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_int, P, P]
     _lib = lib
     return lib
 
@@ -174,6 +182,32 @@ def unfused_stage3(u, residual, alpha, quant="bf16"):
     _load().oracle_unfused_stage3(_ptr(u), _ptr(_c(residual, np.uint16)), float(alpha), M, N,
                                   QUANT[quant], _ptr(o))
     return o
+
+
+DQ_KIND = {"fp8_token": 0, "int8_token": 1, "fp8_block": 2}
+
+
+def f32_to_e4m3(v: float) -> int:
+    """E4M3FN code nearest to the binary32 value v (ties to even, saturating)."""
+    return _load().oracle_f32_to_e4m3_rne(v)
+
+
+def dynamic_quant(kind, X, x_dtype="bf16"):
+    """Dynamic activation quantization of X[M,K] (16-bit float codes).
+
+    kind: "fp8_token" (e4m3 codes, scales [M]), "int8_token" (int8, [M]) or
+    "fp8_block" (e4m3, scales [M, K/128]).  Returns (Q codes [M,K], scales).
+    """
+    X = _c(X, np.uint16)
+    M, K = X.shape
+    q_t = np.int8 if kind == "int8_token" else np.uint8
+    Q = np.empty((M, K), dtype=q_t)
+    sc = np.empty((M, K // 128) if kind == "fp8_block" else (M,), dtype=np.float32)
+    rc = _load().oracle_dynamic_quant(_ptr(X), M, K, 1 if x_dtype == "fp16" else 0,
+                                      DQ_KIND[kind], _ptr(Q), _ptr(sc))
+    if rc:
+        raise ValueError(f"oracle_dynamic_quant: {_ERR.get(rc, rc)}")
+    return Q, sc
 
 
 def within_tolerance(g, r, rel=1e-2, floor=1e-3):

@@ -319,6 +319,92 @@ int oracle_unfused_stage3(const uint16_t *u, const uint16_t *residual, double al
     return O_OK;
 }
 
+/* ------------------------------------------------- dynamic quantization */
+/*
+ * Dynamic activation quantization: the step right before the layer, which
+ * produces its A operand and activation scales at run time.  The pages name
+ * it but do not spell it out: "helion-vllm-linear-backend" (section "Одно
+ * ядро вместо трёх вариантов") gives FP8_Dynamic a per-token activation
+ * scale, W8A8_INT8 the same scaling in int8, and Block_FP8 1x128 activation
+ * blocks; the section on prologue/epilogue strategies of "Совместная работа
+ * Helion и TorchInductor" lists quantization among the input-side (prologue)
+ * transforms.  Readings taken here, for every group g of values (a row for
+ * the per-token kinds, a 1x128 block of a row for the block kind):
+ *
+ *   amax_g  = max |x| over the group                 (exact)
+ *   s_g     = amax_g / QMAX   in binary32, QMAX = 448 (e4m3) or 127 (int8)
+ *             (s_g = 1 when amax_g == 0, so an all-zero group maps to 0)
+ *   v       = x / s_g          in binary32
+ *   e4m3:     q = the E4M3FN code nearest to v, ties to the even code,
+ *             |v| >= 448 saturating to +-448; the sign is kept (a negative
+ *             v that rounds to zero gives -0, code 0x80)
+ *   int8:     q = v rounded to the nearest integer, ties to even, clamped
+ *             to [-127, 127]
+ *
+ * The scale and v are computed in binary32 because that is the precision in
+ * which the kernel takes the same decisions; the rounding of v to a code is
+ * done here by searching the exact decoded values, not by bit tricks.
+ * Inputs must be finite.
+ */
+enum { ODQ_FP8_TOKEN = 0, ODQ_INT8_TOKEN = 1, ODQ_FP8_BLOCK = 2 };
+
+/* E4M3FN code nearest to v (RNE, saturating, sign kept). */
+uint8_t oracle_f32_to_e4m3_rne(float v) {
+    static double val[127]; /* values of the positive finite codes 0x00..0x7E */
+    static int init = 0;
+    if (!init) {
+        for (int c = 0; c < 127; ++c) val[c] = oracle_e4m3_to_f64((uint8_t)c);
+        init = 1;
+    }
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    const double a = fabs((double)v);
+    int c;
+    if (a >= val[126]) {
+        c = 126;
+    } else {
+        int lo = 0; /* largest code with val <= a */
+        while (lo + 1 < 127 && val[lo + 1] <= a) ++lo;
+        const double dlo = a - val[lo], dhi = val[lo + 1] - a; /* both exact */
+        if (dlo < dhi) c = lo;
+        else if (dhi < dlo) c = lo + 1;
+        else c = (lo & 1) ? lo + 1 : lo; /* tie: the even mantissa */
+    }
+    return (uint8_t)(sign | c);
+}
+
+int oracle_dynamic_quant(const uint16_t *X, int64_t M, int64_t K, int x_fp16, int kind,
+                         void *Q, float *scales) {
+    if (!X || !Q || !scales || M < 0 || K < 1 || kind < 0 || kind > 2) return O_BAD_ARG;
+    if (kind == ODQ_FP8_BLOCK && K % 128) return O_BAD_ARG;
+    tables_init();
+    const int64_t glen = kind == ODQ_FP8_BLOCK ? 128 : K; /* group length */
+    const int64_t ngroups = M * (K / glen);
+    const float qmax = kind == ODQ_INT8_TOKEN ? 127.0f : 448.0f;
+    for (int64_t gi = 0; gi < ngroups; ++gi) {
+        const int64_t base = gi * glen; /* groups tile each row in order */
+        float amax = 0.0f;
+        for (int64_t k = 0; k < glen; ++k) {
+            const float x = (float)dec16(x_fp16 ? OQ_FP16 : OQ_BF16, X[base + k]);
+            if (fabsf(x) > amax) amax = fabsf(x);
+        }
+        const float s = amax > 0.0f ? amax / qmax : 1.0f;
+        scales[gi] = s;
+        for (int64_t k = 0; k < glen; ++k) {
+            const float x = (float)dec16(x_fp16 ? OQ_FP16 : OQ_BF16, X[base + k]);
+            const float v = x / s;
+            if (kind == ODQ_INT8_TOKEN) {
+                float r = rintf(v);
+                if (r > 127.0f) r = 127.0f;
+                if (r < -127.0f) r = -127.0f;
+                ((int8_t *)Q)[base + k] = (int8_t)r;
+            } else {
+                ((uint8_t *)Q)[base + k] = oracle_f32_to_e4m3_rne(v);
+            }
+        }
+    }
+    return O_OK;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();
