@@ -30,7 +30,9 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "HIP error",
 # The symbols include/lin_gemm.h declares.
 EXPORTS = ("lin_gemm_create", "lin_gemm_run", "lin_gemm_destroy", "lin_gemm_strerror",
            "lin_gemm_last_error", "lin_gemm_set_force", "lin_gemm_describe",
-           "lin_gemm_run_unfused")
+           "lin_gemm_run_unfused", "lin_gemm_quantize", "lin_gemm_run_dynamic")
+DQ_KIND = {"fp8_token": 0, "int8_token": 1, "fp8_block": 2}
+X_DTYPE = {"bf16": 0, "fp16": 1}
 
 
 class LinGemmError(RuntimeError):
@@ -73,6 +75,11 @@ def library():
     lib.lin_gemm_run_unfused.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, ctypes.c_float,
                                          I, I, P]
     lib.lin_gemm_run_unfused.restype = I
+    lib.lin_gemm_quantize.argtypes = [P, P, I, I64, I64, I, P, P, P]
+    lib.lin_gemm_quantize.restype = I
+    lib.lin_gemm_run_dynamic.argtypes = [P, P, I, P, P, ctypes.c_float, P, P, P, I64, I64, I64,
+                                         I, I, P]
+    lib.lin_gemm_run_dynamic.restype = I
     _lib = lib
     return lib
 
@@ -143,6 +150,29 @@ class Handle:
                                             _ptr(C), _ptr(T), _ptr(U), M, N, K, float(alpha),
                                             _code(QUANT, quant), _code(ACT, act), _stream(stream))
         self._check(rc, "lin_gemm_run_unfused")
+        return C
+
+    def quantize(self, X, Q, scales, kind="fp8_token", x_dtype="bf16", stream=None):
+        """Dynamic activation quantization of X[M,K] into Q[M,K] and scales."""
+        M, K = X.shape
+        rc = self._lib.lin_gemm_quantize(self._h, _ptr(X), _code(X_DTYPE, x_dtype), M, K,
+                                         _code(DQ_KIND, kind), _ptr(Q), _ptr(scales),
+                                         _stream(stream))
+        self._check(rc, "lin_gemm_quantize")
+        return Q, scales
+
+    def run_dynamic(self, X, B, C, quant="fp8_dynamic", act="none", sb=None, alpha=1.0,
+                    bias=None, residual=None, x_dtype="bf16", stream=None):
+        """Quantize X[M,K] (16-bit) on the fly, then the layer of run()."""
+        M, K = X.shape
+        N = B.shape[0]
+        if B.shape[1] != K:
+            raise ValueError(f"inner dimensions differ: X has K={K}, B has {B.shape[1]}")
+        rc = self._lib.lin_gemm_run_dynamic(self._h, _ptr(X), _code(X_DTYPE, x_dtype), _ptr(B),
+                                            _ptr(sb), float(alpha), _ptr(bias), _ptr(residual),
+                                            _ptr(C), M, N, K, _code(QUANT, quant),
+                                            _code(ACT, act), _stream(stream))
+        self._check(rc, "lin_gemm_run_dynamic")
         return C
 
     def set_force(self, spec):

@@ -17,8 +17,8 @@ LIB = os.path.join(HERE, "liblingemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["kernels_tile.hip", "kernels_pp.hip", "kernels_decode.hip", "kernels_misc.hip", "dispatch.cpp",
-           "abi.cpp"]
+SOURCES = ["kernels_tile.hip", "kernels_pp.hip", "kernels_decode.hip", "kernels_misc.hip",
+           "kernels_quant.hip", "dispatch.cpp", "abi.cpp"]
 
 # Packed fp32 instructions are disabled for all device code.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",

@@ -31,6 +31,8 @@ struct lin_gemm_ctx {
   bool ws_zero = true;        // workspace all zero (needed by the atomic reduction)
   int* counters = nullptr;    // per-16-row-group arrival counters (kept at zero between calls)
   size_t counters_n = 0;
+  void* dq = nullptr;         // staging of lin_gemm_run_dynamic: codes, then scales
+  size_t dq_bytes = 0;
 };
 
 namespace {
@@ -233,6 +235,7 @@ int lin_gemm_destroy(lin_gemm_t h) {
   if (!h) return LIN_OK;
   if (h->ws) hipFree(h->ws);
   if (h->counters) hipFree(h->counters);
+  if (h->dq) hipFree(h->dq);
   delete h;
   return LIN_OK;
 }
@@ -371,6 +374,73 @@ int lin_gemm_run_unfused(lin_gemm_t h, const void* A, const void* B, const void*
   e = lg::launch_scale_residual(U, residual, C, M, N, alpha, f16, s);
   if (e != hipSuccess) return hip_fail(h, e, "scale+residual launch");
   return LIN_OK;
+}
+
+int lin_gemm_quantize(lin_gemm_t h, const void* X, int x_dtype, int64_t M, int64_t K, int kind,
+                      void* Q, float* scales, void* stream) {
+  if (!h) return LIN_ERR_INVALID_ARG;
+  h->last_error.clear();
+  if (M < 0 || K < 0) return fail(h, LIN_ERR_INVALID_ARG, "negative size");
+  if (x_dtype != LIN_Q_BF16 && x_dtype != LIN_Q_FP16)
+    return fail(h, LIN_ERR_INVALID_ARG, "x_dtype must be LIN_Q_BF16 or LIN_Q_FP16");
+  if (kind < LIN_DQ_FP8_TOKEN || kind > LIN_DQ_FP8_BLOCK)
+    return fail(h, LIN_ERR_INVALID_ARG, "unknown quantization kind " + std::to_string(kind));
+  if (M == 0) return LIN_OK;
+  if (!X || !Q || !scales) return fail(h, LIN_ERR_INVALID_ARG, "X, Q and scales must be non-null");
+  if (K < 16 || K % 16 != 0)
+    return fail(h, LIN_ERR_UNSUPPORTED, "K must be a positive multiple of 16");
+  if (kind == LIN_DQ_FP8_BLOCK && K % 128 != 0)
+    return fail(h, LIN_ERR_UNSUPPORTED, "1x128 blocks need K % 128 == 0");
+  if (M >= ((int64_t)1 << 31) || K > ((int64_t)1 << 31) || M * K >= ((int64_t)1 << 40))
+    return fail(h, LIN_ERR_UNSUPPORTED, "sizes beyond 2^31 rows / 2^40 values");
+  if (misaligned(X) || misaligned(Q) || misaligned(scales))
+    return fail(h, LIN_ERR_UNSUPPORTED, "X, Q and scales must be 16-byte aligned");
+  hipError_t e = lg::launch_dynamic_quant(kind, x_dtype == LIN_Q_FP16, X, M, K, Q, scales,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(h, e, "quantization launch");
+  return LIN_OK;
+}
+
+int lin_gemm_run_dynamic(lin_gemm_t h, const void* X, int x_dtype, const void* B,
+                         const float* sb, float alpha, const void* bias, const void* residual,
+                         void* C, int64_t M, int64_t N, int64_t K, int quant_mode, int activation,
+                         void* stream) {
+  if (!h) return LIN_ERR_INVALID_ARG;
+  h->last_error.clear();
+  int kind;
+  switch (quant_mode) {
+    case LIN_Q_FP8_DYNAMIC: kind = LIN_DQ_FP8_TOKEN; break;
+    case LIN_Q_W8A8_INT8: kind = LIN_DQ_INT8_TOKEN; break;
+    case LIN_Q_BLOCK_FP8: kind = LIN_DQ_FP8_BLOCK; break;
+    default:
+      return fail(h, LIN_ERR_INVALID_ARG, "run_dynamic needs a quantised mode (2, 3 or 4)");
+  }
+  int rc = check_shape(h, quant_mode, M, N, K);
+  if (rc != LIN_OK || M == 0) return rc;
+  if (!X || !B || !C || !sb) return fail(h, LIN_ERR_INVALID_ARG, "X, B, sb and C must be non-null");
+  // Staging: the codes [M][K], then the scales (256-byte aligned).
+  const size_t qbytes = ((size_t)M * (size_t)K + 255) & ~(size_t)255;
+  const size_t nscale = kind == LIN_DQ_FP8_BLOCK ? (size_t)M * (size_t)(K / 128) : (size_t)M;
+  const size_t need = qbytes + nscale * sizeof(float);
+  hipStream_t s = (hipStream_t)stream;
+  if (need > h->dq_bytes) {
+    hipError_t e = hipStreamSynchronize(s);  // in-flight calls may still read the old staging
+    if (e != hipSuccess) return hip_fail(h, e, "hipStreamSynchronize");
+    if (h->dq) hipFree(h->dq);
+    h->dq = nullptr;
+    h->dq_bytes = 0;
+    const size_t bytes = (need + 255) & ~(size_t)255;
+    if (hipMalloc(&h->dq, bytes) != hipSuccess) {
+      h->dq = nullptr;
+      return fail(h, LIN_ERR_OOM, "staging allocation of " + std::to_string(bytes) + " bytes failed");
+    }
+    h->dq_bytes = bytes;
+  }
+  float* sa = (float*)((char*)h->dq + qbytes);
+  rc = lin_gemm_quantize(h, X, x_dtype, M, K, kind, h->dq, sa, stream);
+  if (rc != LIN_OK) return rc;
+  lin_scales_t sc{sa, sb, alpha};
+  return lin_gemm_run(h, h->dq, B, &sc, bias, residual, C, M, N, K, quant_mode, activation, stream);
 }
 
 }  // extern "C"

@@ -65,5 +65,11 @@ hipError_t launch_bias_act(const void* T, const void* bias, void* U, int64_t M, 
 hipError_t launch_scale_residual(const void* U, const void* residual, void* C, int64_t M,
                                  int64_t N, float alpha, bool f16, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// Dynamic activation quantization (kernels_quant.hip): X[M][K] 16-bit floats
+// -> Q[M][K] codes and fp32 scales, per token ([M]) or per 1x128 block
+// ([M][K/128]).  K % 16 == 0 (K % 128 == 0 for blocks), M >= 1.
+enum DQKind : int { DQ_FP8_TOKEN = 0, DQ_INT8_TOKEN = 1, DQ_FP8_BLOCK = 2 };
+hipError_t launch_dynamic_quant(int kind, bool f16, const void* X, int64_t M, int64_t K, void* Q,
+                                float* scales, hipStream_t s);
 
 }  // namespace lg

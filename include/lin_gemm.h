@@ -150,6 +150,42 @@ int lin_gemm_run_unfused(lin_gemm_t h, const void *A, const void *B, const void 
                          int64_t N, int64_t K, float alpha, int quant_mode, int activation,
                          void *stream);
 
+/* Dynamic activation quantization: the step that produces A and the
+ * activation scales of the quantised modes from 16-bit activations at run
+ * time.  "helion-vllm-linear-backend", section "Одно ядро вместо трёх
+ * вариантов": per-token scales for FP8_Dynamic and W8A8_INT8, 1x128
+ * activation blocks for Block_FP8; the prologue/epilogue section of
+ * "Совместная работа Helion и TorchInductor" counts quantization among the
+ * input-side transforms.  For each group g (a row, or a 1x128 block of a
+ * row):  s_g = max|x| / QMAX in binary32 (QMAX = 448 for e4m3, 127 for
+ * int8; s_g = 1 if the group is all zero), and code = x / s_g (binary32,
+ * correctly rounded) rounded to nearest, ties to even, saturated to
+ * [-QMAX, QMAX].  Inputs must be finite (NaN / Inf give unspecified codes). */
+enum lin_dq_kind {
+    LIN_DQ_FP8_TOKEN = 0,  /* e4m3 codes, scales [M]        (LIN_Q_FP8_DYNAMIC) */
+    LIN_DQ_INT8_TOKEN = 1, /* int8 codes, scales [M]        (LIN_Q_W8A8_INT8)   */
+    LIN_DQ_FP8_BLOCK = 2   /* e4m3 codes, scales [M][K/128] (LIN_Q_BLOCK_FP8)   */
+};
+
+/* Quantize X[M][K] (bf16 if x_dtype == LIN_Q_BF16, fp16 if LIN_Q_FP16) into
+ * Q[M][K] (one byte per value) and scales (fp32, layout per kind).  All
+ * three are caller-owned device buffers, 16-byte aligned.  K must be a
+ * positive multiple of 16 (of 128 for LIN_DQ_FP8_BLOCK), else
+ * LIN_ERR_UNSUPPORTED; M == 0 is a no-op.  Enqueued on `stream`; no
+ * allocation. */
+int lin_gemm_quantize(lin_gemm_t h, const void *X, int x_dtype, int64_t M, int64_t K, int kind,
+                      void *Q, float *scales, void *stream);
+
+/* lin_gemm_quantize of X into handle-owned staging (grown on demand, like
+ * the split-K workspace), then lin_gemm_run with those codes and scales as
+ * A and scales->a.  quant_mode is LIN_Q_FP8_DYNAMIC, LIN_Q_W8A8_INT8 or
+ * LIN_Q_BLOCK_FP8 (else LIN_ERR_INVALID_ARG); sb is the weight scale array
+ * of that mode; other arguments and requirements as in lin_gemm_run. */
+int lin_gemm_run_dynamic(lin_gemm_t h, const void *X, int x_dtype, const void *B,
+                         const float *sb, float alpha, const void *bias, const void *residual,
+                         void *C, int64_t M, int64_t N, int64_t K, int quant_mode,
+                         int activation, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

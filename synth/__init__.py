@@ -203,6 +203,20 @@ def make_custom(quant: str, act: str, M: int, N: int, K: int, seed: int, bias=Tr
                    residual=res_c, alpha=alpha, name=f"{quant}_{act}_{M}x{N}x{K}_s{seed}")
 
 
+def activations16(M: int, K: int, seed: int, x_dtype: str = "bf16", outliers: bool = True):
+    """Seeded 16-bit activations X[M,K] (codes): N(0,1) rows, each scaled by a
+    per-row factor drawn log-uniformly in [0.01, 100], with a few large
+    outliers per row (up to 20x the row's scale) when ``outliers``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    x *= np.exp(rng.uniform(np.log(0.01), np.log(100.0), (M, 1))).astype(np.float32)
+    if outliers and K >= 64:
+        for m in range(M):
+            idx = rng.integers(0, K, 4)
+            x[m, idx] *= rng.uniform(5.0, 20.0, 4).astype(np.float32)
+    return to_fp16_bits(x) if x_dtype == "fp16" else to_bf16_bits(x)
+
+
 def algorithmic_bytes(quant: str, M: int, N: int, K: int, bias: bool, residual: bool) -> int:
     """Compulsory HBM bytes of one fused call: operands, scales, bias,
     residual and the one output write."""

@@ -162,3 +162,46 @@ def test_shipped_table_parses():
         pytest.skip("no shipped table yet")
     h = lg.Handle(path)
     h.close()
+
+
+def _raw_quantize(h, X=FAKE, x_dtype=0, M=4, K=256, kind=0, Q=FAKE, S=FAKE):
+    return lg.library().lin_gemm_quantize(h._h, X, x_dtype, M, K, kind, Q, S, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kind=3), INVALID),
+    (dict(kind=-1), INVALID),
+    (dict(x_dtype=2), INVALID),
+    (dict(M=-1), INVALID),
+    (dict(X=None), INVALID),
+    (dict(Q=None), INVALID),
+    (dict(S=None), INVALID),
+    (dict(K=40), UNSUPPORTED),                 # not a multiple of 16
+    (dict(K=0), UNSUPPORTED),
+    (dict(kind=2, K=144), UNSUPPORTED),        # 1x128 blocks need K % 128
+    (dict(X=FAKE + 8), UNSUPPORTED),           # misaligned
+    (dict(Q=FAKE + 4), UNSUPPORTED),
+    (dict(M=0), OK),                           # no-op
+])
+def test_quantize_argument_errors(cpu_handle, kw, status):
+    assert _raw_quantize(cpu_handle, **kw) == status
+
+
+@pytest.mark.parametrize("quant,status", [(0, INVALID), (1, INVALID), (5, INVALID)])
+def test_run_dynamic_needs_a_quantised_mode(cpu_handle, quant, status):
+    lib = lg.library()
+    assert lib.lin_gemm_run_dynamic(cpu_handle._h, FAKE, 0, FAKE, FAKE, 1.0, None, None, FAKE,
+                                    4, 16, 64, quant, 0, None) == status
+
+
+def test_run_dynamic_shape_errors(cpu_handle):
+    lib = lg.library()
+    # e4m3 rows of 40 bytes; block FP8 with N % 128 != 0; null sb; M == 0
+    assert lib.lin_gemm_run_dynamic(cpu_handle._h, FAKE, 0, FAKE, FAKE, 1.0, None, None, FAKE,
+                                    4, 16, 40, 2, 0, None) == UNSUPPORTED
+    assert lib.lin_gemm_run_dynamic(cpu_handle._h, FAKE, 0, FAKE, FAKE, 1.0, None, None, FAKE,
+                                    4, 100, 256, 4, 0, None) == UNSUPPORTED
+    assert lib.lin_gemm_run_dynamic(cpu_handle._h, FAKE, 0, FAKE, None, 1.0, None, None, FAKE,
+                                    4, 16, 64, 2, 0, None) == INVALID
+    assert lib.lin_gemm_run_dynamic(cpu_handle._h, FAKE, 0, FAKE, FAKE, 1.0, None, None, FAKE,
+                                    0, 16, 64, 2, 0, None) == OK
