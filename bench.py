@@ -215,6 +215,72 @@ def per_shape_table(torch, h, reps):
     return rows
 
 
+def dynamic_quant_rows(torch, h, reps):
+    """The dynamic activation quantization: the kernel alone (per-token e4m3
+    and int8, 1x128-block e4m3) over a rotation of activation copies, and the
+    FP8 decode with quantization in front (lin_gemm_run_dynamic) beside the
+    same decode on pre-quantized activations.  HBM-bound: the compulsory
+    bytes of the kernel are 2 per value read, 1 per code written and 4 per
+    scale."""
+    import synth
+    rows = []
+    kinds = [("fp8_token", "fp8_dynamic", 1, 4096), ("fp8_token", "fp8_dynamic", 32, 4096),
+             ("fp8_token", "fp8_dynamic", 4096, 4096), ("int8_token", "w8a8_int8", 4096, 4096),
+             ("fp8_block", "block_fp8", 4096, 12288)]
+    for kind, quant, M, K in kinds:
+        X = synth.activations16(M, K, seed=M + K)
+        xb = 2 * M * K
+        ncopy = max(2, min(16, -(-NCOPY_TARGET_BYTES // xb)))
+        Xs = [torch.from_numpy(X.view(np.int16)).cuda() for _ in range(ncopy)]
+        Q = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        nsc = M * (K // 128) if kind == "fp8_block" else M
+        S = torch.empty(nsc, dtype=torch.float32, device="cuda")
+        h.quantize(Xs[0], Q, S, kind)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for x in Xs:
+                h.quantize(x, Q, S, kind)
+        t = time_graphs(torch, [g], max(3, reps))[0] / ncopy
+        rows.append(shape_row(f"dynamic_quant_{kind}", quant, M, 0, K, t, 3 * M * K + 4 * nsc,
+                              0, "quantize"))
+        print(f"[shape] {rows[-1]}", file=sys.stderr, flush=True)
+        del g, Xs, Q, S
+    # The headline decode with the quantization in front (a separate kernel,
+    # or the decode kernel's own prologue where the table asks for it),
+    # interleaved with the pre-quantized call.
+    wl = Workload(torch, HEAD_CFG, [1, 8, 32])
+    for M in (1, 8, 32):
+        R = wl.ncopy
+        X = torch.from_numpy(synth.activations16(M, wl.K, seed=M).view(np.int16)).cuda()
+        d = wl.dev[M]
+
+        def call(copy):
+            h.run_dynamic(X, wl.B[copy % R], d["C"], quant=wl.quant, act=wl.act, sb=wl.sb,
+                          alpha=d["alpha"], bias=wl.bias, residual=d["residual"])
+        call(0)
+        torch.cuda.synchronize()
+        gd = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gd):
+            for r in range(R):
+                call(r)
+        gq = wl.graph(h, M, R)
+        td, tq = time_graphs(torch, [gd, gq], max(3, reps))
+        v = h.describe(wl.quant, M, wl.N, wl.K)
+        dyn_variant = (v + " (quantization prologue)") if "dq=1" in v else ("quantize + " + v)
+        # compulsory bytes: the layer's, with A read as 16-bit activations
+        nbytes = wl.bytes(M) - M * wl.K + 2 * M * wl.K
+        rows.append(shape_row("fp8_dynamic_decode_quantize_in_front", wl.quant, M, wl.N, wl.K,
+                              td / R, nbytes, wl.flops(M),
+                              dyn_variant, kernel_calls=1 if "dq=1" in dyn_variant else 2))
+        rows[-1]["us_prequantized"] = round(tq / R * 1e6, 3)
+        print(f"[shape] {rows[-1]}", file=sys.stderr, flush=True)
+        del gd, gq
+    del wl
+    torch.cuda.empty_cache()
+    return rows
+
+
 def unfused_graph(torch, h, wl, M):
     """A HIP graph of the three-kernel path on the prefill problem (GEMM -> T,
     bias+GELU -> U, 0.5*U + residual -> C) over the weight rotation."""
@@ -338,14 +404,15 @@ def main():
 
     # Dominant kernel: the decode instantiation with the most time.  The
     # template arguments are quant kind (2 = e4m3), token tiles (one 16-token
-    # tile up to M = 16, two up to 32), swap-AB, waves, unroll and 16-row
-    # weight tiles per workgroup (1 up to 16 rows, 2 up to 32, else 4).
+    # tile up to M = 16, two up to 32), swap-AB, waves, unroll, 16-row weight
+    # tiles per workgroup (1 up to 16 rows, 2 up to 32, else 4) and the
+    # quantization prologue (false: the headline feeds e4m3 activations).
     def kernel_name(M):
         v = dict(kv.split("=") for kv in h.describe(wl.quant, M, wl.N, wl.K).split()[1:])
         rows = int(v["rows"])
         rt = 1 if rows <= 16 else (2 if rows <= 32 else 4)
         return (f"decode_kernel<2, {1 if M <= 16 else 2}, {'true' if v['swap'] == '1' else 'false'}"
-                f", {v['waves']}, {v['unroll']}, {rt}>")
+                f", {v['waves']}, {v['unroll']}, {rt}, false>")
     groups = {}
     for M in Ms:
         groups.setdefault(kernel_name(M), []).append(M)
@@ -371,7 +438,7 @@ def main():
 
     shapes = None
     if not args.no_shapes:
-        shapes = per_shape_table(torch, h, args.reps)
+        shapes = per_shape_table(torch, h, args.reps) + dynamic_quant_rows(torch, h, args.reps)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
     out = {

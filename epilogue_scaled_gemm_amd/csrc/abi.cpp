@@ -418,11 +418,40 @@ int lin_gemm_run_dynamic(lin_gemm_t h, const void* X, int x_dtype, const void* B
   int rc = check_shape(h, quant_mode, M, N, K);
   if (rc != LIN_OK || M == 0) return rc;
   if (!X || !B || !C || !sb) return fail(h, LIN_ERR_INVALID_ARG, "X, B, sb and C must be non-null");
+  hipStream_t s = (hipStream_t)stream;
+  // Decode shapes: quantize in the kernel's prologue when the chosen variant
+  // has one (bf16 activations).
+  if (x_dtype == LIN_Q_BF16 && M <= 16) {
+    if (activation < LIN_ACT_NONE || (activation > LIN_ACT_SILU && activation != LIN_ACT_RAW_ACC))
+      return fail(h, LIN_ERR_INVALID_ARG, "unknown activation " + std::to_string(activation));
+    if (misaligned(X) || misaligned(B) || misaligned(C) || misaligned(bias) ||
+        misaligned(residual) || misaligned(sb))
+      return fail(h, LIN_ERR_UNSUPPORTED, "X, B, C, sb, bias and residual must be 16-byte aligned");
+    lg::Variant v;
+    rc = select_variant(h, quant_mode, M, N, K, &v);
+    if (rc != LIN_OK) return rc;
+    lg::Call c{};
+    c.A = X; c.B = B; c.M = M; c.N = N; c.K = K;
+    c.KB = K;
+    c.qk = qkind(quant_mode);
+    lin_scales_t sc{nullptr, sb, alpha};
+    c.epi = make_epi(&sc, bias, residual, C, M, N, quant_mode, activation);
+    const int split = resolve_split(v, c);
+    if (v.dq && lg::decode_dq_supported(v, c, split)) {
+      hipError_t e = lg::launch_decode_dq(v, c, s);
+      if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
+      if (std::getenv("LIN_GEMM_LOG"))
+        std::fprintf(stderr, "lin_gemm: dynamic quant=%d M=%lld N=%lld K=%lld -> %s (prologue)\n",
+                     quant_mode, (long long)M, (long long)N, (long long)K,
+                     lg::format_variant(v, split).c_str());
+      return LIN_OK;
+    }
+  }
+  // Otherwise: the quantization kernel into staging, then the layer.
   // Staging: the codes [M][K], then the scales (256-byte aligned).
   const size_t qbytes = ((size_t)M * (size_t)K + 255) & ~(size_t)255;
   const size_t nscale = kind == LIN_DQ_FP8_BLOCK ? (size_t)M * (size_t)(K / 128) : (size_t)M;
   const size_t need = qbytes + nscale * sizeof(float);
-  hipStream_t s = (hipStream_t)stream;
   if (need > h->dq_bytes) {
     hipError_t e = hipStreamSynchronize(s);  // in-flight calls may still read the old staging
     if (e != hipSuccess) return hip_fail(h, e, "hipStreamSynchronize");

@@ -120,6 +120,94 @@ template <bool F16> __device__ inline uint16_t f32_to_h(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// ------------------------------------------- dynamic quantization helpers
+// A quantization group (a token row, or a 1x128 block of one) divides every
+// value by its scale s = max|x| / QMAX and rounds the binary32 quotient to a
+// code.  The quotient must be the correctly rounded x / s.  Rather than a full
+// division per value, the group's reciprocal y = RN(1/s) is formed once and
+// each quotient takes Markstein's correction (P. Markstein, "Computation of
+// elementary functions on the IBM RISC System/6000 processor", IBM J. Res.
+// Dev. 34(1), 1990): q = RN(x y), r = x - s q (exact in one FMA), and
+// RN(q + r y) = RN(x / s) as long as nothing underflows.  Groups whose
+// maximum is below 2^-60 are first scaled by 2^64 (exact; the quotient is
+// unchanged), so the residual cannot underflow wherever the quotient is at
+// least 2^-12; below that (values that round to a zero code in both formats)
+// only the sign is guaranteed, and copysign keeps it.  An exhaustive check
+// over every bf16 / fp16 value within a group's maximum, for every third bf16
+// maximum and both QMAX, found no difference from the true division.
+struct DivBy {
+  float s;  // scale, times k
+  float y;  // RN(1 / s)
+  float k;  // 2^64 or 1
+};
+__device__ inline DivBy make_div(float s, float amax) {
+  DivBy d;
+  d.k = amax < 0x1p-60f ? 0x1p64f : 1.f;
+  d.s = s * d.k;
+  d.y = 1.f / d.s;  // correctly rounded division (the HIP default)
+  return d;
+}
+__device__ inline float div_rn(float x, const DivBy& d) {
+  const float xk = x * d.k;
+  const float q = __fmul_rn(xk, d.y);
+  const float r = __fmaf_rn(-d.s, q, xk);
+  return __builtin_copysignf(__fmaf_rn(r, d.y, q), x);
+}
+// Group scale from its maximum: max / QMAX in binary32, 1 for an all-zero
+// group.
+__device__ inline float group_scale(float amax, float qmax) {
+  return amax > 0.f ? amax / qmax : 1.f;
+}
+
+// Codes of 8 values of one group, packed into 8 bytes: e4m3 by the hardware
+// conversion (round to nearest even) after an explicit clamp to +-448, int8
+// by round-to-nearest-even and a clamp to +-127.
+template <bool INT8>
+__device__ inline i32x2 quant8(const float* x, const DivBy& d) {
+  i32x2 out;
+  if constexpr (INT8) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float r = __builtin_rintf(div_rn(x[4 * w + i], d));
+        r = fminf(fmaxf(r, -127.f), 127.f);
+        word |= ((uint32_t)(int)r & 0xFFu) << (8 * i);
+      }
+      out[w] = (int)word;
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = fminf(fmaxf(div_rn(x[4 * w + i], d), -448.f), 448.f);
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
+      out[w] = word;
+    }
+  }
+  return out;
+}
+
+// Eight 16-bit floats of one 16-byte chunk.
+template <bool F16>
+__device__ inline void unpack8(i32x4 w, float* x) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = h_to_f32<F16>((uint32_t)w[j] & 0xFFFFu);
+    x[2 * j + 1] = h_to_f32<F16>((uint32_t)w[j] >> 16);
+  }
+}
+
+__device__ inline float amax8(const float* x) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+  return m;
+}
+
 // ----------------------------------------------------------- activations
 __device__ inline float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
@@ -288,7 +376,7 @@ __device__ inline void epilogue_prefetch4(const Epi& e, int64_t m, int64_t n0, E
   for (int i = 0; i < 4; ++i) p.sb[i] = 1.f, p.bias[i] = 0.f, p.res[i] = 0.f;
   if (e.raw) return;
   if (e.scale_mode == 1) {
-    p.sam = e.sa[mm];
+    if (e.sa) p.sam = e.sa[mm];  // (no sa: the kernel derives it from its activations)
     if (full) {
       const f32x4 s = *(const f32x4*)(e.sb + n0);
 #pragma unroll

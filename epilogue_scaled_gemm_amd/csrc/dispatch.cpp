@@ -72,6 +72,7 @@ bool parse_variant(const std::string& spec, Variant* out, std::string* err) {
     else if (k == "waves") v.waves = xi;
     else if (k == "unroll") v.unroll = xi;
     else if (k == "rows") v.rows = xi;
+    else if (k == "dq") v.dq = xi ? 1 : 0;
     else { *err = "unknown key '" + k + "'"; return false; }
   }
   if (v.kind == V_TILE && !tile_supported(0, v.bm, v.bn, v.wm, v.wn)) {
@@ -106,6 +107,7 @@ std::string format_variant(const Variant& v, int split) {
   } else {
     os << "decode swap=" << v.swap << " split=" << split << " reduce=" << reduce_name(v.reduce)
        << " waves=" << v.waves << " unroll=" << v.unroll << " rows=" << v.rows;
+    if (v.dq) os << " dq=1";
   }
   return os.str();
 }
@@ -157,11 +159,13 @@ const char* builtin_table() {
   return R"TABLE(
 # quant        m_lo m_hi N     K      variant
 # measured entries (offline sweep on MI355X, graph replay, rotating weights)
-fp8_dynamic    1    2    6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=1 rows=12
+fp8_dynamic    1    1    6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=1 rows=12 dq=1
+fp8_dynamic    2    2    6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=1 rows=12
 fp8_dynamic    3    32   6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=4 rows=24
 w8a8_int8      1    4    24576 4096   decode swap=1 split=1 reduce=twopass waves=4 unroll=4 rows=16
 w8a8_int8      5    32   24576 4096   decode swap=1 split=1 reduce=twopass waves=4 unroll=2 rows=32
-block_fp8      1    16   4096  12288  decode swap=1 split=1 reduce=twopass waves=12 unroll=1 rows=16
+block_fp8      1    1    4096  12288  decode swap=1 split=1 reduce=twopass waves=12 unroll=1 rows=16 dq=1
+block_fp8      2    16   4096  12288  decode swap=1 split=1 reduce=twopass waves=12 unroll=1 rows=16
 block_fp8      17   32   4096  12288  decode swap=1 split=2 reduce=twopass waves=8 unroll=2 rows=32
 block_fp8      257  *    4096  12288  pp split=0 group=4
 block_fp8      33   256  4096  12288  tile bm=64 bn=64 wm=2 wn=2 group=4

@@ -69,7 +69,104 @@ __device__ inline i32x8 cat(i32x4 a, i32x4 b) {
 // the operands in the owning waves instead.
 constexpr bool op_wave(bool swap, int w) { return swap && w >= 8 && w < 16; }
 
-template <int QK, int NTT, bool SWAP, int W, int U, int RT>
+// DQ: A holds bf16 activations X[M][K] instead of codes, and the kernel
+// quantizes them itself in a prologue (swap, one token tile, split 1): the
+// whole workgroup reads its tokens' rows once, takes each group's maximum
+// (per token, or per 1x128 block), and writes the codes to LDS
+// (dynamic shared memory: M rows of KB + 16 bytes, then the scales), while
+// the first weight batch is already in flight.  The K loop then reads its
+// activation fragments from LDS, and the epilogue takes the per-token scale
+// from there.  Codes and scales are those of lin_gemm_quantize.
+constexpr int DQ_CHUNKS = 4;  // 16-byte activation chunks per thread kept in registers
+
+// The quantization prologue, run by every thread of the workgroup.  X[M][K]
+// is contiguous, so chunk c (8 values) of the M x K region sits at X + 8c, in
+// row c / (K/8).  Per-token groups take their maximum through LDS atomics
+// (one barrier); 1x128 blocks are 16 consecutive chunks, i.e. 16 consecutive
+// lanes, and take theirs by a 16-lane shuffle.  Scales go to sal, codes to
+// xq (row stride LS).  Ends with a barrier, after which xq and sal are
+// complete.
+template <int QK>
+__device__ inline void quant_prologue(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                      float* sal, uint8_t* xq, int64_t LS) {
+  constexpr bool BLOCK = QK == QK_FP8_BLOCK;
+  constexpr bool INT8 = QK == QK_I8;
+  constexpr float QMAX = INT8 ? 127.f : 448.f;
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const uint32_t cpr = (uint32_t)(K / 8);
+  const uint32_t nchunk = (uint32_t)M * cpr;
+  i32x4 xc[DQ_CHUNKS];
+#pragma unroll
+  for (int j = 0; j < DQ_CHUNKS; ++j) {
+    // chunks past the region re-read its last chunk and are never stored
+    const uint32_t c = min((uint32_t)(tid + j * nthr), nchunk - 1);
+    if ((uint32_t)(j * nthr) < nchunk) xc[j] = *(const i32x4*)(X + (size_t)c * 8);
+    else xc[j] = i32x4{0, 0, 0, 0};
+  }
+  auto store = [&](uint32_t c, const float* v, const DivBy& d) {
+    const uint32_t m = c / cpr;
+    *(i32x2*)(xq + m * LS + (int64_t)(c - m * cpr) * 8) = quant8<INT8>(v, d);
+  };
+  if constexpr (BLOCK) {
+    const uint32_t kblk = (uint32_t)(K / 128);
+    auto one = [&](uint32_t c, i32x4 w) {
+      float v[8];
+      unpack8<false>(w, v);
+      float am = amax8(v);
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 16));
+      if (c < nchunk) {
+        const float sc = group_scale(am, QMAX);
+        store(c, v, make_div(sc, am));
+        const uint32_t m = c / cpr, k8 = c - m * cpr;
+        if ((k8 & 15) == 0) sal[m * kblk + k8 / 16] = sc;
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < DQ_CHUNKS; ++j) one((uint32_t)(tid + j * nthr), xc[j]);
+    for (uint32_t cb = (uint32_t)(DQ_CHUNKS * nthr); cb < nchunk; cb += (uint32_t)nthr) {
+      const uint32_t c = cb + (uint32_t)tid;
+      one(c, *(const i32x4*)(X + (size_t)min(c, nchunk - 1) * 8));
+    }
+  } else {
+    uint32_t* amax_u = (uint32_t*)(sal + M);
+    if (tid < M) amax_u[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < DQ_CHUNKS; ++j) {
+      const uint32_t c = (uint32_t)(tid + j * nthr);
+      if (c < nchunk) {
+        float v[8];
+        unpack8<false>(xc[j], v);
+        atomicMax(&amax_u[c / cpr], __float_as_uint(amax8(v)));
+      }
+    }
+    for (uint32_t c = (uint32_t)(tid + DQ_CHUNKS * nthr); c < nchunk; c += (uint32_t)nthr) {
+      float v[8];
+      unpack8<false>(*(const i32x4*)(X + (size_t)c * 8), v);
+      atomicMax(&amax_u[c / cpr], __float_as_uint(amax8(v)));
+    }
+    __syncthreads();
+    auto one = [&](uint32_t c, i32x4 w) {
+      const float am = __uint_as_float(amax_u[c / cpr]);
+      float v[8];
+      unpack8<false>(w, v);
+      store(c, v, make_div(group_scale(am, QMAX), am));
+    };
+#pragma unroll
+    for (int j = 0; j < DQ_CHUNKS; ++j) {
+      const uint32_t c = (uint32_t)(tid + j * nthr);
+      if (c < nchunk) one(c, xc[j]);
+    }
+    for (uint32_t c = (uint32_t)(tid + DQ_CHUNKS * nthr); c < nchunk; c += (uint32_t)nthr)
+      one(c, *(const i32x4*)(X + (size_t)c * 8));
+    if (tid < M) sal[tid] = group_scale(__uint_as_float(amax_u[tid]), QMAX);
+  }
+  __syncthreads();
+}
+
+template <int QK, int NTT, bool SWAP, int W, int U, int RT, bool DQ>
 __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int64_t M, int64_t N,
     int64_t KB, int rpw, int split, int steps_per_split, int reduce, Epi e,
@@ -88,6 +185,8 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
   constexpr int NOP = 13;
   __shared__ float opnd[OPW ? NTILE : 1][NOP][64];
   __shared__ int arrival;
+  extern __shared__ __align__(16) uint8_t dq_lds[];
+  static_assert(!DQ || (SWAP && NTT == 1), "the quantization prologue is for swap, one token tile");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -123,6 +222,13 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
   const uint8_t* xp[NTT];
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) xp[tt] = A + min((int64_t)(tt * 16 + l16), M - 1) * KB + g * 32;
+  // With DQ: the codes in LDS (row stride KB + 16) and the scales after them
+  // (sal[M] per token, or sal[M][KB / 128] per block).
+  const int64_t LS = KB + 16;
+  float* sal = (float*)(dq_lds + M * LS);
+  const uint8_t* xl[NTT];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) xl[tt] = dq_lds + min((int64_t)(tt * 16 + l16), M - 1) * LS + g * 32;
 
   // Block scales: sb[n0/128][kb] is uniform over the workgroup; sa[tok][kb]
   // per lane (one token per tile with swap, four without).
@@ -136,7 +242,7 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
 #pragma unroll
       for (int r = 0; r < NS; ++r) {
         const int64_t tok = SWAP ? (tt * 16 + l16) : (tt * 16 + g * 4 + r);
-        sa_p[tt][r] = e.sa + min(tok, M - 1) * KBLK;
+        sa_p[tt][r] = DQ ? nullptr : e.sa + min(tok, M - 1) * KBLK;
       }
   }
 
@@ -146,7 +252,9 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
   // then consume it.  A wave's steps usually fit one batch, so every load of
   // the kernel is in flight at once and each MFMA waits only for its own
   // step.  Each activation slice feeds RT weight tiles.
-  auto load_batch = [&](int t0) {
+  // part: 0 = weights and activations, 1 = weights only, 2 = activations
+  // (and block scales) only.
+  auto load_batch = [&](int t0, int part = 0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u;
@@ -161,13 +269,26 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
       const bool ok1 = live && (o1 < KB);
       const int64_t c0 = (o0 < KB ? o0 : KB - 16) - g * 32;
       const int64_t c1 = (o1 < KB ? o1 : KB - 16) - g * 32;
+      if (part != 2) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        wb[u][rt] = cat(ld16(wp[rt] + c0, ok0 && wrow[rt]), ld16(wp[rt] + c1, ok1 && wrow[rt]));
+        for (int rt = 0; rt < RT; ++rt)
+          wb[u][rt] = cat(ld16(wp[rt] + c0, ok0 && wrow[rt]), ld16(wp[rt] + c1, ok1 && wrow[rt]));
+      }
+      if (part == 1) continue;
+      if constexpr (DQ) {
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt)
-        xb[u][tt] = cat(ld16(xp[tt] + c0, ok0), ld16(xp[tt] + c1, ok1));
-      if constexpr (BLOCK) {
+        for (int tt = 0; tt < NTT; ++tt)
+          xb[u][tt] = cat(ld16(xl[tt] + c0, ok0), ld16(xl[tt] + c1, ok1));
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt)
+          xb[u][tt] = cat(ld16(xp[tt] + c0, ok0), ld16(xp[tt] + c1, ok1));
+      }
+      if constexpr (BLOCK && DQ) {
+        const float sbv = live ? sb_p[st] : 0.f;
+        const int64_t tok = min((int64_t)l16, M - 1);
+        sc[u][0][0] = live ? sal[tok * KBLK + st] * sbv : 0.f;
+      } else if constexpr (BLOCK) {
         const float sbv = live ? sb_p[st] : 0.f;
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt)
@@ -222,8 +343,12 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
   const bool fin_here = split == 1 || reduce != R_TWOPASS;
   constexpr int QPW = (NTILE + W - 1) / W;  // tiles per wave, at most
   EpiPre4 pre[SWAP && !OPW ? QPW : 1];
+  if constexpr (DQ) {
+    if (!opw) load_batch(0, 1);
+    quant_prologue<QK>((const uint16_t*)A, M, KB, sal, dq_lds, LS);
+  }
   if (!opw) {
-    load_batch(0);
+    load_batch(0, DQ ? 2 : 0);
     if constexpr (SWAP && !OPW) {
       if (fin_here) {
 #pragma unroll
@@ -298,19 +423,21 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
   auto finish_swap = [&](int q, int i, const AccT* v) {
     const int64_t nr = n0 + (q / NTT) * 16 + g * 4;
     if (nr >= nend) return;
-    if constexpr (!OPW) {
-      epilogue_run4_pre<F16>(e, (q % NTT) * 16 + l16, nr, v, pre[SWAP && !OPW ? i : 0]);
-      return;
-    }
+    const int64_t m = (q % NTT) * 16 + l16;
     EpiPre4 p;
-    p.sam = opnd[q][0][lane];
+    if constexpr (!OPW) {
+      p = pre[SWAP && !OPW ? i : 0];
+    } else {
+      p.sam = opnd[q][0][lane];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p.sb[j] = opnd[q][1 + j][lane];
-      p.bias[j] = opnd[q][5 + j][lane];
-      p.res[j] = opnd[q][9 + j][lane];
+      for (int j = 0; j < 4; ++j) {
+        p.sb[j] = opnd[q][1 + j][lane];
+        p.bias[j] = opnd[q][5 + j][lane];
+        p.res[j] = opnd[q][9 + j][lane];
+      }
     }
-    epilogue_run4_pre<F16>(e, (q % NTT) * 16 + l16, nr, v, p);
+    if constexpr (DQ && !BLOCK) p.sam = sal[min(m, M - 1)];
+    epilogue_run4_pre<F16>(e, m, nr, v, p);
   };
   auto reduce_tile = [&](int q, AccT* v) {
 #pragma unroll
@@ -420,14 +547,23 @@ __global__ __launch_bounds__(256) void splitk_reduce(const void* __restrict__ ws
   epilogue_run<4, QTraits<QK>::out_f16>(e, m, n, v);
 }
 
-template <int QK, int NTT, bool SWAP, int W, int U, int RT>
+// Dynamic LDS of the quantization prologue: M code rows of KB + 16 bytes,
+// then the scales (per token: M, plus M maxima; per block: M x KB/128).
+inline size_t dq_lds_bytes(int qk, const Call& c) {
+  const size_t rows = (size_t)c.M * (size_t)(c.KB + 16);
+  const size_t sc = qk == QK_FP8_BLOCK ? 4 * (size_t)c.M * (size_t)(c.KB / 128) : 8 * (size_t)c.M;
+  return (rows + sc + 15) & ~(size_t)15;
+}
+
+template <int QK, int NTT, bool SWAP, int W, int U, int RT, bool DQ = false>
 hipError_t launch_d(const Variant& v, const Call& c, int split, hipStream_t s) {
   const int groups = (int)((c.N + v.rows - 1) / v.rows);
   const int total_steps = (int)((c.KB + STEPB - 1) / STEPB);
   const int sps = (total_steps + split - 1) / split;
-  hipLaunchKernelGGL((decode_kernel<QK, NTT, SWAP, W, U, RT>), dim3(groups, split),
+  const size_t dyn = DQ ? dq_lds_bytes(QK, c) : 0;
+  hipLaunchKernelGGL((decode_kernel<QK, NTT, SWAP, W, U, RT, DQ>), dim3(groups, split),
                      dim3((W + (op_wave(SWAP, W) ? 1 : 0)) * 64),
-                     0, s, (const uint8_t*)c.A, (const uint8_t*)c.B, c.M, c.N, c.KB, v.rows, split,
+                     dyn, s, (const uint8_t*)c.A, (const uint8_t*)c.B, c.M, c.N, c.KB, v.rows, split,
                      sps, v.reduce, c.epi, c.ws, c.counters);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || split == 1 || v.reduce != R_TWOPASS) return err;
@@ -463,6 +599,42 @@ hipError_t launch_dq(const Variant& v, const Call& c, int split, hipStream_t s) 
 template <int QK>
 hipError_t launch_q(const Variant& v, const Call& c, int split, hipStream_t s) {
   return c.M <= 16 ? launch_dq<QK, 1>(v, c, split, s) : launch_dq<QK, 2>(v, c, split, s);
+}
+
+// Variants with the quantization prologue (bf16 activations; swap, one token
+// tile, split 1).
+#define LG_DECODE_DQ(X, QK)                                                            \
+  X(QK, 8, 1, 1) X(QK, 8, 2, 1) X(QK, 8, 4, 1) X(QK, 8, 4, 2) X(QK, 12, 1, 1) \
+  X(QK, 4, 4, 1)
+
+// Whether the prologue variant exists and its LDS (static + dynamic) fits
+// the device's per-workgroup limit; if so, *fn is the kernel.
+template <int QK>
+bool dq_kernel(const Variant& v, const Call& c, const void** fn) {
+  *fn = nullptr;
+#define LG_DQ_FN(qk, w, u, rt)                                                      \
+  if (v.waves == w && v.unroll == u && tiles_for(v.rows) == rt)                     \
+    *fn = reinterpret_cast<const void*>(&decode_kernel<qk, 1, true, w, u, rt, true>);
+  LG_DECODE_DQ(LG_DQ_FN, QK)
+#undef LG_DQ_FN
+  if (!*fn) return false;
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, *fn) != hipSuccess) return false;
+  int dev = 0, max_lds = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return false;
+  return attr.sharedSizeBytes + dq_lds_bytes(QK, c) <= (size_t)max_lds;
+}
+
+template <int QK>
+hipError_t launch_dq_prologue(const Variant& v, const Call& c, hipStream_t s) {
+#define LG_DQ_TRY(qk, w, u, rt)                                                     \
+  if (v.waves == w && v.unroll == u && tiles_for(v.rows) == rt)                     \
+    return launch_d<qk, 1, true, w, u, rt, true>(v, c, 1, s);
+  LG_DECODE_DQ(LG_DQ_TRY, QK)
+#undef LG_DQ_TRY
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -504,6 +676,26 @@ hipError_t launch_splitk_reduce(int qk, const void* ws, int split, const Epi& e,
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+bool decode_dq_supported(const Variant& v, const Call& c, int split) {
+  if (v.kind != V_DECODE || v.swap != 1 || split != 1 || c.M < 1 || c.M > 16) return false;
+  const void* fn;
+  switch (c.qk) {
+    case QK_FP8: return dq_kernel<QK_FP8>(v, c, &fn);
+    case QK_I8: return dq_kernel<QK_I8>(v, c, &fn);
+    case QK_FP8_BLOCK: return dq_kernel<QK_FP8_BLOCK>(v, c, &fn);
+  }
+  return false;
+}
+
+hipError_t launch_decode_dq(const Variant& v, const Call& c, hipStream_t s) {
+  switch (c.qk) {
+    case QK_FP8: return launch_dq_prologue<QK_FP8>(v, c, s);
+    case QK_I8: return launch_dq_prologue<QK_I8>(v, c, s);
+    case QK_FP8_BLOCK: return launch_dq_prologue<QK_FP8_BLOCK>(v, c, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const Variant& v, const Call& c, int split, hipStream_t s) {

@@ -21,7 +21,9 @@
 // through LDS.  A 1x128 block is 16 lanes x 8 values: its maximum needs only
 // a 16-lane shuffle reduction, no LDS and no barrier.  e4m3 codes come from
 // the hardware conversion (round to nearest even) after an explicit clamp to
-// +-448; int8 codes from v_rndne and a clamp.
+// +-448; int8 codes from v_rndne and a clamp.  The quotients x / s use one
+// reciprocal per group and an FMA correction per value (div_rn), which gives
+// the correctly rounded quotient without a division per value.
 #include "launch.hpp"
 
 namespace lg {
@@ -29,52 +31,6 @@ namespace {
 
 constexpr int DQ_THREADS = 256;
 constexpr int DQ_CACHE = 4;  // 16-byte chunks per thread kept in registers
-
-template <bool F16>
-__device__ inline void unpack8(i32x4 w, float* x) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    x[2 * j] = h_to_f32<F16>((uint32_t)w[j] & 0xFFFFu);
-    x[2 * j + 1] = h_to_f32<F16>((uint32_t)w[j] >> 16);
-  }
-}
-
-__device__ inline float amax8(const float* x) {
-  float m = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
-  return m;
-}
-
-// Codes of x[i] / s for 8 values, packed into 8 bytes.
-template <bool INT8>
-__device__ inline i32x2 quant8(const float* x, float s) {
-  i32x2 out;
-  if constexpr (INT8) {
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float r = __builtin_rintf(x[4 * w + i] / s);
-        r = fminf(fmaxf(r, -127.f), 127.f);
-        word |= ((uint32_t)(int)r & 0xFFu) << (8 * i);
-      }
-      out[w] = (int)word;
-    }
-  } else {
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = fminf(fmaxf(x[4 * w + i] / s, -448.f), 448.f);
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
-      out[w] = word;
-    }
-  }
-  return out;
-}
 
 // One token row per workgroup.
 template <bool F16, bool INT8>
@@ -113,8 +69,9 @@ __global__ __launch_bounds__(DQ_THREADS) void dq_token_kernel(const uint16_t* __
   if ((tid & 63) == 0) wmax[tid >> 6] = am;
   __syncthreads();
   am = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float s = am > 0.f ? am / (INT8 ? 127.f : 448.f) : 1.f;
+  const float s = group_scale(am, INT8 ? 127.f : 448.f);
   if (tid == 0) scales[row] = s;
+  const DivBy d = make_div(s, am);
 
   // Rounding pass.
 #pragma unroll
@@ -123,13 +80,13 @@ __global__ __launch_bounds__(DQ_THREADS) void dq_token_kernel(const uint16_t* __
     if (c < nch) {
       float v[8];
       unpack8<F16>(cache[j], v);
-      *(i32x2*)(q + (int64_t)c * 8) = quant8<INT8>(v, s);
+      *(i32x2*)(q + (int64_t)c * 8) = quant8<INT8>(v, d);
     }
   }
   for (int c = tid + DQ_CACHE * DQ_THREADS; c < nch; c += DQ_THREADS) {
     float v[8];
     unpack8<F16>(*(const i32x4*)(x + (int64_t)c * 8), v);
-    *(i32x2*)(q + (int64_t)c * 8) = quant8<INT8>(v, s);
+    *(i32x2*)(q + (int64_t)c * 8) = quant8<INT8>(v, d);
   }
 }
 
@@ -152,9 +109,9 @@ __global__ __launch_bounds__(DQ_THREADS) void dq_block_kernel(const uint16_t* __
   float am = amax8(v);
 #pragma unroll
   for (int off = 8; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 16));
-  const float s = am > 0.f ? am / 448.f : 1.f;
+  const float s = group_scale(am, 448.f);
   if (b < nblk) {
-    *(i32x2*)(Q + bc * 128 + sub * 8) = quant8<false>(v, s);
+    *(i32x2*)(Q + bc * 128 + sub * 8) = quant8<false>(v, make_div(s, am));
     if (sub == 0) scales[b] = s;
   }
 }

@@ -26,6 +26,10 @@ struct Variant {
   // weight rows per workgroup (4..64, a multiple of 4; each activation load
   // feeds all of them)
   int swap = 1, split = 0, reduce = R_TWOPASS, waves = 8, unroll = 2, rows = 16;
+  // lin_gemm_run_dynamic with a decode variant: 1 = quantize the activations
+  // in the kernel's prologue where that variant supports it, 0 = in a
+  // separate kernel first (the default: the prologue pays only for one token)
+  int dq = 0;
 };
 
 struct Call {
@@ -55,6 +59,12 @@ bool decode_supported(int swap, int waves, int unroll, int rows);
 int decode_auto_split(const Call& c, const Variant& v);
 size_t decode_ws_bytes(const Variant& v, const Call& c, int split);
 hipError_t launch_decode(const Variant& v, const Call& c, int split, hipStream_t s);
+// Decode with the quantization prologue: c.A holds bf16 activations X[M][K],
+// c.KB = K, c.epi.sa is unused (per-token scales come from the prologue).
+// Supported for swap, split 1, M <= 16, e4m3 / int8 / block e4m3, the
+// variants the library compiles with it, and LDS within the device limit.
+bool decode_dq_supported(const Variant& v, const Call& c, int split);
+hipError_t launch_decode_dq(const Variant& v, const Call& c, hipStream_t s);
 // Second pass of a two-pass split-K reduction: sums the fp32 / int32 slices
 // [split][M][N] in slice order and applies the epilogue.
 hipError_t launch_splitk_reduce(int qk, const void* ws, int split, const Epi& e, hipStream_t s);

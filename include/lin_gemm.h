@@ -176,11 +176,18 @@ enum lin_dq_kind {
 int lin_gemm_quantize(lin_gemm_t h, const void *X, int x_dtype, int64_t M, int64_t K, int kind,
                       void *Q, float *scales, void *stream);
 
-/* lin_gemm_quantize of X into handle-owned staging (grown on demand, like
- * the split-K workspace), then lin_gemm_run with those codes and scales as
- * A and scales->a.  quant_mode is LIN_Q_FP8_DYNAMIC, LIN_Q_W8A8_INT8 or
- * LIN_Q_BLOCK_FP8 (else LIN_ERR_INVALID_ARG); sb is the weight scale array
- * of that mode; other arguments and requirements as in lin_gemm_run. */
+/* The layer on 16-bit activations X[M][K], quantized on the fly as
+ * lin_gemm_quantize does.  quant_mode is LIN_Q_FP8_DYNAMIC, LIN_Q_W8A8_INT8
+ * or LIN_Q_BLOCK_FP8 (else LIN_ERR_INVALID_ARG); sb is the weight scale
+ * array of that mode; other arguments and requirements as in lin_gemm_run.
+ * For bf16 X and up to 16 tokens, when the shape's decode variant asks for
+ * the quantization prologue ("dq=1" in the variant spec) and its LDS fits,
+ * one kernel does both: the workgroup quantizes X into LDS and the K loop
+ * reads the codes from there (the prologue fusion of the input-side
+ * transforms the pages describe).  Otherwise lin_gemm_quantize runs into
+ * handle-owned staging (grown on demand, like the split-K workspace) and
+ * lin_gemm_run follows.  Both forms give the same codes and scales, and the
+ * same output bits for the same variant. */
 int lin_gemm_run_dynamic(lin_gemm_t h, const void *X, int x_dtype, const void *B,
                          const float *sb, float alpha, const void *bias, const void *residual,
                          void *C, int64_t M, int64_t N, int64_t K, int quant_mode,

@@ -151,3 +151,68 @@ def test_run_dynamic_staging_grows_and_shrinks(handle):
                            bias=dev(p.bias))
         torch.cuda.synchronize()
         assert_close(decode_out(C, "fp8_dynamic"), ref, f"staging M={M}")
+
+
+# The quantization prologue inside the decode kernel (lin_gemm_run_dynamic,
+# bf16 activations, up to 16 tokens): each compiled prologue variant against
+# the oracle, and bit for bit against the same variant fed by the separate
+# quantization kernel (the default, dq=0): the codes, scales and summation
+# order are the same, so the outputs must be identical.
+DQ_SHAPES = [(8, 1, 12), (8, 2, 16), (8, 4, 12), (8, 4, 24), (12, 1, 16), (4, 4, 16)]
+DQ_CASES = [
+    ("fp8_dynamic", "none", 1, 1040, 4096, True, False),
+    ("fp8_dynamic", "gelu_tanh", 5, 528, 272, True, True),
+    ("fp8_dynamic", "silu", 16, 6144, 4096, True, False),
+    ("w8a8_int8", "silu", 8, 2064, 4096, False, False),
+    ("w8a8_int8", "none", 2, 256, 1040, True, True),
+    ("block_fp8", "none", 3, 512, 3072, False, True),
+    ("block_fp8", "gelu_tanh", 16, 256, 1024, True, False),
+]
+
+
+def _dyn_run(handle, X, p, spec, act=None, raw=False):
+    M, N = p.M, p.N
+    C = torch.empty((M, N), dtype=torch.int32 if raw else torch.int16, device="cuda")
+    handle.set_force(spec)
+    try:
+        handle.run_dynamic(X, dev(p.B), C, quant=p.quant, act="raw_acc" if raw else (act or p.act),
+                           sb=dev(p.sb), alpha=p.alpha, bias=dev(p.bias),
+                           residual=dev(p.residual))
+    finally:
+        handle.set_force(None)
+    torch.cuda.synchronize()
+    return C.cpu()
+
+
+@pytest.mark.parametrize("case", DQ_CASES, ids=[f"{c[0]}-M{c[2]}-N{c[3]}-K{c[4]}" for c in DQ_CASES])
+def test_prologue_variants_match_oracle_and_two_kernel_path(handle, case):
+    quant, act, M, N, K, b, r = case
+    p = synth.make_custom(quant, act, M, N, K, seed=11 * M + K, bias=b, residual=r)
+    Xh = synth.activations16(M, K, seed=7 * M + N)
+    kind = {"fp8_dynamic": "fp8_token", "w8a8_int8": "int8_token", "block_fp8": "fp8_block"}[quant]
+    Qr, Sr = oracle.dynamic_quant(kind, Xh)
+    ref, acc = oracle.linear(quant, act, Qr, p.B, Sr, p.sb, p.bias, p.residual, p.alpha)
+    X = dev(Xh)
+    for w, u, rows in DQ_SHAPES:
+        if quant == "block_fp8" and 128 % rows:
+            continue
+        spec = f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} rows={rows}"
+        print(f"[prologue] {quant} {M}x{N}x{K} {spec}", flush=True)
+        C1 = _dyn_run(handle, X, p, spec + " dq=1")
+        assert_close(decode_out(C1, quant), ref, f"prologue {quant} {M}x{N}x{K} [{spec}]")
+        C0 = _dyn_run(handle, X, p, spec)
+        assert torch.equal(C1, C0), f"prologue vs two-kernel differ [{spec}]"
+        if acc is not None:
+            Craw = _dyn_run(handle, X, p, spec + " dq=1", raw=True)
+            assert np.array_equal(Craw.numpy(), acc), f"int8 accumulator [{spec}]"
+
+
+def test_prologue_falls_back_when_lds_does_not_fit(handle):
+    # 16 tokens of K = 12288 codes need ~197 KB of LDS: the call takes the
+    # two-kernel path and still matches the oracle.
+    p = synth.make_custom("block_fp8", "none", 16, 256, 12288, seed=3, bias=True)
+    Xh = synth.activations16(16, 12288, seed=4)
+    Qr, Sr = oracle.dynamic_quant("fp8_block", Xh)
+    ref, _ = oracle.linear("block_fp8", "none", Qr, p.B, Sr, p.sb, p.bias)
+    C = _dyn_run(handle, dev(Xh), p, "decode swap=1 split=1 reduce=twopass waves=8 unroll=1 rows=16 dq=1")
+    assert_close(decode_out(C, "block_fp8"), ref, "block fp8 16 x 12288 fallback")
