@@ -9,6 +9,9 @@ works but every call raises.
     h = Handle()
     h.run(A, B, C, quant="fp8_dynamic", act="none", sa=sa, sb=sb, bias=bias)
 
+PyTorch integration (custom operators with fake implementations, an FX pass
+that fuses linear + epilogue chains) lives in ``epilogue_scaled_gemm_amd.torch_ops``.
+
 Operands are contiguous CUDA tensors.  A[M,K] and B[N,K] hold bf16 / fp16 /
 float8_e4m3fn / int8 values (or the same bytes as uint16 / uint8 views);
 bias[N], residual[M,N] and C[M,N] are bf16 (fp16 in fp16 mode); sa, sb are
