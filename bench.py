@@ -90,10 +90,14 @@ def counters_prefill(torch, h):
 
 
 def source_digest():
-    """Hash of the kernel sources (to tell whether stored counters still apply)."""
+    """Hash of the kernel sources, .hip and .hpp (to tell whether stored
+    counters still apply; the variant table and host code do not change a
+    kernel's traffic)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "epilogue_scaled_gemm_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if not name.endswith((".hip", ".hpp")):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]

@@ -153,20 +153,15 @@ bool parse_table(const std::string& text, std::vector<TableEntry>* out, std::str
   return true;
 }
 
-// Built-in default: decode family for up to 32 tokens (swap-AB, K split
-// among the waves of each workgroup), then tile sizes growing with M.
+// Built-in table: the measured decode entries the offline sweep writes
+// (table_mi355x.inc: exact (quant, N, K) shapes and token ranges), the
+// measured prefill-shape entries, then the defaults: decode family for up to 32 tokens (swap-AB, K split among the
+// waves of each workgroup), then tile sizes growing with M.
 const char* builtin_table() {
-  return R"TABLE(
-# quant        m_lo m_hi N     K      variant
-# measured entries (offline sweep on MI355X, graph replay, rotating weights)
-fp8_dynamic    1    1    6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=1 rows=12 dq=1
-fp8_dynamic    2    2    6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=1 rows=12
-fp8_dynamic    3    32   6144  4096   decode swap=1 split=1 reduce=twopass waves=8 unroll=4 rows=24
-w8a8_int8      1    4    24576 4096   decode swap=1 split=1 reduce=twopass waves=4 unroll=4 rows=16
-w8a8_int8      5    32   24576 4096   decode swap=1 split=1 reduce=twopass waves=4 unroll=2 rows=32
-block_fp8      1    1    4096  12288  decode swap=1 split=1 reduce=twopass waves=12 unroll=1 rows=16 dq=1
-block_fp8      2    16   4096  12288  decode swap=1 split=1 reduce=twopass waves=12 unroll=1 rows=16
-block_fp8      17   32   4096  12288  decode swap=1 split=2 reduce=twopass waves=8 unroll=2 rows=32
+  static const std::string text = std::string(
+#include "table_mi355x.inc"
+  ) + R"TABLE(
+# prefill-shape entries (measured by the same sweep)
 block_fp8      257  *    4096  12288  pp split=0 group=4
 block_fp8      33   256  4096  12288  tile bm=64 bn=64 wm=2 wn=2 group=4
 bf16           1025 *    4096  4096   pp group=4
@@ -182,6 +177,7 @@ fp16           1025 *    *     *      pp group=4
 w8a8_int8      1025 *    *     *      pp group=4
 *              1025 *    *     *      tile bm=256 bn=256 wm=2 wn=4 group=4
 )TABLE";
+  return text.c_str();
 }
 
 bool lookup(const std::vector<TableEntry>& t, int quant, long long M, long long N, long long K,

@@ -10,6 +10,15 @@ shapes otherwise); each candidate is timed as a HIP-graph replay of calls
 over a rotation of weight copies larger than the 256 MB MALL.
 
     python -m epilogue_scaled_gemm_amd.sweep [--out PATH] [--workloads 2,3,4]
+        [--all-m] [--dynamic] [--emit-inc PATH]
+
+--all-m sweeps every token count 1..32 of the decode workloads (not only the
+workloads' own list); --dynamic also times lin_gemm_run_dynamic with the
+winning decode variant with and without the quantization prologue (dq=1)
+and keeps the prologue where it is faster; --emit-inc writes the measured
+entries as the C++ include that the library compiles in as its built-in
+table (csrc/table_mi355x.inc).  Consecutive token counts with the same
+winner are merged into one ranged entry.
 """
 import argparse
 import os
@@ -97,7 +106,43 @@ def time_variant(torch, h, p, ops, Bs, spec, reps=10):
     return time_interleaved(torch, [g], reps)[0] / len(Bs)
 
 
-def sweep(workloads, out_path, reps, log=print, max_m=None):
+def capture_dynamic(torch, h, p, ops, Bs, X, spec):
+    """A HIP graph of lin_gemm_run_dynamic calls (rotating B) under `spec`."""
+    h.set_force(spec)
+    try:
+        C = torch.empty((p.M, p.N), dtype=torch.int16, device="cuda")
+
+        def call(i):
+            h.run_dynamic(X, Bs[i % len(Bs)], C, quant=p.quant, act=p.act, sb=ops["sb"],
+                          alpha=p.alpha, bias=ops["bias"], residual=ops["residual"])
+
+        call(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(len(Bs)):
+                call(i)
+    finally:
+        h.set_force(None)
+    return g
+
+
+def merge_ranges(entries):
+    """Consecutive token counts (same quant, N, K) with the same winner ->
+    one (quant, m_lo, m_hi, N, K, spec, [times]) entry."""
+    out = []
+    for q, M, N, K, spec, t in entries:
+        last = out[-1] if out else None
+        if last and last[0] == q and last[3] == N and last[4] == K and last[5] == spec \
+                and last[2] == M - 1:
+            out[-1] = (q, last[1], M, N, K, spec, last[6] + [t])
+        else:
+            out.append((q, M, M, N, K, spec, [t]))
+    return out
+
+
+def sweep(workloads, out_path, reps, log=print, max_m=None, all_m=False, dynamic=False,
+          emit_inc=None):
     import torch
     import synth
     import epilogue_scaled_gemm_amd as lg
@@ -121,7 +166,10 @@ def sweep(workloads, out_path, reps, log=print, max_m=None):
         del src, dst
     for cfg in workloads:
         c = synth.WORKLOADS[cfg]
-        for M in c["Ms"]:
+        ms = list(c["Ms"])
+        if all_m and min(ms) <= 32:
+            ms = sorted(set(ms) | set(range(1, 33)))
+        for M in ms:
             if max_m is not None and M > max_m:
                 continue
             p = synth.make(cfg, M)
@@ -157,16 +205,41 @@ def sweep(workloads, out_path, reps, log=print, max_m=None):
                     best = (t, spec)
             del caps
             log(f"BEST {c['name']} M={M}: {best[0] * 1e6:.2f} us  {best[1]}")
-            entries.append((p.quant, M, p.N, p.K, best[1], best[0]))
+            spec = best[1]
+            if dynamic and M <= 16 and spec.startswith("decode") and \
+                    p.quant in ("fp8_dynamic", "w8a8_int8", "block_fp8"):
+                X = torch.from_numpy(synth.activations16(M, p.K, seed=M).view(np.int16)).cuda()
+                try:
+                    gd = [capture_dynamic(torch, h, p, ops, Bs, X, spec),
+                          capture_dynamic(torch, h, p, ops, Bs, X, spec + " dq=1")]
+                    t0, t1 = (t / len(Bs) for t in time_interleaved(torch, gd, reps))
+                    log(f"DYNAMIC {c['name']} M={M}: separate kernel {t0 * 1e6:.2f} us, "
+                        f"prologue {t1 * 1e6:.2f} us")
+                    if t1 < 0.98 * t0:
+                        spec += " dq=1"
+                    del gd
+                except lg.LinGemmError as ex:
+                    log(f"  no prologue for {spec}: {ex}")
+            entries.append((p.quant, M, p.N, p.K, spec, best[0]))
             del Bs, ops
             torch.cuda.empty_cache()
     h.close()
+    merged = merge_ranges(entries)
+    measured = [f"{q:<12} {lo:<5} {hi:<5} {N:<6} {K:<6} {spec}   # "
+                + ", ".join(f"{t * 1e6:.2f}" for t in ts) + " us"
+                for q, lo, hi, N, K, spec, ts in merged]
+    if emit_inc:
+        with open(emit_inc, "w") as f:
+            f.write("// Measured entries of the built-in variant table, written by\n"
+                    "// epilogue_scaled_gemm_amd.sweep (graph replay over rotating weight\n"
+                    "// copies on an MI355X); microseconds per call in the comments.\n"
+                    "R\"TABLE(\n# quant        m_lo  m_hi  N      K      variant\n"
+                    + "\n".join(measured) + "\n)TABLE\"\n")
+        log(f"wrote {emit_inc}")
     lines = ["# Variant table for MI355X (gfx950), written by epilogue_scaled_gemm_amd.sweep.",
              "# <quant> <m_lo> <m_hi> <N> <K> <variant>   (first match wins; the",
              "# built-in defaults follow the measured entries)",
-             "# measured us per call in the trailing comment"]
-    for q, M, N, K, spec, t in entries:
-        lines.append(f"{q:<12} {M:<5} {M:<5} {N:<6} {K:<6} {spec}   # {t * 1e6:.2f} us")
+             "# measured us per call in the trailing comment"] + measured
     lines += ["*            1     32    *      *      decode swap=1 split=1 reduce=twopass waves=8 unroll=2 rows=16",
               "block_fp8    257   *     *      *      pp split=0 group=4",
               "block_fp8    33    *     *      *      tile bm=128 bn=128 wm=2 wn=2 group=4",
@@ -190,9 +263,14 @@ def main():
     ap.add_argument("--workloads", default="1,2,3,4,5")
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--max-m", type=int, default=None, help="only token counts up to this")
+    ap.add_argument("--all-m", action="store_true", help="every token count 1..32 (decode)")
+    ap.add_argument("--dynamic", action="store_true",
+                    help="choose the quantization prologue (dq=1) where it is faster")
+    ap.add_argument("--emit-inc", default=None, help="write the measured entries as C++ include")
     a = ap.parse_args()
     sweep([int(x) for x in a.workloads.split(",")], a.out, a.reps,
-          log=lambda s: print(s, flush=True), max_m=a.max_m)
+          log=lambda s: print(s, flush=True), max_m=a.max_m, all_m=a.all_m, dynamic=a.dynamic,
+          emit_inc=a.emit_inc)
 
 
 if __name__ == "__main__":
