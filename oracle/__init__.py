@@ -31,7 +31,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
-QUANT = {"bf16": 0, "fp16": 1, "fp8_dynamic": 2, "w8a8_int8": 3, "block_fp8": 4}
+QUANT = {"bf16": 0, "fp16": 1, "fp8_dynamic": 2, "w8a8_int8": 3, "block_fp8": 4, "mxfp4": 5}
 ACT = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3}
 
 _lib = None
@@ -53,6 +53,10 @@ def _load():
     lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
     lib.oracle_fp16_to_f64.restype = ctypes.c_double
     lib.oracle_fp16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_e2m1_to_f64.restype = ctypes.c_double
+    lib.oracle_e2m1_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e8m0_to_f64.restype = ctypes.c_double
+    lib.oracle_e8m0_to_f64.argtypes = [ctypes.c_uint8]
     lib.oracle_f64_to_bf16_rne.restype = ctypes.c_uint16
     lib.oracle_f64_to_bf16_rne.argtypes = [ctypes.c_double]
     lib.oracle_act.restype = ctypes.c_double
@@ -97,6 +101,14 @@ def fp16_to_f64(bits: int) -> float:
     return _load().oracle_fp16_to_f64(bits)
 
 
+def e2m1_to_f64(code: int) -> float:
+    return _load().oracle_e2m1_to_f64(code)
+
+
+def e8m0_to_f64(code: int) -> float:
+    return _load().oracle_e8m0_to_f64(code)
+
+
 def f64_to_bf16(x: float) -> int:
     return _load().oracle_f64_to_bf16_rne(x)
 
@@ -111,6 +123,9 @@ def num_threads() -> int:
 
 def _operands(quant, A, B, sa, sb, bias, residual):
     q = QUANT[quant]
+    if q == 5:  # bf16 activations, packed E2M1 weights, E8M0 weight scales
+        return q, _c(A, np.uint16), _c(B, np.uint8), None, _c(sb, np.uint8), \
+            _c(bias, np.uint16), _c(residual, np.uint16)
     code_t = np.uint16 if q in (0, 1) else (np.int8 if q == 3 else np.uint8)
     A = _c(A, code_t)
     B = _c(B, code_t)
@@ -129,13 +144,15 @@ def linear(quant, act_name, A, B, sa=None, sb=None, bias=None, residual=None, al
     """Reference result r[M,N] (fp64) and, for int8, the int32 accumulator.
 
     A: [M,K] codes, B: [N,K] codes (uint16 for bf16/fp16, uint8 for e4m3,
-    int8 for int8).  sa/sb fp32 per the quant mode's layout.  bias [N] and
+    int8 for int8; for mxfp4 [N,K/2] bytes of two E2M1 codes, low nibble
+    first).  sa/sb fp32 per the quant mode's layout (mxfp4: sb is E8M0
+    bytes [N,K/32], sa unused).  bias [N] and
     residual [M,N] are 16-bit float codes.  Returns (r, acc or None).
     """
     q, A, B, sa, sb, bias, residual = _operands(quant, A, B, sa, sb, bias, residual)
     M, K = A.shape
     N = B.shape[0]
-    assert B.shape[1] == K
+    assert B.shape[1] == (K // 2 if q == 5 else K)
     out = np.empty((M, N), dtype=np.float64)
     acc = np.zeros((M, N), dtype=np.int32) if q == 3 else None
     rc = _load().oracle_linear(_ptr(A), _ptr(B), _ptr(sa), _ptr(sb), float(alpha),

@@ -54,7 +54,8 @@
 
 /* Quant-mode and activation codes (the same numbering as the library's public
  * header; written out here independently). */
-enum { OQ_BF16 = 0, OQ_FP16 = 1, OQ_FP8_DYNAMIC = 2, OQ_W8A8_INT8 = 3, OQ_BLOCK_FP8 = 4 };
+enum { OQ_BF16 = 0, OQ_FP16 = 1, OQ_FP8_DYNAMIC = 2, OQ_W8A8_INT8 = 3, OQ_BLOCK_FP8 = 4,
+       OQ_MXFP4 = 5 };
 enum { OA_NONE = 0, OA_RELU = 1, OA_GELU_TANH = 2, OA_SILU = 3 };
 enum { O_OK = 0, O_BAD_ARG = -1, O_INT32_OVERFLOW = -2 };
 
@@ -70,6 +71,23 @@ double oracle_e4m3_to_f64(uint8_t code) {
     if (e == 0) v = ldexp((double)m / 8.0, -6);
     else v = ldexp(1.0 + (double)m / 8.0, e - 7);
     return s ? -v : v;
+}
+
+/* 4-bit weights (the MI355X-native counterpart of the INT4 / NVFP4 weight
+ * formats "helion-vllm-linear-backend" lists in its section "Зачем трогать
+ * линейные слои"; the pages define no 4-bit format, so the format is taken
+ * from the OCP Microscaling (MX) v1.0 specification, MXFP4):
+ * E2M1 element: s ee m; e == 0: (-1)^s * m/2 (0 or 0.5); otherwise
+ * (-1)^s * 2^(e-1) * (1 + m/2).  No infinity or NaN. */
+double oracle_e2m1_to_f64(uint8_t code) {
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+/* E8M0 shared scale of a block of 32 elements: 2^(e - 127); e == 255 is NaN. */
+double oracle_e8m0_to_f64(uint8_t code) {
+    return code == 255 ? NAN : ldexp(1.0, (int)code - 127);
 }
 
 /* bfloat16: the upper half of an IEEE binary32. */
@@ -187,9 +205,28 @@ static double dot_f(const olayer_t *L, int64_t m, int64_t n, int64_t k0, int64_t
 
 /* Steps (1)-(5) for one output element.  *acc_out receives the int32
  * accumulator in int8 mode. */
+/* MXFP4 weights: B holds two E2M1 codes per byte (k = 2j in the low nibble
+ * of byte j, k = 2j + 1 in the high nibble), row n at B + n*K/2; sb is
+ * reinterpreted as E8M0 bytes [N][K/32].  A is bf16.  The sum is exact in
+ * fp64 unless its terms span more than 53 bits of magnitude. */
+static double dot_mx(const olayer_t *L, int64_t m, int64_t n) {
+    const uint16_t *a = (const uint16_t *)L->A + m * L->K;
+    const uint8_t *b = (const uint8_t *)L->B + n * (L->K / 2);
+    const uint8_t *sc = (const uint8_t *)L->sb + n * (L->K / 32);
+    double s = 0.0;
+    for (int64_t k = 0; k < L->K; ++k) {
+        const uint8_t byte = b[k / 2];
+        const uint8_t code = (k & 1) ? (byte >> 4) : (byte & 15);
+        s += oracle_bf16_to_f64(a[k]) * oracle_e2m1_to_f64(code) * oracle_e8m0_to_f64(sc[k / 32]);
+    }
+    return s;
+}
+
 static int one(const olayer_t *L, int64_t m, int64_t n, double *r_out, int32_t *acc_out) {
     double y;
-    if (L->quant == OQ_W8A8_INT8) {
+    if (L->quant == OQ_MXFP4) {
+        y = dot_mx(L, m, n);
+    } else if (L->quant == OQ_W8A8_INT8) {
         int64_t s = dot_i8(L, m, n);
         if (s > INT32_MAX || s < INT32_MIN) return O_INT32_OVERFLOW;
         if (acc_out) *acc_out = (int32_t)s;
@@ -218,11 +255,12 @@ static int one(const olayer_t *L, int64_t m, int64_t n, double *r_out, int32_t *
 static int check(const olayer_t *L) {
     tables_init();
     if (L->M < 0 || L->N < 0 || L->K < 0) return O_BAD_ARG;
-    if (L->quant < OQ_BF16 || L->quant > OQ_BLOCK_FP8) return O_BAD_ARG;
+    if (L->quant < OQ_BF16 || L->quant > OQ_MXFP4) return O_BAD_ARG;
     if (L->act < OA_NONE || L->act > OA_SILU) return O_BAD_ARG;
     if ((L->quant == OQ_FP8_DYNAMIC || L->quant == OQ_W8A8_INT8 || L->quant == OQ_BLOCK_FP8) &&
         (!L->sa || !L->sb)) return O_BAD_ARG;
     if (L->quant == OQ_BLOCK_FP8 && (L->K % 128 != 0 || L->N % 128 != 0)) return O_BAD_ARG;
+    if (L->quant == OQ_MXFP4 && (!L->sb || L->K % 32 != 0)) return O_BAD_ARG;
     return O_OK;
 }
 

@@ -13,6 +13,7 @@ Workloads follow the five problem shapes the library is measured on:
   3  W8A8 int8 decode          A[M,4096]   B[24576,4096] per-token x per-channel, SiLU
   4  block-FP8 linear          A[M,12288]  B[4096,12288] 1x128 / 128x128 scales, residual
   5  prefill decoder block     A[4096,4096] B[4096,4096] bias, GELU(tanh)*0.5 + residual
+  6  MXFP4-weight decode       A[M,4096] bf16  B[6144,4096] 4-bit E2M1, E8M0 per 32, bias
 
 The (N, K) pairs of 2-4 stand in for the dense-LLM projection shapes that the
 vLLM linear-backend write-up tunes on (its Qwen3 weights and ShareGPT traffic
@@ -42,6 +43,8 @@ WORKLOADS = {
             Ms=(1, 8, 32, 512, 2048), bias=False, residual=True, alpha=1.0, dist="normal"),
     5: dict(name="prefill_bf16_fused", quant="bf16", act="gelu_tanh", N=4096, K=4096,
             Ms=(4096,), bias=True, residual=True, alpha=0.5, dist="normal"),
+    6: dict(name="mxfp4_decode", quant="mxfp4", act="none", N=6144, K=4096,
+            Ms=(1, 2, 4, 8, 16, 24, 32), bias=True, residual=False, alpha=1.0, dist="normal"),
 }
 
 
@@ -128,6 +131,34 @@ def quant_blocks_weight(x: np.ndarray):
     return to_e4m3_codes(q.reshape(N, K)), s
 
 
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+def quant_mxfp4(x: np.ndarray):
+    """OCP MX quantisation of weights [N,K] to packed E2M1 codes [N,K/2]
+    (low nibble first) and E8M0 scales [N,K/32]: per 32 values, the shared
+    exponent floor(log2(max|x|)) - 2 (the largest E2M1 exponent), then each
+    value rounded to the nearest E2M1 value (ties to the even code),
+    saturating at +-6; an all-zero block gets exponent 0."""
+    N, K = x.shape
+    xb = x.astype(np.float64).reshape(N, K // 32, 32)
+    amax = np.abs(xb).max(axis=2)
+    e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, 0)
+    e = np.clip(e, -126, 127).astype(np.int64)
+    v = np.abs(xb) / np.ldexp(1.0, e)[:, :, None]
+    # nearest E2M1 magnitude, ties to the even code (codes 0..7 by magnitude)
+    d = np.abs(v[..., None] - E2M1_VALUES)
+    best = np.argmin(d, axis=-1)
+    dmin = d.min(axis=-1)
+    tie = (np.sum(np.isclose(d, dmin[..., None], rtol=0, atol=0), axis=-1) > 1) & (best % 2 == 1)
+    code = np.where(tie, best + 1, best)
+    code = np.where(v >= 6.0, 7, code).astype(np.uint8)
+    code |= np.where(xb < 0, 8, 0).astype(np.uint8)
+    code = code.reshape(N, K)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8)
+
+
 def encode(quant: str, x: np.ndarray, side: str):
     """fp32 values -> (codes, scales) for one operand side ('a' or 'b')."""
     if quant == "bf16":
@@ -140,6 +171,8 @@ def encode(quant: str, x: np.ndarray, side: str):
         return quant_rows(x, "int8")
     if quant == "block_fp8":
         return quant_blocks_act(x) if side == "a" else quant_blocks_weight(x)
+    if quant == "mxfp4":
+        return (to_bf16_bits(x), None) if side == "a" else quant_mxfp4(x)
     raise ValueError(quant)
 
 
@@ -222,6 +255,8 @@ def algorithmic_bytes(quant: str, M: int, N: int, K: int, bias: bool, residual: 
     residual and the one output write."""
     e = 2 if quant in ("bf16", "fp16") else 1
     b = M * K * e + N * K * e
+    if quant == "mxfp4":  # bf16 activations, 4-bit weights, one E8M0 byte per 32
+        b = 2 * M * K + N * K // 2 + N * K // 32
     if quant in ("fp8_dynamic", "w8a8_int8"):
         b += 4 * M + 4 * N
     elif quant == "block_fp8":
