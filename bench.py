@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12                                     # bytes/s
 MFMA_PEAK = {"bf16": 2.5e15, "fp16": 2.5e15, "fp8_dynamic": 5.0e15, "block_fp8": 5.0e15,
-             "w8a8_int8": 5.0e15}                     # dense, per operand dtype
+             "w8a8_int8": 5.0e15, "mxfp4": 10.1e15}   # dense, per operand dtype
 RIDGE = {q: MFMA_PEAK[q] / HBM_PEAK for q in MFMA_PEAK}
 HEAD_CFG = 2
 NCOPY_TARGET_BYTES = 384 << 20                        # rotation footprint > 256 MB MALL
@@ -192,7 +192,7 @@ def shape_row(name, quant, M, N, K, t, nbytes, flops, variant, kernel_calls=1):
 def per_shape_table(torch, h, reps):
     import synth
     rows = []
-    for cfg in (1, 2, 3, 4, 5):
+    for cfg in (1, 2, 3, 4, 5, 6):
         c = synth.WORKLOADS[cfg]
         wl = Workload(torch, cfg, c["Ms"])
         for M in c["Ms"]:

@@ -25,7 +25,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblingemm.so")
 
-QUANT = {"bf16": 0, "fp16": 1, "fp8_dynamic": 2, "w8a8_int8": 3, "block_fp8": 4}
+QUANT = {"bf16": 0, "fp16": 1, "fp8_dynamic": 2, "w8a8_int8": 3, "block_fp8": 4, "mxfp4": 5}
 ACT = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3, "raw_acc": 255}
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "HIP error",
           -4: "out of memory", -5: "config error"}
@@ -133,8 +133,9 @@ class Handle:
         M = A.shape[0] if M is None else M
         K = A.shape[1] if K is None else K
         N = B.shape[0] if N is None else N
-        if B.shape[1] != K:
-            raise ValueError(f"inner dimensions differ: A has K={K}, B has {B.shape[1]}")
+        kb = K // 2 if quant in ("mxfp4", 5) else K  # 4-bit weights: two codes per byte
+        if B.shape[1] != kb:
+            raise ValueError(f"inner dimensions differ: A has K={K}, B rows have {B.shape[1]}")
         sc = _Scales(None if sa is None else _ptr(sa).value,
                      None if sb is None else _ptr(sb).value, float(alpha))
         rc = self._lib.lin_gemm_run(self._h, _ptr(A), _ptr(B), ctypes.byref(sc), _ptr(bias),

@@ -46,7 +46,10 @@ int hip_fail(lin_gemm_t h, hipError_t e, const char* what) {
   return fail(h, LIN_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-int esize(int quant) { return (quant == LIN_Q_BF16 || quant == LIN_Q_FP16) ? 2 : 1; }
+// Bytes per element of A (bf16 activations in the MXFP4 mode).
+int esize(int quant) {
+  return (quant == LIN_Q_BF16 || quant == LIN_Q_FP16 || quant == LIN_Q_MXFP4) ? 2 : 1;
+}
 
 int qkind(int quant) {
   switch (quant) {
@@ -55,8 +58,14 @@ int qkind(int quant) {
     case LIN_Q_FP8_DYNAMIC: return lg::QK_FP8;
     case LIN_Q_W8A8_INT8: return lg::QK_I8;
     case LIN_Q_BLOCK_FP8: return lg::QK_FP8_BLOCK;
+    case LIN_Q_MXFP4: return lg::QK_MXFP4;
   }
   return -1;
+}
+
+// Bytes of one row of B (the weight): K elements, or K/2 for 4-bit codes.
+int64_t b_row_bytes(int quant, int64_t K) {
+  return quant == LIN_Q_MXFP4 ? K / 2 : K * esize(quant);
 }
 
 bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
@@ -64,7 +73,7 @@ bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 1
 // Shape / pointer checks shared by the fused and unfused entry points.
 int check_shape(lin_gemm_t h, int quant, int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0) return fail(h, LIN_ERR_INVALID_ARG, "negative size");
-  if (quant < LIN_Q_BF16 || quant > LIN_Q_BLOCK_FP8)
+  if (quant < LIN_Q_BF16 || quant > LIN_Q_MXFP4)
     return fail(h, LIN_ERR_INVALID_ARG, "unknown quant mode " + std::to_string(quant));
   if (M == 0) return LIN_OK;
   if (N < 1 || K < 1) return fail(h, LIN_ERR_UNSUPPORTED, "N and K must be >= 1");
@@ -73,6 +82,8 @@ int check_shape(lin_gemm_t h, int quant, int64_t M, int64_t N, int64_t K) {
                                         "(K % 8 for bf16/fp16, K % 16 for e4m3/int8)");
   if (quant == LIN_Q_BLOCK_FP8 && (K % 128 != 0 || N % 128 != 0))
     return fail(h, LIN_ERR_UNSUPPORTED, "block FP8 needs K % 128 == 0 and N % 128 == 0");
+  if (quant == LIN_Q_MXFP4 && (K % 256 != 0 || M > 32))
+    return fail(h, LIN_ERR_UNSUPPORTED, "MXFP4 weights need K % 256 == 0 and M <= 32");
   if (quant == LIN_Q_W8A8_INT8 && K > 131071)
     return fail(h, LIN_ERR_UNSUPPORTED, "int8 needs K <= 131071 (int32 accumulator range)");
   if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31 || K > (int64_t)1 << 31)
@@ -92,6 +103,12 @@ int select_variant(lin_gemm_t h, int quant, int64_t M, int64_t N, int64_t K, lg:
     if (M <= 32) { d.kind = lg::V_DECODE; }
     else { d.kind = lg::V_TILE; d.bm = 128; d.bn = 128; d.wm = 2; d.wn = 2; }
     *v = d;
+  }
+  if (quant == LIN_Q_MXFP4 && !lg::decode_mx_supported(*v)) {
+    if (h->forced) return fail(h, LIN_ERR_UNSUPPORTED, "variant not compiled for MXFP4 weights");
+    *v = lg::Variant();
+    v->kind = lg::V_DECODE;
+    v->waves = 8; v->unroll = 2; v->rows = 16; v->split = 1;
   }
   if (v->kind == lg::V_DECODE && M > 32) {
     if (h->forced) return fail(h, LIN_ERR_UNSUPPORTED, "decode variants need M <= 32");
@@ -274,7 +291,7 @@ int lin_gemm_describe(lin_gemm_t h, int quant_mode, int64_t M, int64_t N, int64_
   rc = select_variant(h, quant_mode, M, N, K, &v);
   if (rc != LIN_OK) return rc;
   lg::Call c{};
-  c.M = M; c.N = N; c.K = K; c.KB = K * esize(quant_mode);
+  c.M = M; c.N = N; c.K = K; c.KB = b_row_bytes(quant_mode, K);
   c.qk = qkind(quant_mode);
   std::string s = lg::format_variant(v, resolve_split(v, c));
   std::snprintf(buf, (size_t)buflen, "%s", s.c_str());
@@ -291,9 +308,11 @@ int lin_gemm_run(lin_gemm_t h, const void* A, const void* B, const lin_scales_t*
   if (!A || !B || !C) return fail(h, LIN_ERR_INVALID_ARG, "A, B and C must be non-null");
   if (!(activation >= LIN_ACT_NONE && activation <= LIN_ACT_SILU) && activation != LIN_ACT_RAW_ACC)
     return fail(h, LIN_ERR_INVALID_ARG, "unknown activation " + std::to_string(activation));
-  const bool quantised = quant_mode >= LIN_Q_FP8_DYNAMIC;
+  const bool quantised = quant_mode >= LIN_Q_FP8_DYNAMIC && quant_mode != LIN_Q_MXFP4;
   if (quantised && (!scales || !scales->a || !scales->b))
     return fail(h, LIN_ERR_INVALID_ARG, "quantised modes need scales->a and scales->b");
+  if (quant_mode == LIN_Q_MXFP4 && (!scales || !scales->b))
+    return fail(h, LIN_ERR_INVALID_ARG, "MXFP4 weights need scales->b (E8M0 bytes)");
   if (misaligned(A) || misaligned(B) || misaligned(C) || misaligned(bias) || misaligned(residual))
     return fail(h, LIN_ERR_UNSUPPORTED, "A, B, C, bias and residual must be 16-byte aligned");
   if (scales && (misaligned(scales->a) || misaligned(scales->b)))
@@ -302,7 +321,7 @@ int lin_gemm_run(lin_gemm_t h, const void* A, const void* B, const lin_scales_t*
   hipStream_t s = (hipStream_t)stream;
   lg::Call c{};
   c.A = A; c.B = B; c.M = M; c.N = N; c.K = K;
-  c.KB = K * esize(quant_mode);
+  c.KB = b_row_bytes(quant_mode, K);
   c.qk = qkind(quant_mode);
   c.epi = make_epi(scales, bias, residual, C, M, N, quant_mode, activation);
 

@@ -22,7 +22,8 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
 
 // Element kinds of the operands.
-enum QKind : int { QK_BF16 = 0, QK_FP16 = 1, QK_FP8 = 2, QK_I8 = 3, QK_FP8_BLOCK = 4 };
+enum QKind : int { QK_BF16 = 0, QK_FP16 = 1, QK_FP8 = 2, QK_I8 = 3, QK_FP8_BLOCK = 4,
+                   QK_MXFP4 = 5 };
 // Activation codes (1 = ReLU and 2 = GELU-tanh keep the listing's numbering).
 enum ActCode : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2, ACT_SILU = 3 };
 
@@ -32,6 +33,7 @@ template <> struct QTraits<QK_FP16> { typedef float Acc; static constexpr bool o
 template <> struct QTraits<QK_FP8> { typedef float Acc; static constexpr bool out_f16 = false; };
 template <> struct QTraits<QK_I8> { typedef int Acc; static constexpr bool out_f16 = false; };
 template <> struct QTraits<QK_FP8_BLOCK> { typedef float Acc; static constexpr bool out_f16 = false; };
+template <> struct QTraits<QK_MXFP4> { typedef float Acc; static constexpr bool out_f16 = false; };
 
 // ----------------------------------------------------------- MFMA wrappers
 // A 16 x 16 output tile per wave.  Every K step covers 128 bytes of each
@@ -102,6 +104,25 @@ template <> struct Mfma<QK_FP8> {
   }
 };
 template <> struct Mfma<QK_FP8_BLOCK> : Mfma<QK_FP8> {};
+// MXFP4 weights meet bf16 activations in the bf16 MFMA; the decode kernel
+// widens each 4-bit weight with its block scale itself (mx_widen8).
+template <> struct Mfma<QK_MXFP4> : Mfma<QK_BF16> {};
+
+// Eight E2M1 weights (one dword, low nibble first) times their E8M0 block
+// scale, as eight bf16 values (an MFMA operand).  The product of an E2M1
+// value (at most two significant bits) and a power of two is exact in bf16.
+__device__ inline i32x4 mx_widen8(uint32_t w, float scale) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  i32x4 out;
+  out[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  out[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  out[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  out[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return out;
+}
+// E8M0 code -> 2^(e - 127) as fp32 (codes 1..254; 0 and 255 are outside the
+// supported domain).
+__device__ inline float e8m0_to_f32(uint32_t e) { return __uint_as_float(e << 23); }
 
 __device__ inline i32x4 lo16(const i32x8& v) { return i32x4{v[0], v[1], v[2], v[3]}; }
 __device__ inline i32x4 hi16(const i32x8& v) { return i32x4{v[4], v[5], v[6], v[7]}; }

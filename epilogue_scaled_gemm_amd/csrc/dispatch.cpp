@@ -8,11 +8,11 @@ namespace lg {
 
 namespace {
 
-const char* kQuantNames[] = {"bf16", "fp16", "fp8_dynamic", "w8a8_int8", "block_fp8"};
+const char* kQuantNames[] = {"bf16", "fp16", "fp8_dynamic", "w8a8_int8", "block_fp8", "mxfp4"};
 
 int quant_of(const std::string& s) {
   if (s == "*") return -1;
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 6; ++i)
     if (s == kQuantNames[i]) return i;
   return -2;
 }

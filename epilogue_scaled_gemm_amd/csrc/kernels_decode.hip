@@ -36,6 +36,8 @@
 //    it; exact for int32, order-dependent rounding for fp32) or twopass
 //    (partials, then splitk_reduce sums them in slice order).  The nonlinear
 //    epilogue always runs on the complete sum.
+#include <type_traits>
+
 #include "launch.hpp"
 
 namespace lg {
@@ -176,6 +178,13 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
   using AccT = typename QTraits<QK>::Acc;
   constexpr bool F16 = QTraits<QK>::out_f16;
   constexpr bool BLOCK = (QK == QK_FP8_BLOCK);
+  // MXFP4 weights: 4-bit codes (KB = K/2 bytes per weight row) with an E8M0
+  // scale per 32 K values, against bf16 activations (XR = 4 activation bytes
+  // per weight byte).  A step is 128 weight bytes = 256 K values; a lane's
+  // 32 bytes are two 32-value scale blocks.  Swap only; K % 256 == 0.
+  constexpr bool MX = (QK == QK_MXFP4);
+  constexpr int XR = MX ? 4 : 1;
+  static_assert(!MX || (SWAP && !DQ), "MXFP4 weights use the swap orientation");
   constexpr int NS = SWAP ? 1 : 4;    // block scales per token tile per lane
   constexpr int NTILE = RT * NTT;     // 16x16 output tiles per workgroup
   __shared__ AccT red[W][NTILE * 4][64];
@@ -221,7 +230,16 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
   }
   const uint8_t* xp[NTT];
 #pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) xp[tt] = A + min((int64_t)(tt * 16 + l16), M - 1) * KB + g * 32;
+  for (int tt = 0; tt < NTT; ++tt)
+    xp[tt] = A + min((int64_t)(tt * 16 + l16), M - 1) * KB * XR + g * 32 * XR;
+  // MXFP4: E8M0 scale bytes [N][KB/16]; a lane's two blocks of a step are
+  // bytes st*8 + 2g and st*8 + 2g + 1 of its row.
+  const uint8_t* msp[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int64_t row = n0 + rt * 16 + l16;
+    msp[rt] = MX ? (const uint8_t*)e.sb + (row < nend ? row : n0) * (KB / 16) + 2 * g : nullptr;
+  }
   // With DQ: the codes in LDS (row stride KB + 16) and the scales after them
   // (sal[M] per token, or sal[M][KB / 128] per block).
   const int64_t LS = KB + 16;
@@ -246,8 +264,12 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
       }
   }
 
-  i32x8 wb[U][RT], xb[U][NTT];
+  struct XMX { i32x4 v[8]; };  // 64 bf16 activations per lane per step (MXFP4)
+  using XB = typename std::conditional<MX, XMX, i32x8>::type;
+  i32x8 wb[U][RT];
+  XB xb[U][NTT];
   float sc[U][NTT][NS];
+  uint32_t msc[U][RT];
   // Issue a whole batch of U steps' loads (straight-line, always in bounds),
   // then consume it.  A wave's steps usually fit one batch, so every load of
   // the kernel is in flight at once and each MFMA waits only for its own
@@ -274,8 +296,18 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
         for (int rt = 0; rt < RT; ++rt)
           wb[u][rt] = cat(ld16(wp[rt] + c0, ok0 && wrow[rt]), ld16(wp[rt] + c1, ok1 && wrow[rt]));
       }
+      if constexpr (MX) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) msc[u][rt] = *(const uint16_t*)(msp[rt] + (int64_t)st * 8);
+      }
       if (part == 1) continue;
-      if constexpr (DQ) {
+      if constexpr (MX) {
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            xb[u][tt].v[j] = ld16(xp[tt] + 4 * c0 + 16 * j, j < 4 ? ok0 : ok1);
+      } else if constexpr (DQ) {
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt)
           xb[u][tt] = cat(ld16(xl[tt] + c0, ok0), ld16(xl[tt] + c1, ok1));
@@ -305,29 +337,44 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
     for (int tt = 0; tt < NTT; ++tt) acc[rt][tt] = C{0, 0, 0, 0};
 
   auto compute_batch = [&]() {
+    if constexpr (MX) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      typename MF::Frag x0[NTT], x1[NTT];
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
-        x0[tt] = MF::prep(lo16(xb[u][tt]));
-        x1[tt] = MF::prep(hi16(xb[u][tt]));
-      }
+        for (int rt = 0; rt < RT; ++rt) {
+          const float s0 = e8m0_to_f32(msc[u][rt] & 0xFFu), s1 = e8m0_to_f32(msc[u][rt] >> 8);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const typename MF::Frag w0 = MF::prep(lo16(wb[u][rt])), w1 = MF::prep(hi16(wb[u][rt]));
+          for (int j = 0; j < 8; ++j) {
+            const i32x4 w = mx_widen8((uint32_t)wb[u][rt][j], j < 4 ? s0 : s1);
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) acc[rt][tt] = MF::mma(w, xb[u][tt].v[j], acc[rt][tt]);
+          }
+        }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        typename MF::Frag x0[NTT], x1[NTT];
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
-          if constexpr (BLOCK) {
-            // One step is one 128-wide K block: scale its exact partial sum.
-            C p = SWAP ? MF::mma(w0, x0[tt], C{0, 0, 0, 0}) : MF::mma(x0[tt], w0, C{0, 0, 0, 0});
-            p = SWAP ? MF::mma(w1, x1[tt], p) : MF::mma(x1[tt], w1, p);
+          x0[tt] = MF::prep(lo16(xb[u][tt]));
+          x1[tt] = MF::prep(hi16(xb[u][tt]));
+        }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[rt][tt][r] += sc[u][tt][SWAP ? 0 : r] * p[r];
-          } else {
-            C a = acc[rt][tt];
-            a = SWAP ? MF::mma(w0, x0[tt], a) : MF::mma(x0[tt], w0, a);
-            acc[rt][tt] = SWAP ? MF::mma(w1, x1[tt], a) : MF::mma(x1[tt], w1, a);
+        for (int rt = 0; rt < RT; ++rt) {
+          const typename MF::Frag w0 = MF::prep(lo16(wb[u][rt])), w1 = MF::prep(hi16(wb[u][rt]));
+#pragma unroll
+          for (int tt = 0; tt < NTT; ++tt) {
+            if constexpr (BLOCK) {
+              // One step is one 128-wide K block: scale its exact partial sum.
+              C p = SWAP ? MF::mma(w0, x0[tt], C{0, 0, 0, 0}) : MF::mma(x0[tt], w0, C{0, 0, 0, 0});
+              p = SWAP ? MF::mma(w1, x1[tt], p) : MF::mma(x1[tt], w1, p);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[rt][tt][r] += sc[u][tt][SWAP ? 0 : r] * p[r];
+            } else {
+              C a = acc[rt][tt];
+              a = SWAP ? MF::mma(w0, x0[tt], a) : MF::mma(x0[tt], w0, a);
+              acc[rt][tt] = SWAP ? MF::mma(w1, x1[tt], a) : MF::mma(x1[tt], w1, a);
+            }
           }
         }
       }
@@ -678,6 +725,30 @@ hipError_t launch_splitk_reduce(int qk, const void* ws, int split, const Epi& e,
   return hipGetLastError();
 }
 
+// MXFP4-weight variants (swap, up to two steps per batch: each step holds 64
+// bf16 activations per lane and token tile in registers).
+#define LG_DECODE_MX(X)                                                                \
+  X(8, 1, 1) X(8, 2, 1) X(16, 1, 1) X(12, 1, 1) X(8, 1, 2) X(4, 2, 2) X(8, 2, 2) X(4, 1, 4) \
+  X(8, 1, 4)
+
+bool decode_mx_supported(const Variant& v) {
+  if (v.kind != V_DECODE || v.swap != 1) return false;
+#define LG_MX_HAS(w, u, rt) if (v.waves == w && v.unroll == u && tiles_for(v.rows) == rt) return true;
+  LG_DECODE_MX(LG_MX_HAS)
+#undef LG_MX_HAS
+  return false;
+}
+
+template <int NTT>
+hipError_t launch_mx(const Variant& v, const Call& c, int split, hipStream_t s) {
+#define LG_MX_TRY(w, u, rt)                                                          \
+  if (v.swap == 1 && v.waves == w && v.unroll == u && tiles_for(v.rows) == rt)      \
+    return launch_d<QK_MXFP4, NTT, true, w, u, rt>(v, c, split, s);
+  LG_DECODE_MX(LG_MX_TRY)
+#undef LG_MX_TRY
+  return hipErrorInvalidValue;
+}
+
 bool decode_dq_supported(const Variant& v, const Call& c, int split) {
   if (v.kind != V_DECODE || v.swap != 1 || split != 1 || c.M < 1 || c.M > 16) return false;
   const void* fn;
@@ -705,6 +776,7 @@ hipError_t launch_decode(const Variant& v, const Call& c, int split, hipStream_t
     case QK_FP8: return launch_q<QK_FP8>(v, c, split, s);
     case QK_I8: return launch_q<QK_I8>(v, c, split, s);
     case QK_FP8_BLOCK: return launch_q<QK_FP8_BLOCK>(v, c, split, s);
+    case QK_MXFP4: return c.M <= 16 ? launch_mx<1>(v, c, split, s) : launch_mx<2>(v, c, split, s);
   }
   return hipErrorInvalidValue;
 }

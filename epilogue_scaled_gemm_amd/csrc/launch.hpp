@@ -64,6 +64,9 @@ hipError_t launch_decode(const Variant& v, const Call& c, int split, hipStream_t
 // Supported for swap, split 1, M <= 16, e4m3 / int8 / block e4m3, the
 // variants the library compiles with it, and LDS within the device limit.
 bool decode_dq_supported(const Variant& v, const Call& c, int split);
+// Whether the decode variant is compiled for MXFP4 weights (swap, waves /
+// unroll / tiles from a short list).
+bool decode_mx_supported(const Variant& v);
 hipError_t launch_decode_dq(const Variant& v, const Call& c, hipStream_t s);
 // Second pass of a two-pass split-K reduction: sums the fp32 / int32 slices
 // [split][M][N] in slice order and applies the epilogue.

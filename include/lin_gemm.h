@@ -40,6 +40,16 @@
  *   scales->a  fp32 [M] (FP8 dynamic, int8) or [M][K/128] (block FP8)
  *   scales->b  fp32 [N] (FP8 dynamic, int8) or [N/128][K/128] (block FP8)
  *
+ * LIN_Q_MXFP4 (4-bit weights; the pages list INT4 / NVFP4 weight formats in
+ * "helion-vllm-linear-backend", section "Зачем трогать линейные слои", and
+ * define none, so the gfx950-native OCP MX v1.0 MXFP4 format is used): A is
+ * bf16 [M][K]; B is [N][K/2] bytes, two E2M1 codes per byte, the even K
+ * index in the low nibble; scales->b points to E8M0 bytes [N][K/32] (one
+ * power-of-two scale 2^(e-127) per 32 consecutive K values of a row, codes
+ * 1..254) and scales->a is unused.  Decode shapes only (M <= 32), K % 256 ==
+ * 0.  C = act(sum_k A[m,k] * e2m1(B[n,k]) * 2^(e[n,k/32]-127) + bias) *
+ * alpha + residual, in bf16.
+ *
  * Streams and errors.  lin_gemm_run enqueues on `stream` (a hipStream_t;
  * NULL = the null stream) and returns without waiting.  The status it
  * returns covers argument checks and launch errors only; a fault inside a
@@ -72,7 +82,8 @@ enum lin_quant {
     LIN_Q_FP16 = 1,
     LIN_Q_FP8_DYNAMIC = 2, /* e4m3 A, B; sa per token [M], sb per channel [N] */
     LIN_Q_W8A8_INT8 = 3,   /* int8 A, B; same scaling; int32 accumulator     */
-    LIN_Q_BLOCK_FP8 = 4    /* e4m3; sa [M][K/128], sb [N/128][K/128]         */
+    LIN_Q_BLOCK_FP8 = 4,   /* e4m3; sa [M][K/128], sb [N/128][K/128]         */
+    LIN_Q_MXFP4 = 5        /* bf16 A; 4-bit B with E8M0 block scales (below) */
 };
 
 /* Activations.  1 and 2 keep the codes of the epilogue listing. */

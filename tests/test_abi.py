@@ -205,3 +205,22 @@ def test_run_dynamic_shape_errors(cpu_handle):
                                     4, 16, 64, 2, 0, None) == INVALID
     assert lib.lin_gemm_run_dynamic(cpu_handle._h, FAKE, 0, FAKE, FAKE, 1.0, None, None, FAKE,
                                     0, 16, 64, 2, 0, None) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(quant=5, K=640, scales=(None, FAKE, 1.0)), UNSUPPORTED),   # K % 256
+    (dict(quant=5, M=33, K=512, scales=(None, FAKE, 1.0)), UNSUPPORTED),
+    (dict(quant=5, K=512, scales=(None, None, 1.0)), INVALID),       # no E8M0 scales
+    (dict(quant=5, M=0, K=512, scales=(None, FAKE, 1.0)), OK),
+])
+def test_mxfp4_argument_errors(cpu_handle, kw, status):
+    assert _raw_run(cpu_handle, **kw) == status
+
+
+def test_mxfp4_describe(cpu_handle):
+    v = cpu_handle.describe("mxfp4", 8, 6144, 4096)
+    assert v.startswith("decode swap=1")
+    cpu_handle.set_force("decode swap=1 split=1 reduce=twopass waves=4 unroll=4 rows=16")
+    with pytest.raises(lg.LinGemmError):
+        cpu_handle.describe("mxfp4", 8, 6144, 4096)        # not compiled for MXFP4
+    cpu_handle.set_force(None)
