@@ -410,13 +410,15 @@ def main():
     # template arguments are quant kind (2 = e4m3), token tiles (one 16-token
     # tile up to M = 16, two up to 32), swap-AB, waves, unroll, 16-row weight
     # tiles per workgroup (1 up to 16 rows, 2 up to 32, else 4) and the
-    # quantization prologue (false: the headline feeds e4m3 activations).
+    # activation mode (0: every lane loads its e4m3 activations itself; 2:
+    # staged through LDS, "xs=1" in the variant).
     def kernel_name(M):
         v = dict(kv.split("=") for kv in h.describe(wl.quant, M, wl.N, wl.K).split()[1:])
         rows = int(v["rows"])
         rt = 1 if rows <= 16 else (2 if rows <= 32 else 4)
+        am = 2 if v.get("xs") == "1" else 0
         return (f"decode_kernel<2, {1 if M <= 16 else 2}, {'true' if v['swap'] == '1' else 'false'}"
-                f", {v['waves']}, {v['unroll']}, {rt}, false>")
+                f", {v['waves']}, {v['unroll']}, {rt}, {am}>")
     groups = {}
     for M in Ms:
         groups.setdefault(kernel_name(M), []).append(M)

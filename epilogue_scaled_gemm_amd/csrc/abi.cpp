@@ -293,6 +293,8 @@ int lin_gemm_describe(lin_gemm_t h, int quant_mode, int64_t M, int64_t N, int64_
   lg::Call c{};
   c.M = M; c.N = N; c.K = K; c.KB = b_row_bytes(quant_mode, K);
   c.qk = qkind(quant_mode);
+  // Report staged activations only where lin_gemm_run would use them.
+  if (v.xs && !lg::decode_xs_supported(v, c)) v.xs = 0;
   std::string s = lg::format_variant(v, resolve_split(v, c));
   std::snprintf(buf, (size_t)buflen, "%s", s.c_str());
   return LIN_OK;
@@ -343,7 +345,8 @@ int lin_gemm_run(lin_gemm_t h, const void* A, const void* B, const lin_scales_t*
     if (rc != LIN_OK) return rc;
     c.ws = h->ws;
     c.counters = h->counters;
-    e = lg::launch_decode(v, c, split, s);
+    e = v.xs && lg::decode_xs_supported(v, c) ? lg::launch_decode_xs(v, c, split, s)
+                                               : lg::launch_decode(v, c, split, s);
   }
   if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
   if (std::getenv("LIN_GEMM_LOG")) {

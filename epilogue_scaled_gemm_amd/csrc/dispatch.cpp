@@ -73,6 +73,7 @@ bool parse_variant(const std::string& spec, Variant* out, std::string* err) {
     else if (k == "unroll") v.unroll = xi;
     else if (k == "rows") v.rows = xi;
     else if (k == "dq") v.dq = xi ? 1 : 0;
+    else if (k == "xs") v.xs = xi ? 1 : 0;
     else { *err = "unknown key '" + k + "'"; return false; }
   }
   if (v.kind == V_TILE && !tile_supported(0, v.bm, v.bn, v.wm, v.wn)) {
@@ -108,6 +109,7 @@ std::string format_variant(const Variant& v, int split) {
     os << "decode swap=" << v.swap << " split=" << split << " reduce=" << reduce_name(v.reduce)
        << " waves=" << v.waves << " unroll=" << v.unroll << " rows=" << v.rows;
     if (v.dq) os << " dq=1";
+    if (v.xs) os << " xs=1";
   }
   return os.str();
 }

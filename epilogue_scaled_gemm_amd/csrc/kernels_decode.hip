@@ -71,7 +71,19 @@ __device__ inline i32x8 cat(i32x4 a, i32x4 b) {
 // the operands in the owning waves instead.
 constexpr bool op_wave(bool swap, int w) { return swap && w >= 8 && w < 16; }
 
-// DQ: A holds bf16 activations X[M][K] instead of codes, and the kernel
+// Activation modes (the kernel's last template argument AM):
+//  AM_GLOBAL  every lane loads its activation fragments from global memory.
+//  AM_STAGE   per step, a wave copies the M tokens' activation bytes it needs
+//             into its own slice of LDS with direct-to-LDS buffer loads (one
+//             16-byte chunk per lane, only the lanes that hold distinct data
+//             in range; one load covers 1 KiB), and the lanes read their
+//             fragments from there.  The lanes of a token tile share tokens
+//             (16 lanes per token at M = 1), so this replaces up to 16
+//             redundant global loads per distinct chunk by LDS broadcasts.
+//             Swap, one token tile.
+//  AM_QUANT   the quantization prologue below.
+//
+// AM_QUANT: A holds bf16 activations X[M][K] instead of codes, and the kernel
 // quantizes them itself in a prologue (swap, one token tile, split 1): the
 // whole workgroup reads its tokens' rows once, takes each group's maximum
 // (per token, or per 1x128 block), and writes the codes to LDS
@@ -79,6 +91,8 @@ constexpr bool op_wave(bool swap, int w) { return swap && w >= 8 && w < 16; }
 // the first weight batch is already in flight.  The K loop then reads its
 // activation fragments from LDS, and the epilogue takes the per-token scale
 // from there.  Codes and scales are those of lin_gemm_quantize.
+enum : int { AM_GLOBAL = 0, AM_QUANT = 1, AM_STAGE = 2 };
+typedef __attribute__((address_space(3))) void lds_void;
 constexpr int DQ_CHUNKS = 4;  // 16-byte activation chunks per thread kept in registers
 
 // The quantization prologue, run by every thread of the workgroup.  X[M][K]
@@ -168,7 +182,7 @@ __device__ inline void quant_prologue(const uint16_t* __restrict__ X, int64_t M,
   __syncthreads();
 }
 
-template <int QK, int NTT, bool SWAP, int W, int U, int RT, bool DQ>
+template <int QK, int NTT, bool SWAP, int W, int U, int RT, int AM>
 __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int64_t M, int64_t N,
     int64_t KB, int rpw, int split, int steps_per_split, int reduce, Epi e,
@@ -184,7 +198,10 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
   // 32 bytes are two 32-value scale blocks.  Swap only; K % 256 == 0.
   constexpr bool MX = (QK == QK_MXFP4);
   constexpr int XR = MX ? 4 : 1;
+  constexpr bool DQ = AM == AM_QUANT;
+  constexpr bool XS = AM == AM_STAGE;
   static_assert(!MX || (SWAP && !DQ), "MXFP4 weights use the swap orientation");
+  static_assert(!XS || (SWAP && NTT == 1), "staged activations are for swap, one token tile");
   constexpr int NS = SWAP ? 1 : 4;    // block scales per token tile per lane
   constexpr int NTILE = RT * NTT;     // 16x16 output tiles per workgroup
   __shared__ AccT red[W][NTILE * 4][64];
@@ -247,6 +264,17 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
   const uint8_t* xl[NTT];
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) xl[tt] = dq_lds + min((int64_t)(tt * 16 + l16), M - 1) * LS + g * 32;
+  // With AM_STAGE: this wave's LDS slice holds, per batch step u, the M
+  // tokens' activation bytes of the step (XSB bytes each, token-major), in
+  // XSL bytes: whole KiB, since every direct-to-LDS load writes 64 x 16
+  // bytes (lanes out of range write zeros).
+  constexpr int XSB = STEPB * XR;
+  const int xs_chunks = (int)M * (XSB / 16);  // 16-byte chunks per step
+  const int XSL = (xs_chunks + 63) / 64 * 1024;
+  uint8_t* xsl = dq_lds + (int64_t)wave * U * XSL;
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, XS ? (int)(M * KB * XR) : 0, 0x00020000);
+  bool xok[U][2];
 
   // Block scales: sb[n0/128][kb] is uniform over the workgroup; sa[tok][kb]
   // per lane (one token per tile with swap, four without).
@@ -301,7 +329,21 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
         for (int rt = 0; rt < RT; ++rt) msc[u][rt] = *(const uint16_t*)(msp[rt] + (int64_t)st * 8);
       }
       if (part == 1) continue;
-      if constexpr (MX) {
+      if constexpr (XS) {
+        // One direct-to-LDS load per 64 chunks: chunk q (token q / (XSB/16),
+        // piece q % (XSB/16)) lands at byte 16 q of the step's slice; lanes
+        // past the last chunk get an out-of-range offset (no access).
+        xok[u][0] = ok0;
+        xok[u][1] = ok1;
+        for (int i = 0; i * 64 < xs_chunks; ++i) {
+          const int q = i * 64 + lane;
+          const int tq = q / (XSB / 16), pq = q - tq * (XSB / 16);
+          const int voff = q < xs_chunks ? (int)(tq * KB * XR + (int64_t)st * XSB + pq * 16)
+                                         : 0x7FFFFFF0;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              xrs, (lds_void*)(xsl + (int64_t)u * XSL + i * 1024), 16, voff, 0, 0, 0);
+        }
+      } else if constexpr (MX) {
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
@@ -336,7 +378,26 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) acc[rt][tt] = C{0, 0, 0, 0};
 
+  // With AM_STAGE: the step's fragments from the wave's LDS slice, once the
+  // direct-to-LDS loads have landed (vmcnt 0; the weight loads of the batch
+  // are needed now anyway).
+  auto read_staged = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    const int64_t tok = min((int64_t)l16, M - 1);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint8_t* xr = xsl + (int64_t)u * XSL + tok * XSB + g * 32 * XR;
+      if constexpr (MX) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xb[u][0].v[j] = ld16(xr + 16 * j, j < 4 ? xok[u][0] : xok[u][1]);
+      } else {
+        xb[u][0] = cat(ld16(xr, xok[u][0]), ld16(xr + 16, xok[u][1]));
+      }
+    }
+  };
+
   auto compute_batch = [&]() {
+    if constexpr (XS) read_staged();
     if constexpr (MX) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -602,13 +663,22 @@ inline size_t dq_lds_bytes(int qk, const Call& c) {
   return (rows + sc + 15) & ~(size_t)15;
 }
 
-template <int QK, int NTT, bool SWAP, int W, int U, int RT, bool DQ = false>
+// Dynamic LDS of the staged-activation mode: W waves x U steps x the M
+// tokens' activation bytes of one step, rounded up to whole KiB (the
+// direct-to-LDS loads write 1 KiB each).
+inline size_t xs_lds_bytes(int qk, int W, int U, const Call& c) {
+  const size_t chunks = (size_t)c.M * STEPB * (qk == QK_MXFP4 ? 4 : 1) / 16;
+  return (size_t)W * U * ((chunks + 63) / 64 * 1024);
+}
+
+template <int QK, int NTT, bool SWAP, int W, int U, int RT, int AM = AM_GLOBAL>
 hipError_t launch_d(const Variant& v, const Call& c, int split, hipStream_t s) {
+  constexpr bool DQ = AM == AM_QUANT;
   const int groups = (int)((c.N + v.rows - 1) / v.rows);
   const int total_steps = (int)((c.KB + STEPB - 1) / STEPB);
   const int sps = (total_steps + split - 1) / split;
-  const size_t dyn = DQ ? dq_lds_bytes(QK, c) : 0;
-  hipLaunchKernelGGL((decode_kernel<QK, NTT, SWAP, W, U, RT, DQ>), dim3(groups, split),
+  const size_t dyn = DQ ? dq_lds_bytes(QK, c) : (AM == AM_STAGE ? xs_lds_bytes(QK, W, U, c) : 0);
+  hipLaunchKernelGGL((decode_kernel<QK, NTT, SWAP, W, U, RT, AM>), dim3(groups, split),
                      dim3((W + (op_wave(SWAP, W) ? 1 : 0)) * 64),
                      dyn, s, (const uint8_t*)c.A, (const uint8_t*)c.B, c.M, c.N, c.KB, v.rows, split,
                      sps, v.reduce, c.epi, c.ws, c.counters);
@@ -661,7 +731,7 @@ bool dq_kernel(const Variant& v, const Call& c, const void** fn) {
   *fn = nullptr;
 #define LG_DQ_FN(qk, w, u, rt)                                                      \
   if (v.waves == w && v.unroll == u && tiles_for(v.rows) == rt)                     \
-    *fn = reinterpret_cast<const void*>(&decode_kernel<qk, 1, true, w, u, rt, true>);
+    *fn = reinterpret_cast<const void*>(&decode_kernel<qk, 1, true, w, u, rt, AM_QUANT>);
   LG_DECODE_DQ(LG_DQ_FN, QK)
 #undef LG_DQ_FN
   if (!*fn) return false;
@@ -678,7 +748,7 @@ template <int QK>
 hipError_t launch_dq_prologue(const Variant& v, const Call& c, hipStream_t s) {
 #define LG_DQ_TRY(qk, w, u, rt)                                                     \
   if (v.waves == w && v.unroll == u && tiles_for(v.rows) == rt)                     \
-    return launch_d<qk, 1, true, w, u, rt, true>(v, c, 1, s);
+    return launch_d<qk, 1, true, w, u, rt, AM_QUANT>(v, c, 1, s);
   LG_DECODE_DQ(LG_DQ_TRY, QK)
 #undef LG_DQ_TRY
   return hipErrorInvalidValue;
@@ -746,6 +816,42 @@ hipError_t launch_mx(const Variant& v, const Call& c, int split, hipStream_t s) 
     return launch_d<QK_MXFP4, NTT, true, w, u, rt>(v, c, split, s);
   LG_DECODE_MX(LG_MX_TRY)
 #undef LG_MX_TRY
+  return hipErrorInvalidValue;
+}
+
+// Variants with staged activations (AM_STAGE; swap, one token tile).
+#define LG_DECODE_XS(X)                                                                \
+  X(QK_FP8, 8, 1, 1) X(QK_FP8, 8, 2, 1) X(QK_FP8, 8, 4, 1) X(QK_FP8, 8, 4, 2)          \
+  X(QK_FP8, 12, 1, 1) X(QK_MXFP4, 8, 1, 1) X(QK_MXFP4, 8, 2, 1) X(QK_MXFP4, 8, 1, 2)   \
+  X(QK_MXFP4, 12, 1, 1)
+
+bool decode_xs_supported(const Variant& v, const Call& c) {
+  if (v.kind != V_DECODE || v.swap != 1 || c.M < 1 || c.M > 16) return false;
+  const void* fn = nullptr;
+  int w_ = 0, u_ = 0;
+#define LG_XS_FN(q_, w, u, rt)                                                      \
+  if (c.qk == q_ && v.waves == w && v.unroll == u && tiles_for(v.rows) == rt) {     \
+    fn = reinterpret_cast<const void*>(&decode_kernel<q_, 1, true, w, u, rt, AM_STAGE>); \
+    w_ = w; u_ = u;                                                                 \
+  }
+  LG_DECODE_XS(LG_XS_FN)
+#undef LG_XS_FN
+  if (!fn) return false;
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, fn) != hipSuccess) return false;
+  int dev = 0, max_lds = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return false;
+  return attr.sharedSizeBytes + xs_lds_bytes(c.qk, w_, u_, c) <= (size_t)max_lds;
+}
+
+hipError_t launch_decode_xs(const Variant& v, const Call& c, int split, hipStream_t s) {
+#define LG_XS_TRY(q_, w, u, rt)                                                     \
+  if (c.qk == q_ && v.waves == w && v.unroll == u && tiles_for(v.rows) == rt)       \
+    return launch_d<q_, 1, true, w, u, rt, AM_STAGE>(v, c, split, s);
+  LG_DECODE_XS(LG_XS_TRY)
+#undef LG_XS_TRY
   return hipErrorInvalidValue;
 }
 

@@ -30,6 +30,9 @@ struct Variant {
   // in the kernel's prologue where that variant supports it, 0 = in a
   // separate kernel first (the default: the prologue pays only for one token)
   int dq = 0;
+  // decode family: 1 = stage the activations through LDS where the variant
+  // is compiled for it (small M), 0 = every lane loads its own
+  int xs = 0;
 };
 
 struct Call {
@@ -67,6 +70,11 @@ bool decode_dq_supported(const Variant& v, const Call& c, int split);
 // Whether the decode variant is compiled for MXFP4 weights (swap, waves /
 // unroll / tiles from a short list).
 bool decode_mx_supported(const Variant& v);
+// Decode with activations staged through LDS (AM_STAGE): e4m3 and MXFP4
+// weights, swap, M <= 16, the variants compiled with it, LDS within the
+// device limit.
+bool decode_xs_supported(const Variant& v, const Call& c);
+hipError_t launch_decode_xs(const Variant& v, const Call& c, int split, hipStream_t s);
 hipError_t launch_decode_dq(const Variant& v, const Call& c, hipStream_t s);
 // Second pass of a two-pass split-K reduction: sums the fp32 / int32 slices
 // [split][M][N] in slice order and applies the epilogue.
