@@ -823,7 +823,8 @@ hipError_t launch_mx(const Variant& v, const Call& c, int split, hipStream_t s) 
 #define LG_DECODE_XS(X)                                                                \
   X(QK_FP8, 8, 1, 1) X(QK_FP8, 8, 2, 1) X(QK_FP8, 8, 4, 1) X(QK_FP8, 8, 4, 2)          \
   X(QK_FP8, 12, 1, 1) X(QK_MXFP4, 8, 1, 1) X(QK_MXFP4, 8, 2, 1) X(QK_MXFP4, 8, 1, 2)   \
-  X(QK_MXFP4, 12, 1, 1)
+  X(QK_MXFP4, 12, 1, 1) X(QK_I8, 4, 4, 1) X(QK_I8, 8, 2, 1) X(QK_I8, 8, 4, 2)          \
+  X(QK_FP8_BLOCK, 12, 1, 1) X(QK_FP8_BLOCK, 8, 1, 1) X(QK_FP8_BLOCK, 16, 1, 1)
 
 bool decode_xs_supported(const Variant& v, const Call& c) {
   if (v.kind != V_DECODE || v.swap != 1 || c.M < 1 || c.M > 16) return false;

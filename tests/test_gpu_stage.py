@@ -2,8 +2,9 @@
 its steps' activation bytes into LDS with direct-to-LDS loads and the lanes
 read their fragments from there).  The products and their order are those of
 the same variant without staging, so the outputs must be identical bit for
-bit; they are also checked against the oracle.  Covers e4m3 and MXFP4
-weights, ragged K tails (e4m3), one to sixteen tokens and a split-K case."""
+bit; they are also checked against the oracle (the int8 accumulator
+exactly).  Covers e4m3, int8, block e4m3 and MXFP4 weights, ragged K tails
+(e4m3), one to sixteen tokens and a split-K case."""
 import numpy as np
 import pytest
 import torch
@@ -22,7 +23,11 @@ CASES = [("fp8_dynamic", "none", 1, 1040, 4096, True, False),
          ("fp8_dynamic", "silu", 16, 6144, 1024, True, False),
          ("mxfp4", "none", 1, 1040, 4096, True, False),
          ("mxfp4", "relu", 5, 528, 256, False, True),
-         ("mxfp4", "silu", 16, 272, 512, True, False)]
+         ("mxfp4", "silu", 16, 272, 512, True, False),
+         ("w8a8_int8", "silu", 4, 2064, 4096, False, False),
+         ("block_fp8", "none", 3, 512, 3072, False, True)]
+I8_SHAPES = [(4, 4, 16), (8, 2, 16), (8, 4, 24)]
+BLOCK_SHAPES = [(12, 1, 16), (8, 1, 16), (16, 1, 16)]
 
 
 @pytest.fixture(scope="module")
@@ -50,7 +55,8 @@ def test_staged_activations_match(handle, case):
     p = synth.make_custom(quant, act, M, N, K, seed=3 * M + N + K, bias=b, residual=r)
     ref, _ = oracle.linear(quant, act, p.A, p.B, sa=p.sa, sb=p.sb, bias=p.bias,
                            residual=p.residual, alpha=p.alpha)
-    shapes = MX_SHAPES if quant == "mxfp4" else FP8_SHAPES
+    shapes = {"mxfp4": MX_SHAPES, "w8a8_int8": I8_SHAPES, "block_fp8": BLOCK_SHAPES}.get(
+        quant, FP8_SHAPES)
     specs = [f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} rows={rows}"
              for w, u, rows in shapes]
     specs.append("decode swap=1 split=2 reduce=lastwg waves=8 unroll=1 rows=16")
@@ -65,4 +71,15 @@ def test_staged_activations_match(handle, case):
         C0 = run(handle, p, spec)
         assert torch.equal(C1, C0), f"staged vs direct differ [{spec}]"
         assert_close(decode_out(C1, quant), ref, f"staged {quant} {M}x{N}x{K} [{spec}]")
+        if quant == "w8a8_int8":
+            Craw = torch.empty((M, N), dtype=torch.int32, device="cuda")
+            handle.set_force(spec + " xs=1")
+            try:
+                handle.run(dev(p.A), dev(p.B), Craw, quant=quant, act="raw_acc", sa=dev(p.sa),
+                           sb=dev(p.sb))
+            finally:
+                handle.set_force(None)
+            torch.cuda.synchronize()
+            _, acc = oracle.linear(quant, "none", p.A, p.B, p.sa, p.sb)
+            assert np.array_equal(Craw.cpu().numpy(), acc), f"int8 accumulator [{spec}]"
     assert staged >= len(specs) - 2, "the staged mode was not used"
