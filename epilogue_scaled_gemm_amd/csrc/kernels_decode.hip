@@ -80,7 +80,7 @@ constexpr bool op_wave(bool swap, int w) { return swap && w >= 8 && w < 16; }
 //             fragments from there.  The lanes of a token tile share tokens
 //             (16 lanes per token at M = 1), so this replaces up to 16
 //             redundant global loads per distinct chunk by LDS broadcasts.
-//             Swap, one token tile.
+//             Swap orientation.
 //  AM_QUANT   the quantization prologue below.
 //
 // AM_QUANT: A holds bf16 activations X[M][K] instead of codes, and the kernel
@@ -201,7 +201,7 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
   constexpr bool DQ = AM == AM_QUANT;
   constexpr bool XS = AM == AM_STAGE;
   static_assert(!MX || (SWAP && !DQ), "MXFP4 weights use the swap orientation");
-  static_assert(!XS || (SWAP && NTT == 1), "staged activations are for swap, one token tile");
+  static_assert(!XS || SWAP, "staged activations are for the swap orientation");
   constexpr int NS = SWAP ? 1 : 4;    // block scales per token tile per lane
   constexpr int NTILE = RT * NTT;     // 16x16 output tiles per workgroup
   __shared__ AccT red[W][NTILE * 4][64];
@@ -383,17 +383,20 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
   // are needed now anyway).
   auto read_staged = [&]() {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    const int64_t tok = min((int64_t)l16, M - 1);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint8_t* xr = xsl + (int64_t)u * XSL + tok * XSB + g * 32 * XR;
-      if constexpr (MX) {
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xb[u][0].v[j] = ld16(xr + 16 * j, j < 4 ? xok[u][0] : xok[u][1]);
-      } else {
-        xb[u][0] = cat(ld16(xr, xok[u][0]), ld16(xr + 16, xok[u][1]));
+      for (int tt = 0; tt < NTT; ++tt) {
+        const int64_t tok = min((int64_t)(tt * 16 + l16), M - 1);
+        const uint8_t* xr = xsl + (int64_t)u * XSL + tok * XSB + g * 32 * XR;
+        if constexpr (MX) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            xb[u][tt].v[j] = ld16(xr + 16 * j, j < 4 ? xok[u][0] : xok[u][1]);
+        } else {
+          xb[u][tt] = cat(ld16(xr, xok[u][0]), ld16(xr + 16, xok[u][1]));
+        }
       }
-    }
   };
 
   auto compute_batch = [&]() {
@@ -821,18 +824,22 @@ hipError_t launch_mx(const Variant& v, const Call& c, int split, hipStream_t s) 
 
 // Variants with staged activations (AM_STAGE; swap, one token tile).
 #define LG_DECODE_XS(X)                                                                \
-  X(QK_FP8, 8, 1, 1) X(QK_FP8, 8, 2, 1) X(QK_FP8, 8, 4, 1) X(QK_FP8, 8, 4, 2)          \
-  X(QK_FP8, 12, 1, 1) X(QK_MXFP4, 8, 1, 1) X(QK_MXFP4, 8, 2, 1) X(QK_MXFP4, 8, 1, 2)   \
-  X(QK_MXFP4, 12, 1, 1) X(QK_I8, 4, 4, 1) X(QK_I8, 8, 2, 1) X(QK_I8, 8, 4, 2)          \
-  X(QK_FP8_BLOCK, 12, 1, 1) X(QK_FP8_BLOCK, 8, 1, 1) X(QK_FP8_BLOCK, 16, 1, 1)
+  X(QK_FP8, 1, 8, 1, 1) X(QK_FP8, 1, 8, 2, 1) X(QK_FP8, 1, 8, 4, 1) X(QK_FP8, 1, 8, 4, 2) \
+  X(QK_FP8, 1, 12, 1, 1) X(QK_MXFP4, 1, 8, 1, 1) X(QK_MXFP4, 1, 8, 2, 1)                 \
+  X(QK_MXFP4, 1, 8, 1, 2) X(QK_MXFP4, 1, 12, 1, 1) X(QK_I8, 1, 4, 4, 1) X(QK_I8, 1, 8, 2, 1) \
+  X(QK_I8, 1, 8, 4, 2) X(QK_FP8_BLOCK, 1, 12, 1, 1) X(QK_FP8_BLOCK, 1, 8, 1, 1)          \
+  X(QK_FP8_BLOCK, 1, 16, 1, 1) X(QK_FP8, 2, 8, 1, 2) X(QK_FP8, 2, 8, 4, 2)              \
+  X(QK_I8, 2, 4, 2, 2) X(QK_MXFP4, 2, 4, 2, 2) X(QK_MXFP4, 2, 8, 1, 2)                 \
+  X(QK_FP8_BLOCK, 2, 8, 2, 2)
 
 bool decode_xs_supported(const Variant& v, const Call& c) {
-  if (v.kind != V_DECODE || v.swap != 1 || c.M < 1 || c.M > 16) return false;
+  if (v.kind != V_DECODE || v.swap != 1 || c.M < 1 || c.M > 32) return false;
+  const int ntt = c.M <= 16 ? 1 : 2;
   const void* fn = nullptr;
   int w_ = 0, u_ = 0;
-#define LG_XS_FN(q_, w, u, rt)                                                      \
-  if (c.qk == q_ && v.waves == w && v.unroll == u && tiles_for(v.rows) == rt) {     \
-    fn = reinterpret_cast<const void*>(&decode_kernel<q_, 1, true, w, u, rt, AM_STAGE>); \
+#define LG_XS_FN(q_, nt, w, u, rt)                                                  \
+  if (c.qk == q_ && ntt == nt && v.waves == w && v.unroll == u && tiles_for(v.rows) == rt) { \
+    fn = reinterpret_cast<const void*>(&decode_kernel<q_, nt, true, w, u, rt, AM_STAGE>); \
     w_ = w; u_ = u;                                                                 \
   }
   LG_DECODE_XS(LG_XS_FN)
@@ -848,9 +855,10 @@ bool decode_xs_supported(const Variant& v, const Call& c) {
 }
 
 hipError_t launch_decode_xs(const Variant& v, const Call& c, int split, hipStream_t s) {
-#define LG_XS_TRY(q_, w, u, rt)                                                     \
-  if (c.qk == q_ && v.waves == w && v.unroll == u && tiles_for(v.rows) == rt)       \
-    return launch_d<q_, 1, true, w, u, rt, AM_STAGE>(v, c, split, s);
+  const int ntt = c.M <= 16 ? 1 : 2;
+#define LG_XS_TRY(q_, nt, w, u, rt)                                                 \
+  if (c.qk == q_ && ntt == nt && v.waves == w && v.unroll == u && tiles_for(v.rows) == rt) \
+    return launch_d<q_, nt, true, w, u, rt, AM_STAGE>(v, c, split, s);
   LG_DECODE_XS(LG_XS_TRY)
 #undef LG_XS_TRY
   return hipErrorInvalidValue;

@@ -43,10 +43,11 @@ DECODE_CANDIDATES = [
 ] + ["decode swap=0 split=1 reduce=twopass waves=8 unroll=2",
      "decode swap=1 split=2 reduce=lastwg waves=8 unroll=1 rows=32",
      "decode swap=1 split=2 reduce=atomic waves=8 unroll=1 rows=32"]
-# Staged activations (xs=1), compiled for some shapes per weight format, M <= 16
+# Staged activations (xs=1), compiled for some shapes per weight format
 # (a shape without it runs unstaged and simply times the same).
 XS_SHAPES = [(8, 1, 12), (8, 1, 16), (8, 2, 16), (8, 4, 12), (8, 4, 24), (12, 1, 16),
-             (8, 1, 24), (8, 2, 12), (4, 4, 16), (16, 1, 16)]
+             (8, 1, 24), (8, 2, 12), (4, 4, 16), (16, 1, 16), (4, 2, 32), (8, 1, 32),
+             (8, 2, 32)]
 XS_CANDIDATES = [f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} rows={r} xs=1"
                  for w, u, r in XS_SHAPES]
 
@@ -183,7 +184,7 @@ def sweep(workloads, out_path, reps, log=print, max_m=None, all_m=False, dynamic
             ncopy = max(2, min(32, -(-ROTATION_BYTES // p.B.nbytes)))
             Bs = [ops["B"]] + [ops["B"].clone() for _ in range(ncopy - 1)]
             cands = DECODE_CANDIDATES if M <= 32 else TILE_CANDIDATES
-            if M <= 16 and p.quant in ("fp8_dynamic", "mxfp4", "w8a8_int8", "block_fp8"):
+            if p.quant in ("fp8_dynamic", "mxfp4", "w8a8_int8", "block_fp8"):
                 cands = cands + XS_CANDIDATES
             # Warm every candidate first (the handle's split-K workspace only
             # grows, so it reaches its final size before any graph is

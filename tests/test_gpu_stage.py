@@ -83,3 +83,29 @@ def test_staged_activations_match(handle, case):
             _, acc = oracle.linear(quant, "none", p.A, p.B, p.sa, p.sb)
             assert np.array_equal(Craw.cpu().numpy(), acc), f"int8 accumulator [{spec}]"
     assert staged >= len(specs) - 2, "the staged mode was not used"
+
+
+# Two token tiles (17..32 tokens): the variants compiled with staging there.
+TWO_TILE = [("fp8_dynamic", "none", 24, 1040, 4096, True, False, [(8, 1, 24), (8, 1, 32), (8, 4, 24)]),
+            ("w8a8_int8", "silu", 32, 528, 1024, False, False, [(4, 2, 32)]),
+            ("mxfp4", "gelu_tanh", 20, 272, 512, True, True, [(4, 2, 32), (8, 1, 24)]),
+            ("block_fp8", "none", 17, 256, 1024, False, True, [(8, 2, 32)])]
+
+
+@pytest.mark.parametrize("case", TWO_TILE, ids=[f"{c[0]}-M{c[2]}" for c in TWO_TILE])
+def test_staged_two_token_tiles(handle, case):
+    quant, act, M, N, K, b, r, shapes = case
+    p = synth.make_custom(quant, act, M, N, K, seed=5 * M + N, bias=b, residual=r)
+    ref, acc = oracle.linear(quant, act, p.A, p.B, sa=p.sa, sb=p.sb, bias=p.bias,
+                             residual=p.residual, alpha=p.alpha)
+    for w, u, rows in shapes:
+        spec = f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} rows={rows}"
+        handle.set_force(spec + " xs=1")
+        used = "xs=1" in handle.describe(quant, M, N, K)
+        handle.set_force(None)
+        print(f"[stage] {quant} {M}x{N}x{K} {spec} staged={used}", flush=True)
+        assert used, f"staged mode not available for {spec}"
+        C1 = run(handle, p, spec + " xs=1")
+        C0 = run(handle, p, spec)
+        assert torch.equal(C1, C0), f"staged vs direct differ [{spec}]"
+        assert_close(decode_out(C1, quant), ref, f"staged {quant} {M}x{N}x{K} [{spec}]")
