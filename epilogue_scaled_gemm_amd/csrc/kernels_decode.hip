@@ -36,7 +36,9 @@
 //    it; exact for int32, order-dependent rounding for fp32) or twopass
 //    (partials, then splitk_reduce sums them in slice order).  The nonlinear
 //    epilogue always runs on the complete sum.
+#include <mutex>
 #include <type_traits>
+#include <unordered_map>
 
 #include "launch.hpp"
 
@@ -727,6 +729,32 @@ hipError_t launch_q(const Variant& v, const Call& c, int split, hipStream_t s) {
   X(QK, 8, 1, 1) X(QK, 8, 2, 1) X(QK, 8, 4, 1) X(QK, 8, 4, 2) X(QK, 12, 1, 1) \
   X(QK, 4, 4, 1)
 
+// Whether a kernel's static LDS plus `dyn` bytes of dynamic LDS fit the
+// current device's per-workgroup limit.  The kernel's static size and each
+// device's limit are queried once and cached (the calls sit on the launch
+// path).
+bool lds_fits(const void* fn, size_t dyn) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, size_t> static_lds;
+  static int dev_max[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = static_lds.find(fn);
+  if (it == static_lds.end()) {
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, fn) != hipSuccess) return false;
+    it = static_lds.emplace(fn, attr.sharedSizeBytes).first;
+  }
+  if (dev_max[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+      return false;
+    dev_max[dev] = v;
+  }
+  return it->second + dyn <= (size_t)dev_max[dev];
+}
+
 // Whether the prologue variant exists and its LDS (static + dynamic) fits
 // the device's per-workgroup limit; if so, *fn is the kernel.
 template <int QK>
@@ -737,14 +765,7 @@ bool dq_kernel(const Variant& v, const Call& c, const void** fn) {
     *fn = reinterpret_cast<const void*>(&decode_kernel<qk, 1, true, w, u, rt, AM_QUANT>);
   LG_DECODE_DQ(LG_DQ_FN, QK)
 #undef LG_DQ_FN
-  if (!*fn) return false;
-  hipFuncAttributes attr;
-  if (hipFuncGetAttributes(&attr, *fn) != hipSuccess) return false;
-  int dev = 0, max_lds = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-    return false;
-  return attr.sharedSizeBytes + dq_lds_bytes(QK, c) <= (size_t)max_lds;
+  return *fn && lds_fits(*fn, dq_lds_bytes(QK, c));
 }
 
 template <int QK>
@@ -844,14 +865,7 @@ bool decode_xs_supported(const Variant& v, const Call& c) {
   }
   LG_DECODE_XS(LG_XS_FN)
 #undef LG_XS_FN
-  if (!fn) return false;
-  hipFuncAttributes attr;
-  if (hipFuncGetAttributes(&attr, fn) != hipSuccess) return false;
-  int dev = 0, max_lds = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-    return false;
-  return attr.sharedSizeBytes + xs_lds_bytes(c.qk, w_, u_, c) <= (size_t)max_lds;
+  return fn && lds_fits(fn, xs_lds_bytes(c.qk, w_, u_, c));
 }
 
 hipError_t launch_decode_xs(const Variant& v, const Call& c, int split, hipStream_t s) {
