@@ -33,7 +33,8 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "HIP error",
 # The symbols include/lin_gemm.h declares.
 EXPORTS = ("lin_gemm_create", "lin_gemm_run", "lin_gemm_destroy", "lin_gemm_strerror",
            "lin_gemm_last_error", "lin_gemm_set_force", "lin_gemm_describe",
-           "lin_gemm_run_unfused", "lin_gemm_quantize", "lin_gemm_run_dynamic")
+           "lin_gemm_run_unfused", "lin_gemm_quantize", "lin_gemm_run_dynamic",
+           "lin_gemm_run_grouped")
 DQ_KIND = {"fp8_token": 0, "int8_token": 1, "fp8_block": 2}
 X_DTYPE = {"bf16": 0, "fp16": 1}
 
@@ -83,6 +84,9 @@ def library():
     lib.lin_gemm_run_dynamic.argtypes = [P, P, I, P, P, ctypes.c_float, P, P, P, I64, I64, I64,
                                          I, I, P]
     lib.lin_gemm_run_dynamic.restype = I
+    lib.lin_gemm_run_grouped.argtypes = [P, P, P, ctypes.POINTER(_Scales), P, P, P, P, I64, I64,
+                                         I64, I64, I64, I, I, P]
+    lib.lin_gemm_run_grouped.restype = I
     _lib = lib
     return lib
 
@@ -177,6 +181,26 @@ class Handle:
                                             _ptr(C), M, N, K, _code(QUANT, quant),
                                             _code(ACT, act), _stream(stream))
         self._check(rc, "lin_gemm_run_dynamic")
+        return C
+
+    def run_grouped(self, A, B, C, offsets, quant="bf16", act="none", sa=None, sb=None,
+                    alpha=1.0, bias=None, residual=None, max_rows=0, stream=None):
+        """Mixture-of-experts layer: A[M,K] rows sorted by expert, B[E,N,K]
+        (E,N,K/2 bytes for mxfp4), offsets int32[E+1] on the GPU; expert x's
+        rows [offsets[x], offsets[x+1]) use B[x], sb[x] and bias[x]."""
+        M, K = A.shape
+        E, N, kb = B.shape
+        if kb != (K // 2 if quant in ("mxfp4", 5) else K):
+            raise ValueError(f"inner dimensions differ: A has K={K}, B rows have {kb}")
+        if offsets.dtype != torch.int32 or offsets.numel() != E + 1:
+            raise ValueError("offsets must be int32 with E + 1 entries")
+        sc = _Scales(None if sa is None else _ptr(sa).value,
+                     None if sb is None else _ptr(sb).value, float(alpha))
+        rc = self._lib.lin_gemm_run_grouped(self._h, _ptr(A), _ptr(B), ctypes.byref(sc),
+                                            _ptr(bias), _ptr(residual), _ptr(C), _ptr(offsets),
+                                            E, M, N, K, int(max_rows), _code(QUANT, quant),
+                                            _code(ACT, act), _stream(stream))
+        self._check(rc, "lin_gemm_run_grouped")
         return C
 
     def set_force(self, spec):

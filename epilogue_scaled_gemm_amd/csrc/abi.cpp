@@ -9,6 +9,7 @@
 // anything is enqueued; kernels never see a shape they were not built for.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -492,6 +493,52 @@ int lin_gemm_run_dynamic(lin_gemm_t h, const void* X, int x_dtype, const void* B
   if (rc != LIN_OK) return rc;
   lin_scales_t sc{sa, sb, alpha};
   return lin_gemm_run(h, h->dq, B, &sc, bias, residual, C, M, N, K, quant_mode, activation, stream);
+}
+
+int lin_gemm_run_grouped(lin_gemm_t h, const void* A, const void* B, const lin_scales_t* scales,
+                         const void* bias, const void* residual, void* C, const int32_t* offsets,
+                         int64_t E, int64_t M, int64_t N, int64_t K, int64_t max_rows,
+                         int quant_mode, int activation, void* stream) {
+  if (!h) return LIN_ERR_INVALID_ARG;
+  h->last_error.clear();
+  if (E < 0 || M < 0 || max_rows < 0) return fail(h, LIN_ERR_INVALID_ARG, "negative size");
+  // Each token chunk is a decode-shaped call of up to 32 rows: the shape rules
+  // of lin_gemm_run apply to it.
+  int rc = check_shape(h, quant_mode, M == 0 ? 0 : 1, N, K);
+  if (rc != LIN_OK || M == 0 || E == 0) return rc;
+  if (M >= ((int64_t)1 << 31)) return fail(h, LIN_ERR_UNSUPPORTED, "M beyond 2^31");
+  if (E > 65535) return fail(h, LIN_ERR_UNSUPPORTED, "more than 65535 experts");
+  if (!A || !B || !C || !offsets)
+    return fail(h, LIN_ERR_INVALID_ARG, "A, B, C and offsets must be non-null");
+  if (!(activation >= LIN_ACT_NONE && activation <= LIN_ACT_SILU) && activation != LIN_ACT_RAW_ACC)
+    return fail(h, LIN_ERR_INVALID_ARG, "unknown activation " + std::to_string(activation));
+  const bool quantised = quant_mode >= LIN_Q_FP8_DYNAMIC && quant_mode != LIN_Q_MXFP4;
+  if (quantised && (!scales || !scales->a || !scales->b))
+    return fail(h, LIN_ERR_INVALID_ARG, "quantised modes need scales->a and scales->b");
+  if (quant_mode == LIN_Q_MXFP4 && (!scales || !scales->b))
+    return fail(h, LIN_ERR_INVALID_ARG, "MXFP4 weights need scales->b (E8M0 bytes)");
+  if (misaligned(A) || misaligned(B) || misaligned(C) || misaligned(bias) || misaligned(residual))
+    return fail(h, LIN_ERR_UNSUPPORTED, "A, B, C, bias and residual must be 16-byte aligned");
+  if (scales && (misaligned(scales->a) || misaligned(scales->b)))
+    return fail(h, LIN_ERR_UNSUPPORTED, "scale arrays must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(offsets) & 3)
+    return fail(h, LIN_ERR_UNSUPPORTED, "offsets must be 4-byte aligned");
+
+  lg::Call c{};
+  c.A = A; c.B = B; c.M = M; c.N = N; c.K = K;
+  c.KB = b_row_bytes(quant_mode, K);
+  c.qk = qkind(quant_mode);
+  c.epi = make_epi(scales, bias, residual, C, M, N, quant_mode, activation);
+  const int64_t bound = (max_rows == 0 || max_rows > M) ? M : max_rows;
+  const int ntt = bound <= 16 ? 1 : 2;
+  const int chunks = (int)std::min<int64_t>((bound + 16 * ntt - 1) / (16 * ntt), 65535);
+  // Staged activations where the variant exists, unless a forced variant
+  // says otherwise.
+  bool xs = h->forced ? h->force.xs != 0 : true;
+  xs = xs && lg::grouped_xs_supported(c.qk, ntt, c.KB);
+  hipError_t e = lg::launch_grouped(c, offsets, E, ntt, chunks, xs, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(h, e, "grouped kernel launch");
+  return LIN_OK;
 }
 
 }  // extern "C"

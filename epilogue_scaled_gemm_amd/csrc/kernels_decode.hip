@@ -184,10 +184,12 @@ __device__ inline void quant_prologue(const uint16_t* __restrict__ X, int64_t M,
   __syncthreads();
 }
 
+// The body of the decode kernel: workgroup blockIdx.x owns weight rows
+// [blockIdx.x * rpw, + rpw) and K slice sidx of `split`.
 template <int QK, int NTT, bool SWAP, int W, int U, int RT, int AM>
-__global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_kernel(
+__device__ __forceinline__ void decode_body(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int64_t M, int64_t N,
-    int64_t KB, int rpw, int split, int steps_per_split, int reduce, Epi e,
+    int64_t KB, int rpw, int split, int sidx, int steps_per_split, int reduce, Epi e,
     void* __restrict__ ws, int* __restrict__ counters) {
   using MF = Mfma<QK>;
   using C = typename MF::C;
@@ -227,7 +229,6 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
   // multiple of 4); rows of its MFMA tiles past that are masked.
   const int64_t n0 = (int64_t)blockIdx.x * rpw;
   const int64_t nend = min(n0 + rpw, N);
-  const int sidx = blockIdx.y;
   const int total_steps = (int)((KB + STEPB - 1) / STEPB);
   const int beg = sidx * steps_per_split;
   const int end = min(beg + steps_per_split, total_steps);
@@ -638,6 +639,61 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
   if (threadIdx.x == 0) st_agent(counters + blockIdx.x, 0);
 }
 
+template <int QK, int NTT, bool SWAP, int W, int U, int RT, int AM>
+__global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int64_t M, int64_t N,
+    int64_t KB, int rpw, int split, int steps_per_split, int reduce, Epi e,
+    void* __restrict__ ws, int* __restrict__ counters) {
+  decode_body<QK, NTT, SWAP, W, U, RT, AM>(A, B, M, N, KB, rpw, split, (int)blockIdx.y,
+                                           steps_per_split, reduce, e, ws, counters);
+}
+
+// Grouped form (a mixture-of-experts layer, tokens sorted by expert):
+// expert x = blockIdx.y owns rows [offsets[x], offsets[x+1]) of A, the
+// residual and C, and its own weight B[x] (N rows of KB bytes) with its
+// weight scales and bias.  The expert's rows go through the decode body in
+// chunks of 16 NTT tokens (swap orientation, no split-K: the experts
+// already give the grid its width), chunk c on workgroup z = c mod
+// gridDim.z, so any segment length is covered whatever the grid's depth;
+// an expert without rows costs its workgroups two scalar loads.  Offsets
+// are clamped into [0, M] and an end below its start is an empty segment:
+// a malformed offset array gives wrong rows, never an access outside A, C
+// or the residual.
+template <int QK, int NTT, int W, int U, int RT, int AM>
+__global__ __launch_bounds__((W + (op_wave(true, W) ? 1 : 0)) * 64) void grouped_decode_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+    const int* __restrict__ offsets, int64_t M, int64_t N, int64_t KB, int rpw, int steps,
+    Epi e) {
+  constexpr bool MX = QK == QK_MXFP4;
+  constexpr bool BLOCK = QK == QK_FP8_BLOCK;
+  constexpr int64_t XR = MX ? 4 : 1;
+  constexpr int64_t MT = 16 * NTT;
+  const int64_t x = blockIdx.y;
+  const int64_t lo = min(max((int64_t)offsets[x], (int64_t)0), M);
+  const int64_t hi = min(max((int64_t)offsets[x + 1], lo), M);
+  const int64_t first = lo + (int64_t)blockIdx.z * MT;
+  if (first >= hi) return;
+  // The expert's weight, weight scales ([N] per channel, [N/128][KB/128]
+  // blocks, or [N][KB/16] E8M0 bytes) and bias.
+  const uint8_t* Bx = B + x * N * KB;
+  Epi ex = e;
+  if constexpr (MX) ex.sb = (const float*)((const uint8_t*)e.sb + x * N * (KB / 16));
+  else if constexpr (BLOCK) ex.sb = e.sb + x * (N / 128) * (KB / 128);
+  else if (e.sb) ex.sb = e.sb + x * N;
+  if (e.bias) ex.bias = e.bias + x * N;
+  const int64_t esz = e.raw ? 4 : 2;
+  for (int64_t r0 = first; r0 < hi; r0 += (int64_t)gridDim.z * MT) {
+    if (r0 != first) __syncthreads();  // the previous chunk is done with the LDS
+    Epi ec = ex;
+    ec.M = min(MT, hi - r0);
+    if (e.sa) ec.sa = e.sa + r0 * (BLOCK ? KB / 128 : 1);
+    if (e.residual) ec.residual = e.residual + r0 * N;
+    ec.C = (uint8_t*)e.C + r0 * N * esz;
+    decode_body<QK, NTT, true, W, U, RT, AM>(A + r0 * KB * XR, Bx, ec.M, N, KB, rpw, 1, 0,
+                                             steps, R_NONE, ec, nullptr, nullptr);
+  }
+}
+
 // Second pass of the two-pass reduction: sum the split partials of 4
 // consecutive columns in slice order, then the epilogue.
 template <int QK>
@@ -895,6 +951,73 @@ hipError_t launch_decode_dq(const Variant& v, const Call& c, hipStream_t s) {
     case QK_I8: return launch_dq_prologue<QK_I8>(v, c, s);
     case QK_FP8_BLOCK: return launch_dq_prologue<QK_FP8_BLOCK>(v, c, s);
   }
+  return hipErrorInvalidValue;
+}
+
+// Grouped (mixture-of-experts) variants: per quant mode and token tiles
+// (one: chunks of up to 16 tokens, two: up to 32), one variant with
+// activations loaded by each lane and, for the 8-bit and 4-bit weights, one
+// with activations staged through LDS.
+#define LG_GROUPED(X)                                                                    \
+  X(QK_BF16, 1, 8, 2, 1, AM_GLOBAL) X(QK_BF16, 2, 8, 1, 2, AM_GLOBAL)                    \
+  X(QK_FP16, 1, 8, 2, 1, AM_GLOBAL) X(QK_FP16, 2, 8, 1, 2, AM_GLOBAL)                    \
+  X(QK_FP8, 1, 8, 2, 1, AM_GLOBAL) X(QK_FP8, 2, 8, 1, 2, AM_GLOBAL)                      \
+  X(QK_FP8, 1, 8, 2, 1, AM_STAGE) X(QK_FP8, 2, 8, 1, 2, AM_STAGE)                        \
+  X(QK_I8, 1, 8, 2, 1, AM_GLOBAL) X(QK_I8, 2, 8, 1, 2, AM_GLOBAL)                        \
+  X(QK_I8, 1, 8, 2, 1, AM_STAGE) X(QK_I8, 2, 4, 2, 2, AM_STAGE)                          \
+  X(QK_FP8_BLOCK, 1, 8, 2, 1, AM_GLOBAL) X(QK_FP8_BLOCK, 2, 8, 1, 2, AM_GLOBAL)          \
+  X(QK_FP8_BLOCK, 1, 8, 1, 1, AM_STAGE) X(QK_FP8_BLOCK, 2, 8, 2, 2, AM_STAGE)            \
+  X(QK_MXFP4, 1, 8, 2, 1, AM_GLOBAL) X(QK_MXFP4, 2, 8, 1, 2, AM_GLOBAL)                  \
+  X(QK_MXFP4, 1, 8, 2, 1, AM_STAGE) X(QK_MXFP4, 2, 4, 2, 2, AM_STAGE)
+
+namespace {
+// The grouped variant for (qk, ntt, staged), its kernel and its LDS need.
+struct GroupedPick {
+  const void* fn = nullptr;
+  int w = 0, u = 0, rt = 0;
+};
+GroupedPick grouped_pick(int qk, int ntt, bool xs) {
+  GroupedPick p;
+#define LG_G_FN(q_, nt, w_, u_, rt_, am)                                             \
+  if (!p.fn && qk == q_ && ntt == nt && xs == (am == AM_STAGE)) {                   \
+    p.fn = reinterpret_cast<const void*>(&grouped_decode_kernel<q_, nt, w_, u_, rt_, am>); \
+    p.w = w_; p.u = u_; p.rt = rt_;                                                 \
+  }
+  LG_GROUPED(LG_G_FN)
+#undef LG_G_FN
+  return p;
+}
+}  // namespace
+
+bool grouped_xs_supported(int qk, int ntt, int64_t KB) {
+  const GroupedPick p = grouped_pick(qk, ntt, true);
+  if (!p.fn) return false;
+  Call c{};
+  c.qk = qk; c.M = 16 * ntt; c.KB = KB;
+  return lds_fits(p.fn, xs_lds_bytes(qk, p.w, p.u, c));
+}
+
+hipError_t launch_grouped(const Call& c, const int* offsets, int64_t E, int ntt, int chunks,
+                          bool xs, hipStream_t s) {
+  const GroupedPick p = grouped_pick(c.qk, ntt, xs);
+  if (!p.fn || E < 1 || E > 65535 || chunks < 1 || chunks > 65535) return hipErrorInvalidValue;
+  const int rows = 16 * p.rt;
+  const int64_t groups = (c.N + rows - 1) / rows;
+  const int steps = (int)((c.KB + STEPB - 1) / STEPB);
+  Call cm = c;
+  cm.M = 16 * ntt;  // staging holds one chunk
+  const size_t dyn = xs ? xs_lds_bytes(c.qk, p.w, p.u, cm) : 0;
+  const dim3 grid((unsigned)groups, (unsigned)E, (unsigned)chunks);
+#define LG_G_TRY(q_, nt, w_, u_, rt_, am)                                               \
+  if (c.qk == q_ && ntt == nt && xs == (am == AM_STAGE)) {                            \
+    hipLaunchKernelGGL((grouped_decode_kernel<q_, nt, w_, u_, rt_, am>), grid,         \
+                       dim3((w_ + (op_wave(true, w_) ? 1 : 0)) * 64), dyn, s,           \
+                       (const uint8_t*)c.A, (const uint8_t*)c.B, offsets, c.M, c.N, c.KB, \
+                       rows, steps, c.epi);                                             \
+    return hipGetLastError();                                                         \
+  }
+  LG_GROUPED(LG_G_TRY)
+#undef LG_G_TRY
   return hipErrorInvalidValue;
 }
 

@@ -204,6 +204,41 @@ int lin_gemm_run_dynamic(lin_gemm_t h, const void *X, int x_dtype, const void *B
                          void *C, int64_t M, int64_t N, int64_t K, int quant_mode,
                          int activation, void *stream);
 
+/* Grouped layer for a mixture of experts: E experts, the M token rows
+ * sorted by expert, expert x owning rows [offsets[x], offsets[x+1]) of A,
+ * residual and C, each multiplied by its own weight with its own scales and
+ * bias -- every segment is exactly lin_gemm_run on its rows with its
+ * expert's operands.  "helion-vllm-linear-backend" names a mixture-of-experts
+ * backend among its next steps (section "Что дальше") and defines
+ * none; this is the plain reading: a grouped product with per-expert
+ * weights, the per-token scales following their rows.
+ * Layouts (dense, contiguous, caller-owned device memory, 16-byte aligned):
+ *   A, residual, C, scales->a  as lin_gemm_run with M rows in expert order
+ *   B         [E][N][K] (per quant mode; [E][N][K/2] bytes for MXFP4)
+ *   scales->b [E][N] (FP8 dynamic, int8), [E][N/128][K/128] (block FP8),
+ *             [E][N][K/32] E8M0 bytes (MXFP4)
+ *   bias      [E][N] or NULL
+ *   offsets   int32 [E+1] in device memory (4-byte aligned), non-decreasing
+ *             from 0 to M.  The kernel reads it: it may be produced on the
+ *             same stream just before.  Values are clamped into [0, M] and a
+ *             segment whose end is below its start is empty, so a malformed
+ *             array gives wrong rows but no out-of-bounds access; rows no
+ *             segment covers are left unwritten.
+ * max_rows is an upper bound on any expert's row count that the caller
+ * knows (0 = M).  It sizes the grid only: rows run in chunks of up to 16
+ * (max_rows <= 16) or 32 tokens, each chunk streaming its expert's weight,
+ * and a workgroup takes every gridDim-th chunk of its expert, so a bound
+ * below the true count still gives the right result (more slowly).  The
+ * kernels are the decode family (swap orientation, no split-K), meant for
+ * decode-sized segments: a long segment streams the expert's weight once
+ * per chunk.  Requirements: those of lin_gemm_run for N and K per mode
+ * (MXFP4: K % 256 == 0; no limit on M), E <= 65535, M < 2^31.  E == 0 or
+ * M == 0 is a no-op.  No allocation; enqueued on `stream`. */
+int lin_gemm_run_grouped(lin_gemm_t h, const void *A, const void *B, const lin_scales_t *scales,
+                         const void *bias, const void *residual, void *C, const int32_t *offsets,
+                         int64_t E, int64_t M, int64_t N, int64_t K, int64_t max_rows,
+                         int quant_mode, int activation, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

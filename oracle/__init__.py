@@ -183,6 +183,37 @@ def linear_at(quant, act_name, A, B, idx_m, idx_n, sa=None, sb=None, bias=None,
     return out, acc
 
 
+def grouped_linear(quant, act_name, A, Bs, offsets, sa=None, sbs=None, biases=None,
+                   residual=None, alpha=1.0):
+    """Grouped layer (a mixture-of-experts linear): tokens sorted by expert,
+    expert e owning the rows [offsets[e], offsets[e+1]) of A, residual and the
+    result, multiplied by its own weight Bs[e] with its own weight scales
+    sbs[e] and bias biases[e].  Each segment is exactly `linear` on its rows;
+    per-token activation scales sa are sliced with the rows.  Returns the
+    [M, N] result and, for int8, the accumulator.
+
+    "helion-vllm-linear-backend", section "Что дальше": a mixture-of-experts
+    backend is named as work in progress and not defined; this is the plain
+    reading (a per-expert product over each expert's rows)."""
+    M = A.shape[0]
+    N = Bs[0].shape[0]
+    out = np.zeros((M, N), dtype=np.float64)
+    acc = np.zeros((M, N), dtype=np.int32) if quant == "w8a8_int8" else None
+    for e in range(len(Bs)):
+        m0, m1 = int(offsets[e]), int(offsets[e + 1])
+        if m1 <= m0:
+            continue
+        r, a = linear(quant, act_name, A[m0:m1], Bs[e],
+                      None if sa is None else sa[m0:m1],
+                      None if sbs is None else sbs[e],
+                      None if biases is None else biases[e],
+                      None if residual is None else residual[m0:m1], alpha)
+        out[m0:m1] = r
+        if acc is not None:
+            acc[m0:m1] = a
+    return out, acc
+
+
 def unfused_stage2(t, bias, quant="bf16", act_name="gelu_tanh"):
     t = _c(t, np.uint16)
     M, N = t.shape

@@ -250,6 +250,30 @@ def activations16(M: int, K: int, seed: int, x_dtype: str = "bf16", outliers: bo
     return to_fp16_bits(x) if x_dtype == "fp16" else to_bf16_bits(x)
 
 
+def make_grouped(quant: str, act: str, sizes, N: int, K: int, seed: int, bias=True,
+                 residual=False):
+    """A seeded mixture-of-experts problem: len(sizes) experts, expert e
+    receiving sizes[e] tokens (tokens sorted by expert); per-expert weights,
+    weight scales and bias.  Returns a dict of codes plus the int32 offsets."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    E = len(sizes)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M = int(offsets[-1])
+    Bs, sbs, biases = [], [], []
+    for _ in range(E):
+        B, sb = encode(quant, _draw(rng, (N, K), "normal", 0.02), "b")
+        Bs.append(B)
+        sbs.append(sb)
+        biases.append(encode16(quant, rng.random(N, dtype=np.float32) - np.float32(0.5))
+                      if bias else None)
+    A, sa = encode(quant, _draw(rng, (max(M, 1), K), "normal", 1.0), "a")
+    A = A[:M]
+    sa = None if sa is None else sa[:M]
+    res = encode16(quant, rng.standard_normal((M, N), dtype=np.float32)) if residual else None
+    return dict(quant=quant, act=act, M=M, N=N, K=K, E=E, A=A, Bs=Bs, sa=sa, sbs=sbs,
+                biases=biases if bias else None, residual=res, offsets=offsets)
+
+
 def algorithmic_bytes(quant: str, M: int, N: int, K: int, bias: bool, residual: bool) -> int:
     """Compulsory HBM bytes of one fused call: operands, scales, bias,
     residual and the one output write."""

@@ -224,3 +224,34 @@ def test_mxfp4_describe(cpu_handle):
     with pytest.raises(lg.LinGemmError):
         cpu_handle.describe("mxfp4", 8, 6144, 4096)        # not compiled for MXFP4
     cpu_handle.set_force(None)
+
+
+def _raw_grouped(h, A=FAKE, B=FAKE, C=FAKE, offsets=FAKE, E=4, M=8, N=16, K=64, max_rows=0,
+                 quant=0, act=0, scales=None, bias=None, residual=None):
+    lib = lg.library()
+    sc = lg._Scales(*(scales if scales else (None, None, 1.0)))
+    return lib.lin_gemm_run_grouped(h._h, A, B, ctypes.byref(sc), bias, residual, C, offsets, E,
+                                    M, N, K, max_rows, quant, act, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(E=-1), INVALID),
+    (dict(M=-1), INVALID),
+    (dict(max_rows=-2), INVALID),
+    (dict(quant=9), INVALID),
+    (dict(act=7), INVALID),
+    (dict(offsets=None), INVALID),
+    (dict(A=None), INVALID),
+    (dict(quant=2), INVALID),                                        # no scales
+    (dict(quant=5, K=512, scales=(None, None, 1.0)), INVALID),       # no E8M0 scales
+    (dict(K=20), UNSUPPORTED),                                       # 40-byte rows
+    (dict(quant=4, N=100, K=256, scales=(FAKE, FAKE, 1.0)), UNSUPPORTED),
+    (dict(quant=5, K=640, scales=(None, FAKE, 1.0)), UNSUPPORTED),   # K % 256
+    (dict(E=70000), UNSUPPORTED),
+    (dict(offsets=FAKE + 2), UNSUPPORTED),                           # misaligned offsets
+    (dict(C=FAKE + 8), UNSUPPORTED),
+    (dict(M=0), OK),                                                 # no-ops
+    (dict(E=0), OK),
+])
+def test_grouped_argument_errors(cpu_handle, kw, status):
+    assert _raw_grouped(cpu_handle, **kw) == status

@@ -1,0 +1,146 @@
+"""The grouped (mixture-of-experts) layer against the oracle, through the C
+ABI: each expert's segment of rows with its own weight, scales and bias.
+
+Segments of every size class: empty experts, single tokens, segments that
+fill one token tile, that spill into a second chunk and (with a max_rows
+bound below the true size) that one workgroup must loop over.  int8 is
+compared bit-exactly on the raw int32 accumulator; the other modes within
+the relative tolerance.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+lg = pytest.importorskip("epilogue_scaled_gemm_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(x):
+    if x is None:
+        return None
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        x = x.view(np.int16)
+    return torch.from_numpy(x).cuda()
+
+
+def stack(arrs):
+    return None if arrs is None or arrs[0] is None else np.ascontiguousarray(np.stack(arrs))
+
+
+def run(h, g, act=None, raw=False, max_rows=0, alpha=1.0):
+    M, N = g["M"], g["N"]
+    dt = torch.int32 if (raw and g["quant"] == "w8a8_int8") else (
+        torch.float32 if raw else torch.int16)
+    C = torch.full((M, N), -1, dtype=dt, device="cuda")
+    h.run_grouped(dev(g["A"]), dev(stack(g["Bs"])), C, dev(g["offsets"]), quant=g["quant"],
+                  act="raw_acc" if raw else (act or g["act"]), sa=dev(g["sa"]),
+                  sb=dev(stack(g["sbs"])), alpha=alpha, bias=dev(stack(g["biases"])),
+                  residual=dev(g["residual"]), max_rows=max_rows)
+    torch.cuda.synchronize()
+    return C.cpu()
+
+
+def bf16(C, quant):
+    t = C.view(torch.float16 if quant == "fp16" else torch.bfloat16)
+    return t.double().numpy()
+
+
+SIZES = {
+    "mixed": [3, 0, 1, 16, 0, 17, 5, 2],
+    "tiny": [1, 1, 0, 1],
+    "wide": [40, 0, 7, 33],
+}
+
+
+@pytest.fixture(scope="module")
+def h():
+    with lg.Handle() as hh:
+        yield hh
+
+
+@pytest.mark.parametrize("quant,act,N,K", [
+    ("bf16", "gelu_tanh", 64, 256),
+    ("fp16", "silu", 48, 128),
+    ("fp8_dynamic", "silu", 96, 512),
+    ("block_fp8", "none", 256, 384),
+    ("mxfp4", "gelu_tanh", 80, 512),
+])
+@pytest.mark.parametrize("sizes", ["mixed", "tiny", "wide"])
+@pytest.mark.parametrize("xs", [0, 1])
+def test_grouped_matches_oracle(h, quant, act, N, K, sizes, xs):
+    g = synth.make_grouped(quant, act, SIZES[sizes], N, K, seed=zlib.crc32(f"{quant}/{sizes}".encode()) % 1000,
+                           residual=True)
+    h.set_force(f"decode xs={xs}")
+    try:
+        got = bf16(run(h, g, alpha=0.75), quant)
+    finally:
+        h.set_force(None)
+    ref, _ = oracle.grouped_linear(quant, act, g["A"], g["Bs"], g["offsets"], sa=g["sa"],
+                                   sbs=g["sbs"], biases=g["biases"], residual=g["residual"],
+                                   alpha=0.75)
+    ok = oracle.within_tolerance(got, ref)
+    assert ok.all(), f"{(~ok).sum()} of {ok.size} outside tolerance"
+
+
+@pytest.mark.parametrize("sizes", ["mixed", "wide"])
+@pytest.mark.parametrize("xs", [0, 1])
+@pytest.mark.parametrize("max_rows", [0, 1, 16, 33])
+def test_grouped_int8_accumulator_bit_exact(h, sizes, xs, max_rows):
+    g = synth.make_grouped("w8a8_int8", "silu", SIZES[sizes], 112, 640, seed=5)
+    h.set_force(f"decode xs={xs}")
+    try:
+        acc = run(h, g, raw=True, max_rows=max_rows).numpy()
+        out = bf16(run(h, g, max_rows=max_rows), "w8a8_int8")
+    finally:
+        h.set_force(None)
+    ref, racc = oracle.grouped_linear("w8a8_int8", "silu", g["A"], g["Bs"], g["offsets"],
+                                      sa=g["sa"], sbs=g["sbs"], biases=g["biases"])
+    assert np.array_equal(acc, racc)
+    assert oracle.within_tolerance(out, ref).all()
+
+
+def test_grouped_uncovered_rows_untouched_and_bad_offsets_clamped(h):
+    # offsets not starting at 0, an end beyond M and a decreasing last pair:
+    # clamped into [0, M] ([2,6), [6,M), empty); rows outside every segment
+    # keep their contents.
+    g = synth.make_grouped("fp8_dynamic", "none", [4, 4, 4], 32, 256, seed=9)
+    M = g["M"]
+    off = np.array([2, 6, 1000, 3], dtype=np.int32)
+    C = torch.full((M, 32), 0x1234, dtype=torch.int16, device="cuda")
+    h.run_grouped(dev(g["A"]), dev(stack(g["Bs"])), C, dev(off), quant="fp8_dynamic",
+                  sa=dev(g["sa"]), sb=dev(stack(g["sbs"])), bias=dev(stack(g["biases"])))
+    torch.cuda.synchronize()
+    got = bf16(C.cpu(), "fp8_dynamic")
+    eff = np.array([2, 6, M, M], dtype=np.int32)
+    ref, _ = oracle.grouped_linear("fp8_dynamic", "none", g["A"], g["Bs"], eff, sa=g["sa"],
+                                   sbs=g["sbs"], biases=g["biases"])
+    assert (C.cpu()[:2] == 0x1234).all()
+    assert oracle.within_tolerance(got[2:], ref[2:]).all()
+
+
+def test_grouped_matches_per_expert_dense_calls(h):
+    # The grouped call gives the same bits as lin_gemm_run on each segment
+    # with the same variant family (staged fp8, one token tile).
+    g = synth.make_grouped("fp8_dynamic", "gelu_tanh", [5, 9, 0, 16], 192, 1024, seed=4)
+    grp = run(h, g, max_rows=16)
+    off = g["offsets"]
+    for x in range(4):
+        m0, m1 = off[x], off[x + 1]
+        if m1 == m0:
+            continue
+        C = torch.empty((m1 - m0, 192), dtype=torch.int16, device="cuda")
+        h.set_force("decode swap=1 split=1 waves=8 unroll=2 rows=16 xs=1")
+        try:
+            h.run(dev(g["A"][m0:m1]), dev(g["Bs"][x]), C, quant="fp8_dynamic", act="gelu_tanh",
+                  sa=dev(g["sa"][m0:m1]), sb=dev(g["sbs"][x]), bias=dev(g["biases"][x]))
+        finally:
+            h.set_force(None)
+        torch.cuda.synchronize()
+        assert torch.equal(C.cpu(), grp[m0:m1])
