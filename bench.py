@@ -285,6 +285,75 @@ def dynamic_quant_rows(torch, h, reps):
     return rows
 
 
+def moe_rows(torch, h, reps, ncopy=16):
+    """Mixture-of-experts decode (synth.MOE): one grouped call per routing,
+    beside the same routing run as one lin_gemm_run per expert with rows.
+    Each of the `ncopy` replays of a graph uses its own routing and its own
+    copy of the expert weights, so no replay finds its experts in the
+    last-level cache.  The row bound passed is the token count (experts are
+    distinct per token, so no expert gets more rows than there are tokens).  Eight distinct expert weights are drawn and repeated
+    over the 128 experts (the bytes streamed, not their values, set the
+    time)."""
+    import synth
+    c = synth.MOE
+    E, N, K, quant = c["E"], c["N"], c["K"], c["quant"]
+    g8 = synth.make_grouped(quant, c["act"], [0] * 8, N, K, seed=77, bias=False)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    B8, sb8 = dev(np.stack(g8["Bs"])), dev(np.stack(g8["sbs"]))
+    Bs = [B8.repeat(E // 8, 1, 1).contiguous() for _ in range(ncopy)]
+    sbs = [sb8.repeat(E // 8, 1).contiguous() for _ in range(ncopy)]
+    rows = []
+    for T in c["Ts"]:
+        M = T * c["topk"]
+        routes = []
+        for r in range(ncopy):
+            sizes = synth.moe_routing(T, E, c["topk"], seed=1000 * T + r)
+            off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+            rng = np.random.Generator(np.random.PCG64(r))
+            A, sa = synth.encode(quant, rng.standard_normal((M, K), dtype=np.float32), "a")
+            d = dict(sizes=sizes, off=off, offd=dev(off), A=dev(A), sa=dev(sa),
+                     C=torch.empty((M, N), dtype=torch.int16, device="cuda"))
+            # per-expert scale slices in their own (aligned) buffers
+            d["sa_seg"] = {x: dev(sa[off[x]:off[x + 1]]) for x in range(E) if sizes[x]}
+            routes.append(d)
+
+        def grouped(r):
+            d = routes[r]
+            h.run_grouped(d["A"], Bs[r], d["C"], d["offd"], quant=quant, act=c["act"],
+                          sa=d["sa"], sb=sbs[r], max_rows=T)
+
+        def loop(r):
+            d = routes[r]
+            for x, sa_x in d["sa_seg"].items():
+                m0, m1 = int(d["off"][x]), int(d["off"][x + 1])
+                h.run(d["A"][m0:m1], Bs[r][x], d["C"][m0:m1], quant=quant, act=c["act"],
+                      sa=sa_x, sb=sbs[r][x])
+
+        graphs = []
+        for fn in (grouped, loop):
+            for r in range(ncopy):
+                fn(r)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for r in range(ncopy):
+                    fn(r)
+            graphs.append(g)
+        tg, tl = time_graphs(torch, graphs, max(3, reps))
+        nbytes = int(np.mean([synth.moe_bytes(quant, d["sizes"], N, K) for d in routes]))
+        active = float(np.mean([np.count_nonzero(d["sizes"]) for d in routes]))
+        row = shape_row(c["name"], quant, M, N, K, tg / ncopy, nbytes, 2 * M * N * K,
+                        f"grouped decode, {E} experts top-{c['topk']}")
+        row.update(tokens=T, active_experts=active, us_per_expert_loop=round(tl / ncopy * 1e6, 3),
+                   loop_kernels_per_call=active)
+        rows.append(row)
+        print(f"[shape] {row}", file=sys.stderr, flush=True)
+        del graphs, routes
+    del Bs, sbs
+    torch.cuda.empty_cache()
+    return rows
+
+
 def unfused_graph(torch, h, wl, M):
     """A HIP graph of the three-kernel path on the prefill problem (GEMM -> T,
     bias+GELU -> U, 0.5*U + residual -> C) over the weight rotation."""
@@ -444,7 +513,8 @@ def main():
 
     shapes = None
     if not args.no_shapes:
-        shapes = per_shape_table(torch, h, args.reps) + dynamic_quant_rows(torch, h, args.reps)
+        shapes = (per_shape_table(torch, h, args.reps) + dynamic_quant_rows(torch, h, args.reps)
+                  + moe_rows(torch, h, args.reps))
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
     out = {

@@ -529,14 +529,34 @@ int lin_gemm_run_grouped(lin_gemm_t h, const void* A, const void* B, const lin_s
   c.KB = b_row_bytes(quant_mode, K);
   c.qk = qkind(quant_mode);
   c.epi = make_epi(scales, bias, residual, C, M, N, quant_mode, activation);
+  // Token tiles and grid depth from the mean rows per expert (M / E, the
+  // typical segment) capped by the caller's bound: two 16-token tiles only
+  // when segments of more than 16 rows are the rule (a workgroup loops over
+  // the chunks of a longer-than-usual segment, re-reading its weight slice
+  // from the cache), and the grid as deep as a typical segment's chunks.
   const int64_t bound = (max_rows == 0 || max_rows > M) ? M : max_rows;
-  const int ntt = bound <= 16 ? 1 : 2;
-  const int chunks = (int)std::min<int64_t>((bound + 16 * ntt - 1) / (16 * ntt), 65535);
-  // Staged activations where the variant exists, unless a forced variant
-  // says otherwise.
-  bool xs = h->forced ? h->force.xs != 0 : true;
-  xs = xs && lg::grouped_xs_supported(c.qk, ntt, c.KB);
-  hipError_t e = lg::launch_grouped(c, offsets, E, ntt, chunks, xs, (hipStream_t)stream);
+  const int64_t mean = std::min(bound, (M + E - 1) / E);
+  const int ntt = mean <= 16 ? 1 : 2;
+  const int chunks = (int)std::min<int64_t>((mean + 16 * ntt - 1) / (16 * ntt), 65535);
+  // A forced decode variant picks the grouped variant: its waves, unroll
+  // and rows where that grouped variant is compiled, else the default with
+  // its staging choice (staging dropped where the mode has none).
+  // Unforced: the default of the mode, every lane loading its own
+  // activations (staging measured no faster on decode-sized segments).
+  lg::Variant v;
+  v.waves = 0;
+  v.xs = 0;
+  if (h->forced) {
+    if (h->force.kind != lg::V_DECODE || h->force.swap != 1)
+      return fail(h, LIN_ERR_UNSUPPORTED, "grouped calls use swap-orientation decode variants");
+    v = h->force;
+    if (!lg::grouped_supported(v, c.qk, ntt, c.KB)) v.waves = 0;
+  }
+  if (!lg::grouped_supported(v, c.qk, ntt, c.KB)) {
+    v.waves = 0;
+    v.xs = 0;
+  }
+  hipError_t e = lg::launch_grouped(v, c, offsets, E, ntt, chunks, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(h, e, "grouped kernel launch");
   return LIN_OK;
 }

@@ -36,6 +36,7 @@
 //    it; exact for int32, order-dependent rounding for fp32) or twopass
 //    (partials, then splitk_reduce sums them in slice order).  The nonlinear
 //    epilogue always runs on the complete sum.
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 #include <unordered_map>
@@ -648,29 +649,68 @@ __global__ __launch_bounds__((W + (op_wave(SWAP, W) ? 1 : 0)) * 64) void decode_
                                            steps_per_split, reduce, e, ws, counters);
 }
 
+// The k-th expert (in expert order) whose segment [offsets[x], offsets[x+1])
+// is non-empty, with the segment clamped into [0, M] (an end below its
+// start is empty); x = -1 if there are at most k.  Each wave computes it
+// alone (no LDS, no barrier): 64 experts per ballot, the offsets of four
+// ballots loaded at once.
+__device__ inline void kth_segment(const int* __restrict__ offsets, int E, int M, int k, int& x,
+                                   int& lo, int& hi) {
+  const int lane = threadIdx.x & 63;
+  x = -1; lo = 0; hi = 0;
+  for (int base = 0; base < E; base += 256) {
+    int l[4], h[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = base + 64 * j + lane;
+      const bool in = i < E;
+      const int a = in ? offsets[i] : 0, b = in ? offsets[i + 1] : 0;
+      l[j] = min(max(a, 0), M);
+      h[j] = min(max(b, l[j]), M);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ne = h[j] > l[j];
+      const uint64_t bits = __ballot(ne);
+      const int cnt = __popcll(bits);
+      if (k < cnt) {
+        const int below = (int)__builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(bits >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0u));
+        const int src = __ffsll((unsigned long long)__ballot(ne && below == k)) - 1;
+        x = __builtin_amdgcn_readfirstlane(base + 64 * j + src);
+        lo = __builtin_amdgcn_readfirstlane(__shfl(l[j], src));
+        hi = __builtin_amdgcn_readfirstlane(__shfl(h[j], src));
+        return;
+      }
+      k -= cnt;
+    }
+  }
+}
+
 // Grouped form (a mixture-of-experts layer, tokens sorted by expert):
-// expert x = blockIdx.y owns rows [offsets[x], offsets[x+1]) of A, the
-// residual and C, and its own weight B[x] (N rows of KB bytes) with its
-// weight scales and bias.  The expert's rows go through the decode body in
-// chunks of 16 NTT tokens (swap orientation, no split-K: the experts
-// already give the grid its width), chunk c on workgroup z = c mod
-// gridDim.z, so any segment length is covered whatever the grid's depth;
-// an expert without rows costs its workgroups two scalar loads.  Offsets
-// are clamped into [0, M] and an end below its start is an empty segment:
-// a malformed offset array gives wrong rows, never an access outside A, C
-// or the residual.
+// expert x owns rows [offsets[x], offsets[x+1]) of A, the residual and C,
+// and its own weight B[x] (N rows of KB bytes) with its weight scales and
+// bias.  Workgroup row y = blockIdx.y serves the y-th expert that has rows,
+// so min(E, M) rows of workgroups cover every case and experts without rows
+// cost nothing.  The expert's rows go through the decode body in chunks of
+// 16 NTT tokens (swap orientation, no split-K: the experts already give the
+// grid its width), chunk c on workgroup z = c mod gridDim.z, so any segment
+// length is covered whatever the grid's depth.  Offsets are clamped into
+// [0, M] and an end below its start is an empty segment: a malformed offset
+// array gives wrong rows, never an access outside A, C or the residual.
 template <int QK, int NTT, int W, int U, int RT, int AM>
 __global__ __launch_bounds__((W + (op_wave(true, W) ? 1 : 0)) * 64) void grouped_decode_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
-    const int* __restrict__ offsets, int64_t M, int64_t N, int64_t KB, int rpw, int steps,
-    Epi e) {
+    const int* __restrict__ offsets, int E, int64_t M, int64_t N, int64_t KB, int rpw,
+    int steps, Epi e) {
   constexpr bool MX = QK == QK_MXFP4;
   constexpr bool BLOCK = QK == QK_FP8_BLOCK;
   constexpr int64_t XR = MX ? 4 : 1;
   constexpr int64_t MT = 16 * NTT;
-  const int64_t x = blockIdx.y;
-  const int64_t lo = min(max((int64_t)offsets[x], (int64_t)0), M);
-  const int64_t hi = min(max((int64_t)offsets[x + 1], lo), M);
+  int xi, loi, hii;
+  kth_segment(offsets, E, (int)M, (int)blockIdx.y, xi, loi, hii);
+  if (xi < 0) return;
+  const int64_t x = xi, lo = loi, hi = hii;
   const int64_t first = lo + (int64_t)blockIdx.z * MT;
   if (first >= hi) return;
   // The expert's weight, weight scales ([N] per channel, [N/128][KB/128]
@@ -954,21 +994,30 @@ hipError_t launch_decode_dq(const Variant& v, const Call& c, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-// Grouped (mixture-of-experts) variants: per quant mode and token tiles
-// (one: chunks of up to 16 tokens, two: up to 32), one variant with
-// activations loaded by each lane and, for the 8-bit and 4-bit weights, one
-// with activations staged through LDS.
+// Grouped (mixture-of-experts) variants, by quant mode and token tiles (one:
+// chunks of up to 16 tokens, two: up to 32), with activations loaded by each
+// lane (AM_GLOBAL) or staged through LDS (AM_STAGE; 8-bit and 4-bit
+// weights).  The first entry of a (mode, tiles, staging) triple is its
+// default: four waves, two steps per batch, 32 weight rows per workgroup --
+// an expert's weight is short in K, and fewer waves each streaming longer
+// runs beat the dense decode's eight (measured on a 128-expert top-8 layer,
+// N = 1536, K = 2048).  The rest are alternatives for forced variants and
+// the sweep.
+#define LG_GROUPED_MODE(X, Q)                                                            \
+  X(Q, 1, 4, 2, 2, AM_GLOBAL) X(Q, 2, 4, 2, 2, AM_GLOBAL)                                \
+  X(Q, 1, 8, 2, 1, AM_GLOBAL) X(Q, 2, 8, 1, 2, AM_GLOBAL)
+#define LG_GROUPED_STAGE(X, Q) X(Q, 1, 4, 2, 2, AM_STAGE) X(Q, 2, 4, 2, 2, AM_STAGE)
 #define LG_GROUPED(X)                                                                    \
-  X(QK_BF16, 1, 8, 2, 1, AM_GLOBAL) X(QK_BF16, 2, 8, 1, 2, AM_GLOBAL)                    \
-  X(QK_FP16, 1, 8, 2, 1, AM_GLOBAL) X(QK_FP16, 2, 8, 1, 2, AM_GLOBAL)                    \
-  X(QK_FP8, 1, 8, 2, 1, AM_GLOBAL) X(QK_FP8, 2, 8, 1, 2, AM_GLOBAL)                      \
+  LG_GROUPED_MODE(X, QK_BF16) LG_GROUPED_MODE(X, QK_FP16) LG_GROUPED_MODE(X, QK_FP8)       \
+  LG_GROUPED_MODE(X, QK_I8) LG_GROUPED_MODE(X, QK_FP8_BLOCK) LG_GROUPED_MODE(X, QK_MXFP4)  \
+  LG_GROUPED_STAGE(X, QK_FP8) LG_GROUPED_STAGE(X, QK_I8) LG_GROUPED_STAGE(X, QK_FP8_BLOCK)  \
+  LG_GROUPED_STAGE(X, QK_MXFP4)                                                          \
   X(QK_FP8, 1, 8, 2, 1, AM_STAGE) X(QK_FP8, 2, 8, 1, 2, AM_STAGE)                        \
-  X(QK_I8, 1, 8, 2, 1, AM_GLOBAL) X(QK_I8, 2, 8, 1, 2, AM_GLOBAL)                        \
-  X(QK_I8, 1, 8, 2, 1, AM_STAGE) X(QK_I8, 2, 4, 2, 2, AM_STAGE)                          \
-  X(QK_FP8_BLOCK, 1, 8, 2, 1, AM_GLOBAL) X(QK_FP8_BLOCK, 2, 8, 1, 2, AM_GLOBAL)          \
-  X(QK_FP8_BLOCK, 1, 8, 1, 1, AM_STAGE) X(QK_FP8_BLOCK, 2, 8, 2, 2, AM_STAGE)            \
-  X(QK_MXFP4, 1, 8, 2, 1, AM_GLOBAL) X(QK_MXFP4, 2, 8, 1, 2, AM_GLOBAL)                  \
-  X(QK_MXFP4, 1, 8, 2, 1, AM_STAGE) X(QK_MXFP4, 2, 4, 2, 2, AM_STAGE)
+  X(QK_I8, 1, 8, 2, 1, AM_STAGE) X(QK_FP8_BLOCK, 1, 8, 1, 1, AM_STAGE)                   \
+  X(QK_MXFP4, 1, 8, 2, 1, AM_STAGE)                                                      \
+  X(QK_FP8, 1, 4, 4, 1, AM_GLOBAL) X(QK_FP8, 1, 4, 1, 4, AM_GLOBAL)                      \
+  X(QK_FP8, 2, 4, 1, 4, AM_GLOBAL) X(QK_FP8, 1, 8, 2, 2, AM_GLOBAL)                      \
+  X(QK_FP8, 2, 8, 2, 2, AM_GLOBAL) X(QK_FP8, 1, 8, 1, 4, AM_GLOBAL)
 
 namespace {
 // The grouped variant for (qk, ntt, staged), its kernel and its LDS need.
@@ -976,10 +1025,13 @@ struct GroupedPick {
   const void* fn = nullptr;
   int w = 0, u = 0, rt = 0;
 };
-GroupedPick grouped_pick(int qk, int ntt, bool xs) {
+// w == 0: the default of (qk, ntt, xs); else the entry with waves w,
+// unroll u and rt 16-row tiles, if compiled.
+GroupedPick grouped_pick(int qk, int ntt, bool xs, int w, int u, int rt) {
   GroupedPick p;
 #define LG_G_FN(q_, nt, w_, u_, rt_, am)                                             \
-  if (!p.fn && qk == q_ && ntt == nt && xs == (am == AM_STAGE)) {                   \
+  if (!p.fn && qk == q_ && ntt == nt && xs == (am == AM_STAGE) &&                   \
+      (w == 0 || (w == w_ && u == u_ && rt == rt_))) {                              \
     p.fn = reinterpret_cast<const void*>(&grouped_decode_kernel<q_, nt, w_, u_, rt_, am>); \
     p.w = w_; p.u = u_; p.rt = rt_;                                                 \
   }
@@ -989,31 +1041,37 @@ GroupedPick grouped_pick(int qk, int ntt, bool xs) {
 }
 }  // namespace
 
-bool grouped_xs_supported(int qk, int ntt, int64_t KB) {
-  const GroupedPick p = grouped_pick(qk, ntt, true);
+bool grouped_supported(const Variant& v, int qk, int ntt, int64_t KB) {
+  const int w = v.waves, rt = w ? tiles_for(v.rows) : 0;
+  if (w && (v.rows < 4 || v.rows > 64 || v.rows % 4 != 0)) return false;
+  if (w && qk == QK_FP8_BLOCK && 128 % v.rows != 0) return false;
+  const GroupedPick p = grouped_pick(qk, ntt, v.xs != 0, w, v.unroll, rt);
   if (!p.fn) return false;
+  if (!v.xs) return true;
   Call c{};
   c.qk = qk; c.M = 16 * ntt; c.KB = KB;
   return lds_fits(p.fn, xs_lds_bytes(qk, p.w, p.u, c));
 }
 
-hipError_t launch_grouped(const Call& c, const int* offsets, int64_t E, int ntt, int chunks,
-                          bool xs, hipStream_t s) {
-  const GroupedPick p = grouped_pick(c.qk, ntt, xs);
+hipError_t launch_grouped(const Variant& v, const Call& c, const int* offsets, int64_t E,
+                          int ntt, int chunks, hipStream_t s) {
+  const bool xs = v.xs != 0;
+  const int w = v.waves, rt = w ? tiles_for(v.rows) : 0;
+  const GroupedPick p = grouped_pick(c.qk, ntt, xs, w, v.unroll, rt);
   if (!p.fn || E < 1 || E > 65535 || chunks < 1 || chunks > 65535) return hipErrorInvalidValue;
-  const int rows = 16 * p.rt;
+  const int rows = w ? v.rows : 16 * p.rt;
   const int64_t groups = (c.N + rows - 1) / rows;
   const int steps = (int)((c.KB + STEPB - 1) / STEPB);
   Call cm = c;
   cm.M = 16 * ntt;  // staging holds one chunk
   const size_t dyn = xs ? xs_lds_bytes(c.qk, p.w, p.u, cm) : 0;
-  const dim3 grid((unsigned)groups, (unsigned)E, (unsigned)chunks);
+  const dim3 grid((unsigned)groups, (unsigned)std::min<int64_t>(E, c.M), (unsigned)chunks);
 #define LG_G_TRY(q_, nt, w_, u_, rt_, am)                                               \
-  if (c.qk == q_ && ntt == nt && xs == (am == AM_STAGE)) {                            \
+  if (p.fn == reinterpret_cast<const void*>(&grouped_decode_kernel<q_, nt, w_, u_, rt_, am>)) { \
     hipLaunchKernelGGL((grouped_decode_kernel<q_, nt, w_, u_, rt_, am>), grid,         \
                        dim3((w_ + (op_wave(true, w_) ? 1 : 0)) * 64), dyn, s,           \
-                       (const uint8_t*)c.A, (const uint8_t*)c.B, offsets, c.M, c.N, c.KB, \
-                       rows, steps, c.epi);                                             \
+                       (const uint8_t*)c.A, (const uint8_t*)c.B, offsets, (int)E, c.M, c.N, \
+                       c.KB, rows, steps, c.epi);                                       \
     return hipGetLastError();                                                         \
   }
   LG_GROUPED(LG_G_TRY)

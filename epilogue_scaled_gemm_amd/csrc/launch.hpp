@@ -80,11 +80,13 @@ hipError_t launch_decode_dq(const Variant& v, const Call& c, hipStream_t s);
 // rows [offsets[x], offsets[x+1]) of the [M] rows of c.A / C / residual, the
 // weight c.B + x N KB and its scales and bias (per-expert strides of N
 // rows); token chunks of 16 ntt rows (ntt 1 or 2), `chunks` workgroups deep
-// per expert and weight-row group.  xs: activations staged through LDS
-// (grouped_xs_supported first).
-bool grouped_xs_supported(int qk, int ntt, int64_t KB);
-hipError_t launch_grouped(const Call& c, const int* offsets, int64_t E, int ntt, int chunks,
-                          bool xs, hipStream_t s);
+// per expert and weight-row group.  Variant: waves == 0 takes the default
+// of (quant, ntt, xs); otherwise waves / unroll / rows pick a compiled
+// grouped variant.  v.xs: activations staged through LDS.  Check
+// grouped_supported first.
+bool grouped_supported(const Variant& v, int qk, int ntt, int64_t KB);
+hipError_t launch_grouped(const Variant& v, const Call& c, const int* offsets, int64_t E,
+                          int ntt, int chunks, hipStream_t s);
 // Second pass of a two-pass split-K reduction: sums the fp32 / int32 slices
 // [split][M][N] in slice order and applies the epilogue.
 hipError_t launch_splitk_reduce(int qk, const void* ws, int split, const Epi& e, hipStream_t s);

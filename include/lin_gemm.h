@@ -225,13 +225,15 @@ int lin_gemm_run_dynamic(lin_gemm_t h, const void *X, int x_dtype, const void *B
  *             array gives wrong rows but no out-of-bounds access; rows no
  *             segment covers are left unwritten.
  * max_rows is an upper bound on any expert's row count that the caller
- * knows (0 = M).  It sizes the grid only: rows run in chunks of up to 16
- * (max_rows <= 16) or 32 tokens, each chunk streaming its expert's weight,
- * and a workgroup takes every gridDim-th chunk of its expert, so a bound
- * below the true count still gives the right result (more slowly).  The
- * kernels are the decode family (swap orientation, no split-K), meant for
- * decode-sized segments: a long segment streams the expert's weight once
- * per chunk.  Requirements: those of lin_gemm_run for N and K per mode
+ * knows (0 = M; for top-k routing over distinct experts, the token count).
+ * It only shapes the launch: rows run in chunks of up to 16 tokens (32 when
+ * min(max_rows, ceil(M / E)) > 16), each chunk streaming its expert's
+ * weight, the grid holds min(E, M) rows of workgroups, each serving one
+ * expert that has rows, and as many chunk slots as a segment of
+ * min(max_rows, ceil(M / E)) rows needs; a workgroup loops over the
+ * further chunks of a longer segment, so any segment lengths give the right
+ * result.  The kernels are the decode family (swap orientation, no
+ * split-K), meant for decode-sized segments.  Requirements: those of lin_gemm_run for N and K per mode
  * (MXFP4: K % 256 == 0; no limit on M), E <= 65535, M < 2^31.  E == 0 or
  * M == 0 is a no-op.  No allocation; enqueued on `stream`. */
 int lin_gemm_run_grouped(lin_gemm_t h, const void *A, const void *B, const lin_scales_t *scales,

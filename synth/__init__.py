@@ -47,6 +47,33 @@ WORKLOADS = {
             Ms=(1, 2, 4, 8, 16, 24, 32), bias=True, residual=False, alpha=1.0, dist="normal"),
 }
 
+# Mixture-of-experts decode: 128 experts, each token routed to 8 distinct
+# experts drawn uniformly (seeded), hidden size K = 2048, expert width 768
+# with the gate and up projections stacked (N = 1536); FP8 dynamic scaling
+# as workload 2; T tokens give 8 T routed rows.
+MOE = dict(name="fp8_moe_decode", quant="fp8_dynamic", act="none", E=128, topk=8, N=1536,
+           K=2048, Ts=(1, 4, 16, 32))
+
+
+def moe_routing(T: int, E: int, topk: int, seed: int) -> np.ndarray:
+    """Rows per expert when each of T tokens picks `topk` distinct experts
+    uniformly at random."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    picks = np.concatenate([rng.permutation(E)[:topk] for _ in range(T)]) if T else \
+        np.zeros(0, np.int64)
+    return np.bincount(picks, minlength=E).astype(np.int64)
+
+
+def moe_bytes(quant: str, sizes, N: int, K: int) -> int:
+    """Compulsory HBM bytes of one grouped call: each expert with rows
+    streams its weight and weight scales once; every routed row reads its
+    activation row and scale and writes its output row; the offsets."""
+    sizes = np.asarray(sizes)
+    M = int(sizes.sum())
+    active = int(np.count_nonzero(sizes))
+    return (algorithmic_bytes(quant, M, N, K, False, False) - N * K - 4 * N
+            + active * (N * K + 4 * N) + 4 * (len(sizes) + 1))
+
 
 @dataclass
 class Problem:

@@ -2,8 +2,9 @@
 ABI: each expert's segment of rows with its own weight, scales and bias.
 
 Segments of every size class: empty experts, single tokens, segments that
-fill one token tile, that spill into a second chunk and (with a max_rows
-bound below the true size) that one workgroup must loop over.  int8 is
+fill one token tile, that spill into a second chunk, that one workgroup
+loops over (a max_rows bound, or a mean segment, below the true size) and
+that spread over a grid several chunks deep.  int8 is
 compared bit-exactly on the raw int32 accumulator; the other modes within
 the relative tolerance.
 """
@@ -56,7 +57,14 @@ SIZES = {
     "mixed": [3, 0, 1, 16, 0, 17, 5, 2],
     "tiny": [1, 1, 0, 1],
     "wide": [40, 0, 7, 33],
+    "deep": [70, 50],   # two 16-token tiles, two chunk slots, three chunks in the first
 }
+
+
+# The default grouped variant (no force), its staged form, and the
+# eight-wave alternative, staged and not.
+SPECS = ["", "decode swap=1 waves=4 unroll=2 rows=32 xs=1",
+         "decode swap=1 waves=8 unroll=2 rows=16 xs=0", "decode swap=1 waves=8 unroll=2 rows=16 xs=1"]
 
 
 @pytest.fixture(scope="module")
@@ -72,12 +80,12 @@ def h():
     ("block_fp8", "none", 256, 384),
     ("mxfp4", "gelu_tanh", 80, 512),
 ])
-@pytest.mark.parametrize("sizes", ["mixed", "tiny", "wide"])
-@pytest.mark.parametrize("xs", [0, 1])
-def test_grouped_matches_oracle(h, quant, act, N, K, sizes, xs):
-    g = synth.make_grouped(quant, act, SIZES[sizes], N, K, seed=zlib.crc32(f"{quant}/{sizes}".encode()) % 1000,
-                           residual=True)
-    h.set_force(f"decode xs={xs}")
+@pytest.mark.parametrize("sizes", ["mixed", "tiny", "wide", "deep"])
+@pytest.mark.parametrize("spec", SPECS)
+def test_grouped_matches_oracle(h, quant, act, N, K, sizes, spec):
+    g = synth.make_grouped(quant, act, SIZES[sizes], N, K,
+                           seed=zlib.crc32(f"{quant}/{sizes}".encode()) % 1000, residual=True)
+    h.set_force(spec)
     try:
         got = bf16(run(h, g, alpha=0.75), quant)
     finally:
@@ -89,12 +97,12 @@ def test_grouped_matches_oracle(h, quant, act, N, K, sizes, xs):
     assert ok.all(), f"{(~ok).sum()} of {ok.size} outside tolerance"
 
 
-@pytest.mark.parametrize("sizes", ["mixed", "wide"])
-@pytest.mark.parametrize("xs", [0, 1])
+@pytest.mark.parametrize("sizes", ["mixed", "wide", "deep"])
+@pytest.mark.parametrize("spec", SPECS)
 @pytest.mark.parametrize("max_rows", [0, 1, 16, 33])
-def test_grouped_int8_accumulator_bit_exact(h, sizes, xs, max_rows):
+def test_grouped_int8_accumulator_bit_exact(h, sizes, spec, max_rows):
     g = synth.make_grouped("w8a8_int8", "silu", SIZES[sizes], 112, 640, seed=5)
-    h.set_force(f"decode xs={xs}")
+    h.set_force(spec)
     try:
         acc = run(h, g, raw=True, max_rows=max_rows).numpy()
         out = bf16(run(h, g, max_rows=max_rows), "w8a8_int8")
@@ -127,7 +135,7 @@ def test_grouped_uncovered_rows_untouched_and_bad_offsets_clamped(h):
 
 def test_grouped_matches_per_expert_dense_calls(h):
     # The grouped call gives the same bits as lin_gemm_run on each segment
-    # with the same variant family (staged fp8, one token tile).
+    # with the same variant (four waves, 32 rows, one token tile).
     g = synth.make_grouped("fp8_dynamic", "gelu_tanh", [5, 9, 0, 16], 192, 1024, seed=4)
     grp = run(h, g, max_rows=16)
     off = g["offsets"]
@@ -136,7 +144,7 @@ def test_grouped_matches_per_expert_dense_calls(h):
         if m1 == m0:
             continue
         C = torch.empty((m1 - m0, 192), dtype=torch.int16, device="cuda")
-        h.set_force("decode swap=1 split=1 waves=8 unroll=2 rows=16 xs=1")
+        h.set_force("decode swap=1 split=1 waves=4 unroll=2 rows=32")
         try:
             h.run(dev(g["A"][m0:m1]), dev(g["Bs"][x]), C, quant="fp8_dynamic", act="gelu_tanh",
                   sa=dev(g["sa"][m0:m1]), sb=dev(g["sbs"][x]), bias=dev(g["biases"][x]))
