@@ -83,8 +83,8 @@ int check_shape(lin_gemm_t h, int quant, int64_t M, int64_t N, int64_t K) {
                                         "(K % 8 for bf16/fp16, K % 16 for e4m3/int8)");
   if (quant == LIN_Q_BLOCK_FP8 && (K % 128 != 0 || N % 128 != 0))
     return fail(h, LIN_ERR_UNSUPPORTED, "block FP8 needs K % 128 == 0 and N % 128 == 0");
-  if (quant == LIN_Q_MXFP4 && (K % 256 != 0 || M > 32))
-    return fail(h, LIN_ERR_UNSUPPORTED, "MXFP4 weights need K % 256 == 0 and M <= 32");
+  if (quant == LIN_Q_MXFP4 && K % 256 != 0)
+    return fail(h, LIN_ERR_UNSUPPORTED, "MXFP4 weights need K % 256 == 0");
   if (quant == LIN_Q_W8A8_INT8 && K > 131071)
     return fail(h, LIN_ERR_UNSUPPORTED, "int8 needs K <= 131071 (int32 accumulator range)");
   if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31 || K > (int64_t)1 << 31)
@@ -105,7 +105,7 @@ int select_variant(lin_gemm_t h, int quant, int64_t M, int64_t N, int64_t K, lg:
     else { d.kind = lg::V_TILE; d.bm = 128; d.bn = 128; d.wm = 2; d.wn = 2; }
     *v = d;
   }
-  if (quant == LIN_Q_MXFP4 && !lg::decode_mx_supported(*v)) {
+  if (quant == LIN_Q_MXFP4 && M <= 32 && !lg::decode_mx_supported(*v)) {
     if (h->forced) return fail(h, LIN_ERR_UNSUPPORTED, "variant not compiled for MXFP4 weights");
     *v = lg::Variant();
     v->kind = lg::V_DECODE;
@@ -126,6 +126,12 @@ int select_variant(lin_gemm_t h, int quant, int64_t M, int64_t N, int64_t K, lg:
                     "pp variants cover bf16, fp16, int8 and block FP8 (split-K for block FP8 only)");
       v->kind = lg::V_TILE; v->bm = 128; v->bn = 128; v->wm = 2; v->wn = 2;
     }
+  }
+  // 4-bit weights take the tile shapes whose weight loads split evenly (32
+  // rows of 32 bytes per load instruction).
+  if (v->kind == lg::V_TILE && !lg::tile_supported(qkind(quant), v->bm, v->bn, v->wm, v->wn)) {
+    if (h->forced) return fail(h, LIN_ERR_UNSUPPORTED, "tile shape not compiled for this mode");
+    v->bm = 128; v->bn = 128; v->wm = 2; v->wn = 2;
   }
   // Block scales are uniform over a decode workgroup's rows only when the
   // rows sit inside one 128-row scale block.

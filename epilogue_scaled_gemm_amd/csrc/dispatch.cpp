@@ -168,6 +168,7 @@ block_fp8      257  *    4096  12288  pp split=0 group=4
 block_fp8      33   256  4096  12288  tile bm=64 bn=64 wm=2 wn=2 group=4
 bf16           1025 *    4096  4096   pp group=4
 bf16           33   256  256   512    tile bm=64 bn=64 wm=2 wn=2 group=4
+mxfp4          33   1024 *     *      tile bm=64 bn=128 wm=1 wn=4 group=4
 # defaults
 *              1    32   *     *      decode swap=1 split=1 reduce=twopass waves=8 unroll=2
 block_fp8      257  *    *     *      pp split=0 group=4

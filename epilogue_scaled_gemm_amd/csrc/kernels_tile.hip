@@ -27,6 +27,14 @@
 //    the operand panels it shares in its own L2.
 //  * Rows past M / N and 16-byte chunks past the end of K read as zero
 //    (buffer bounds); rows past M / N are masked on store.
+//  * MXFP4 weights (4-bit E2M1 codes with an E8M0 scale per 32 K values)
+//    against bf16 activations: a stage is 64 K values, 128 bytes of an
+//    activation row and 32 bytes of a weight row.  Weight rows sit in LDS at
+//    32 bytes each, their two 16-byte halves swapped on every other group of
+//    8 rows, so the 8-byte fragment reads of 16 rows hit distinct banks.
+//    Each lane widens its 8 weights of a k-step times their block scale to
+//    bf16 in registers (exact) and the bf16 MFMA takes them; the scales are
+//    read from memory one stage ahead.
 #include "launch.hpp"
 
 namespace lg {
@@ -34,16 +42,14 @@ namespace {
 
 constexpr int ROWB = 128;  // bytes of K per stage row
 
-template <int BM, int BN, int WM, int WN>
+// RB: bytes of a weight row per stage (128, or 32 for 4-bit weights).
+template <int BM, int BN, int WM, int WN, int RB = ROWB>
 struct TileShape {
   static constexpr int NT = WM * WN * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 16, FN = TN / 16;
-  static constexpr int A_LD = BM * 8 / NT;  // 16-byte chunks per thread per stage
-  static constexpr int B_LD = BN * 8 / NT;
-  static constexpr int STAGE = (BM + BN) * ROWB;
+  static constexpr int STAGE = BM * ROWB + BN * RB;
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
-  static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "load split");
 };
 
 // 16-byte chunk swizzle of LDS row R: chunk c of row R is stored at position
@@ -56,7 +62,12 @@ template <int QK, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int64_t M, int64_t N,
     int64_t KB, int tiles_m, int tiles_n, int group_m, Epi e) {
-  using S = TileShape<BM, BN, WM, WN>;
+  // MXFP4: KB is the weight row's bytes (K / 2); activation rows have
+  // XR = 4 times as many bytes (bf16).
+  constexpr bool MX = (QK == QK_MXFP4);
+  constexpr int XR = MX ? 4 : 1;
+  constexpr int RB = MX ? 32 : ROWB;  // weight bytes per row per stage
+  using S = TileShape<BM, BN, WM, WN, RB>;
   using MF = Mfma<QK>;
   using C = typename MF::C;
   using AccT = typename QTraits<QK>::Acc;
@@ -90,11 +101,15 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
   // tile's valid rows, and chunks past the end of K get an out-of-range
   // offset, so both read as zero.
   constexpr int NW = WM * WN;
-  constexpr int A_OCT = BM / 8 / NW, B_OCT = BN / 8 / NW;  // 8-row groups per wave per stage
-  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "direct-load split");
+  // Rows per direct-load instruction: 8 of 128 bytes, or 32 weight rows of
+  // 32 bytes (two lanes per row).
+  constexpr int BG = MX ? 32 : 8;
+  constexpr int A_OCT = BM / 8 / NW, B_OCT = BN / BG / NW;  // instructions per wave per stage
+  static_assert(BM % (8 * NW) == 0 && BN % (BG * NW) == 0, "direct-load split");
+  const int64_t KA = KB * XR;  // bytes of an activation row
   const int a_rows = (int)min((int64_t)BM, M - m0), b_rows = (int)min((int64_t)BN, N - n0);
   const __amdgpu_buffer_rsrc_t rsrc_a =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * KB), (short)0, (int)(a_rows * KB), 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * KA), (short)0, (int)(a_rows * KA), 0x00020000);
   const __amdgpu_buffer_rsrc_t rsrc_b =
       __builtin_amdgcn_make_buffer_rsrc((void*)(B + n0 * KB), (short)0, (int)(b_rows * KB), 0x00020000);
   // Weight rows sit in LDS in the order the fragments read them: within a
@@ -104,29 +119,31 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
   for (int i = 0; i < A_OCT; ++i) {
     const int r = (wave * A_OCT + i) * 8 + (lane >> 3);
     a_chk[i] = ((lane & 7) ^ swz(r)) << 4;
-    a_off[i] = r * (int)KB + a_chk[i];
+    a_off[i] = r * (int)KA + a_chk[i];
   }
 #pragma unroll
   for (int i = 0; i < B_OCT; ++i) {
-    const int R = (wave * B_OCT + i) * 8 + (lane >> 3);  // LDS row in the tile
+    // LDS row in the tile; with 4-bit weights, lane i fills half i % 2 of
+    // row i / 2 with the half that the swap puts there.
+    const int R = (wave * B_OCT + i) * BG + (MX ? (lane >> 1) : (lane >> 3));
     const int sec = R / TN, Rs = R % TN;
     const int r = sec * TN + (Rs % 16) * FN + Rs / 16;    // weight row in the tile
-    b_chk[i] = ((lane & 7) ^ swz(R)) << 4;
+    b_chk[i] = MX ? (((lane & 1) ^ ((R >> 3) & 1)) << 4) : (((lane & 7) ^ swz(R)) << 4);
     b_off[i] = r * (int)KB + b_chk[i];
   }
   typedef __attribute__((address_space(3))) void lds_void;
   auto dload = [&](int kt, int buf) {
     uint8_t* base = lds + buf * S::STAGE;
-    const int koff = kt * ROWB;
+    const int koff = kt * ROWB, kboff = kt * RB;
 #pragma unroll
     for (int i = 0; i < A_OCT; ++i) {
-      const int off = (koff + a_chk[i] < KB) ? a_off[i] + koff : 0x7FFFFFF0;
+      const int off = (koff + a_chk[i] < KA) ? a_off[i] + koff : 0x7FFFFFF0;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_void*)(base + (wave * A_OCT + i) * 1024),
                                                16, off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < B_OCT; ++i) {
-      const int off = (koff + b_chk[i] < KB) ? b_off[i] + koff : 0x7FFFFFF0;
+      const int off = (kboff + b_chk[i] < KB) ? b_off[i] + kboff : 0x7FFFFFF0;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b,
                                                (lds_void*)(base + BM * ROWB + (wave * B_OCT + i) * 1024),
                                                16, off, 0, 0, 0);
@@ -148,6 +165,31 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
   auto w_frag16 = [&](const uint8_t* base, int j, int ch) {
     const int r = fw_row[j];
     return *(const i32x4*)(base + BM * ROWB + r * ROWB + ((ch ^ swz(r)) << 4));
+  };
+  // 4-bit weights: this lane's 8 bytes of the stage (16 K values, k-steps 0
+  // and 1 of its lane group: bytes 8 g .. 8 g + 8 of the 32-byte row).
+  auto w_frag_mx = [&](const uint8_t* base, int j) {
+    const int r = fw_row[j];
+    return *(const i32x2*)(base + BM * ROWB + r * RB + ((((g >> 1) ^ ((r >> 3) & 1))) << 4) +
+                           (g & 1) * 8);
+  };
+  // E8M0 scales [N][KB / 16] of this lane's weight rows; a stage spans two
+  // 32-value blocks and lane group g's values sit in block g / 2.  Rows past
+  // N read the last row (their outputs are never stored).
+  const uint8_t* msp[MX ? FN : 1];
+  if constexpr (MX) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = min(n0 + wave_n * TN + l16 * FN + j, N - 1);
+      msp[j] = (const uint8_t*)e.sb + n * (KB / 16) + (g >> 1);
+    }
+  }
+  uint32_t msc_cur[MX ? FN : 1], msc_nxt[MX ? FN : 1];
+  auto mload = [&](int kt, uint32_t* o) {
+    if constexpr (MX) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) o[j] = msp[j][kt * 2];
+    }
   };
 
   // Block scales: sb is uniform over a wave's columns, sa varies per lane.
@@ -183,9 +225,10 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = C{0, 0, 0, 0};
 
-  const int KT = (int)((KB + ROWB - 1) / ROWB);
+  const int KT = (int)((KB + RB - 1) / RB);
   dload(0, 0);
   sload(0, sa_cur, sb_cur);
+  mload(0, msc_cur);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
@@ -193,8 +236,29 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
     if (kt + 1 < KT) {
       dload(kt + 1, (kt + 1) & 1);
       sload(kt + 1, sa_nxt, sb_nxt);
+      mload(kt + 1, msc_nxt);
     }
-    if constexpr (!BLOCK) {
+    if constexpr (MX) {
+      i32x2 wr[FN];
+      float wsc[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        wr[j] = w_frag_mx(base, j);
+        wsc[j] = e8m0_to_f32(msc_cur[j]);
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        typename MF::Frag wf[FN], af[FM];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) wf[j] = mx_widen8((uint32_t)wr[j][s], wsc[j]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[i] = MF::prep(a_frag16(base, i, 2 * g + s));
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = MF::mma(wf[j], af[i], acc[i][j]);
+      }
+    } else if constexpr (!BLOCK) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         typename MF::Frag wf[FN], af[FM];
@@ -237,6 +301,10 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
       for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i];
       sb_cur = sb_nxt;
     }
+    if constexpr (MX) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) msc_cur[j] = msc_nxt[j];
+    }
     __syncthreads();
   }
 
@@ -260,7 +328,7 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
 
 template <int QK, int BM, int BN, int WM, int WN>
 hipError_t launch_t(const Variant& v, const Call& c, hipStream_t s) {
-  using S = TileShape<BM, BN, WM, WN>;
+  using S = TileShape<BM, BN, WM, WN, QK == QK_MXFP4 ? 32 : ROWB>;
   const int tiles_m = (int)((c.M + BM - 1) / BM);
   const int tiles_n = (int)((c.N + BN - 1) / BN);
   const size_t lds = 2 * (size_t)S::STAGE;
@@ -290,10 +358,17 @@ hipError_t launch_t(const Variant& v, const Call& c, hipStream_t s) {
   X(256, 128, 2, 4)       \
   X(128, 128, 2, 4)
 
+// 4-bit weights load 32 weight rows per instruction: BN must be a multiple
+// of 32 times the wave count.
+constexpr bool mx_shape_ok(int bn, int wm, int wn) { return bn % (32 * wm * wn) == 0; }
+
 template <int QK>
 hipError_t launch_q(const Variant& v, const Call& c, hipStream_t s) {
-#define LG_TRY(b_m, b_n, w_m, w_n) \
-  if (v.bm == b_m && v.bn == b_n && v.wm == w_m && v.wn == w_n) return launch_t<QK, b_m, b_n, w_m, w_n>(v, c, s);
+#define LG_TRY(b_m, b_n, w_m, w_n)                                          \
+  if constexpr (QK != QK_MXFP4 || mx_shape_ok(b_n, w_m, w_n)) {              \
+    if (v.bm == b_m && v.bn == b_n && v.wm == w_m && v.wn == w_n)           \
+      return launch_t<QK, b_m, b_n, w_m, w_n>(v, c, s);                     \
+  }
   LG_TILE_SHAPES(LG_TRY)
 #undef LG_TRY
   return hipErrorInvalidValue;
@@ -302,9 +377,8 @@ hipError_t launch_q(const Variant& v, const Call& c, hipStream_t s) {
 }  // namespace
 
 bool tile_supported(int qk, int bm, int bn, int wm, int wn) {
-  (void)qk;
 #define LG_HAS(b_m, b_n, w_m, w_n) \
-  if (bm == b_m && bn == b_n && wm == w_m && wn == w_n) return true;
+  if (bm == b_m && bn == b_n && wm == w_m && wn == w_n) return qk != QK_MXFP4 || mx_shape_ok(bn, wm, wn);
   LG_TILE_SHAPES(LG_HAS)
 #undef LG_HAS
   return false;
@@ -317,6 +391,7 @@ hipError_t launch_tile(const Variant& v, const Call& c, hipStream_t s) {
     case QK_FP8: return launch_q<QK_FP8>(v, c, s);
     case QK_I8: return launch_q<QK_I8>(v, c, s);
     case QK_FP8_BLOCK: return launch_q<QK_FP8_BLOCK>(v, c, s);
+    case QK_MXFP4: return launch_q<QK_MXFP4>(v, c, s);
   }
   return hipErrorInvalidValue;
 }

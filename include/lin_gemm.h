@@ -46,9 +46,9 @@
  * bf16 [M][K]; B is [N][K/2] bytes, two E2M1 codes per byte, the even K
  * index in the low nibble; scales->b points to E8M0 bytes [N][K/32] (one
  * power-of-two scale 2^(e-127) per 32 consecutive K values of a row, codes
- * 1..254) and scales->a is unused.  Decode shapes only (M <= 32), K % 256 ==
- * 0.  C = act(sum_k A[m,k] * e2m1(B[n,k]) * 2^(e[n,k/32]-127) + bias) *
- * alpha + residual, in bf16.
+ * 1..254) and scales->a is unused.  K % 256 == 0; any M (decode kernels up
+ * to 32 tokens, tile kernels beyond).  C = act(sum_k A[m,k] * e2m1(B[n,k]) *
+ * 2^(e[n,k/32]-127) + bias) * alpha + residual, in bf16.
  *
  * Streams and errors.  lin_gemm_run enqueues on `stream` (a hipStream_t;
  * NULL = the null stream) and returns without waiting.  The status it

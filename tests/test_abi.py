@@ -209,7 +209,7 @@ def test_run_dynamic_shape_errors(cpu_handle):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(quant=5, K=640, scales=(None, FAKE, 1.0)), UNSUPPORTED),   # K % 256
-    (dict(quant=5, M=33, K=512, scales=(None, FAKE, 1.0)), UNSUPPORTED),
+    (dict(quant=5, M=33, K=512, scales=(None, FAKE + 4, 1.0)), UNSUPPORTED),  # misaligned
     (dict(quant=5, K=512, scales=(None, None, 1.0)), INVALID),       # no E8M0 scales
     (dict(quant=5, M=0, K=512, scales=(None, FAKE, 1.0)), OK),
 ])
@@ -220,6 +220,13 @@ def test_mxfp4_argument_errors(cpu_handle, kw, status):
 def test_mxfp4_describe(cpu_handle):
     v = cpu_handle.describe("mxfp4", 8, 6144, 4096)
     assert v.startswith("decode swap=1")
+    for M in (33, 300, 4096):  # tile shapes whose weight loads split evenly
+        v = dict(kv.split("=") for kv in cpu_handle.describe("mxfp4", M, 6144, 4096).split()[1:])
+        assert int(v["bn"]) % (32 * int(v["wm"]) * int(v["wn"])) == 0, v
+    cpu_handle.set_force("tile bm=64 bn=64 wm=2 wn=2")
+    with pytest.raises(lg.LinGemmError):
+        cpu_handle.describe("mxfp4", 64, 6144, 4096)
+    cpu_handle.set_force(None)
     cpu_handle.set_force("decode swap=1 split=1 reduce=twopass waves=4 unroll=4 rows=16")
     with pytest.raises(lg.LinGemmError):
         cpu_handle.describe("mxfp4", 8, 6144, 4096)        # not compiled for MXFP4
