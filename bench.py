@@ -32,8 +32,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12                                     # bytes/s
+# Dense MFMA peaks per operand dtype.  mxfp4 pairs 4-bit weights with bf16
+# activations: no fp4 x fp4 instruction applies, the contraction is bf16.
 MFMA_PEAK = {"bf16": 2.5e15, "fp16": 2.5e15, "fp8_dynamic": 5.0e15, "block_fp8": 5.0e15,
-             "w8a8_int8": 5.0e15, "mxfp4": 10.1e15}   # dense, per operand dtype
+             "w8a8_int8": 5.0e15, "mxfp4": 2.5e15}
 RIDGE = {q: MFMA_PEAK[q] / HBM_PEAK for q in MFMA_PEAK}
 HEAD_CFG = 2
 NCOPY_TARGET_BYTES = 384 << 20                        # rotation footprint > 256 MB MALL
@@ -286,7 +288,7 @@ def dynamic_quant_rows(torch, h, reps):
 
 
 def moe_rows(torch, h, reps, ncopy=16):
-    """Mixture-of-experts decode (synth.MOE): one grouped call per routing,
+    """Mixture-of-experts layer (synth.MOE): one grouped call per routing,
     beside the same routing run as one lin_gemm_run per expert with rows.
     Each of the `ncopy` replays of a graph uses its own routing and its own
     copy of the expert weights, so no replay finds its experts in the
@@ -342,8 +344,9 @@ def moe_rows(torch, h, reps, ncopy=16):
         tg, tl = time_graphs(torch, graphs, max(3, reps))
         nbytes = int(np.mean([synth.moe_bytes(quant, d["sizes"], N, K) for d in routes]))
         active = float(np.mean([np.count_nonzero(d["sizes"]) for d in routes]))
-        row = shape_row(c["name"], quant, M, N, K, tg / ncopy, nbytes, 2 * M * N * K,
-                        f"grouped decode, {E} experts top-{c['topk']}")
+        row = shape_row(f"{c['name']}_{'decode' if T <= 32 else 'prefill'}", quant, M, N, K,
+                        tg / ncopy, nbytes, 2 * M * N * K,
+                        f"grouped, {E} experts top-{c['topk']}")
         row.update(tokens=T, active_experts=active, us_per_expert_loop=round(tl / ncopy * 1e6, 3),
                    loop_kernels_per_call=active)
         rows.append(row)

@@ -259,6 +259,26 @@ struct Epi {
   int64_t M, N;
 };
 
+// The epilogue operands of expert x's rows [r0, r0 + rows) in a grouped
+// (mixture-of-experts) layer: the expert's weight scales ([E][N] per
+// channel, [E][N/128][KB/128] blocks, or [E][N][KB/16] E8M0 bytes) and bias
+// ([E][N]); the rows' activation scales ([M] or [M][KB/128]), residual and
+// output ([M][N]).
+template <int QK>
+__device__ inline Epi grouped_epi(const Epi& e, int64_t x, int64_t r0, int64_t rows, int64_t KB) {
+  Epi ec = e;
+  const int64_t N = e.N;
+  if constexpr (QK == QK_MXFP4) ec.sb = (const float*)((const uint8_t*)e.sb + x * N * (KB / 16));
+  else if constexpr (QK == QK_FP8_BLOCK) ec.sb = e.sb + x * (N / 128) * (KB / 128);
+  else if (e.sb) ec.sb = e.sb + x * N;
+  if (e.bias) ec.bias = e.bias + x * N;
+  if (e.sa) ec.sa = e.sa + r0 * (QK == QK_FP8_BLOCK ? KB / 128 : 1);
+  if (e.residual) ec.residual = e.residual + r0 * N;
+  ec.C = (uint8_t*)e.C + r0 * N * (e.raw ? 4 : 2);
+  ec.M = rows;
+  return ec;
+}
+
 // Load / store G consecutive 16-bit floats (G = 4: 8 bytes, G = 8: 16 bytes).
 template <int G, bool F16> __device__ inline void load_h(const uint16_t* p, float* out) {
   if (G == 8) {

@@ -703,9 +703,7 @@ __global__ __launch_bounds__((W + (op_wave(true, W) ? 1 : 0)) * 64) void grouped
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
     const int* __restrict__ offsets, int E, int64_t M, int64_t N, int64_t KB, int rpw,
     int steps, Epi e) {
-  constexpr bool MX = QK == QK_MXFP4;
-  constexpr bool BLOCK = QK == QK_FP8_BLOCK;
-  constexpr int64_t XR = MX ? 4 : 1;
+  constexpr int64_t XR = QK == QK_MXFP4 ? 4 : 1;
   constexpr int64_t MT = 16 * NTT;
   int xi, loi, hii;
   kth_segment(offsets, E, (int)M, (int)blockIdx.y, xi, loi, hii);
@@ -713,24 +711,13 @@ __global__ __launch_bounds__((W + (op_wave(true, W) ? 1 : 0)) * 64) void grouped
   const int64_t x = xi, lo = loi, hi = hii;
   const int64_t first = lo + (int64_t)blockIdx.z * MT;
   if (first >= hi) return;
-  // The expert's weight, weight scales ([N] per channel, [N/128][KB/128]
-  // blocks, or [N][KB/16] E8M0 bytes) and bias.
   const uint8_t* Bx = B + x * N * KB;
-  Epi ex = e;
-  if constexpr (MX) ex.sb = (const float*)((const uint8_t*)e.sb + x * N * (KB / 16));
-  else if constexpr (BLOCK) ex.sb = e.sb + x * (N / 128) * (KB / 128);
-  else if (e.sb) ex.sb = e.sb + x * N;
-  if (e.bias) ex.bias = e.bias + x * N;
-  const int64_t esz = e.raw ? 4 : 2;
   for (int64_t r0 = first; r0 < hi; r0 += (int64_t)gridDim.z * MT) {
     if (r0 != first) __syncthreads();  // the previous chunk is done with the LDS
-    Epi ec = ex;
-    ec.M = min(MT, hi - r0);
-    if (e.sa) ec.sa = e.sa + r0 * (BLOCK ? KB / 128 : 1);
-    if (e.residual) ec.residual = e.residual + r0 * N;
-    ec.C = (uint8_t*)e.C + r0 * N * esz;
-    decode_body<QK, NTT, true, W, U, RT, AM>(A + r0 * KB * XR, Bx, ec.M, N, KB, rpw, 1, 0,
-                                             steps, R_NONE, ec, nullptr, nullptr);
+    const int64_t rows = min(MT, hi - r0);
+    decode_body<QK, NTT, true, W, U, RT, AM>(A + r0 * KB * XR, Bx, rows, N, KB, rpw, 1, 0,
+                                             steps, R_NONE, grouped_epi<QK>(e, x, r0, rows, KB),
+                                             nullptr, nullptr);
   }
 }
 

@@ -35,6 +35,8 @@
 //    Each lane widens its 8 weights of a k-step times their block scale to
 //    bf16 in registers (exact) and the bf16 MFMA takes them; the scales are
 //    read from memory one stage ahead.
+#include <algorithm>
+
 #include "launch.hpp"
 
 namespace lg {
@@ -58,10 +60,12 @@ struct TileShape {
 // 16-byte bank groups (64 banks x 4 bytes = two 128-byte rows).
 __device__ inline int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
+// The body of the tile kernel: the workgroup computes the BM x BN output tile
+// at (m0, n0).
 template <int QK, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int64_t M, int64_t N,
-    int64_t KB, int tiles_m, int tiles_n, int group_m, Epi e) {
+__device__ __forceinline__ void tile_body(const uint8_t* __restrict__ A,
+                                          const uint8_t* __restrict__ B, int64_t M, int64_t N,
+                                          int64_t KB, int64_t m0, int64_t n0, Epi e) {
   // MXFP4: KB is the weight row's bytes (K / 2); activation rows have
   // XR = 4 times as many bytes (bf16).
   constexpr bool MX = (QK == QK_MXFP4);
@@ -81,18 +85,6 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
   const int wave = tid >> 6;
   const int wave_m = wave % WM, wave_n = wave / WM;
   const int g = lane >> 4, l16 = lane & 15;
-
-  // Tile coordinates: XCD-contiguous remap, then a grouped raster.
-  const int nblk = tiles_m * tiles_n;
-  int L = blockIdx.x;
-  if ((nblk & 7) == 0) L = (L & 7) * (nblk >> 3) + (L >> 3);
-  const int gsz = group_m * tiles_n;
-  const int grp = L / gsz;
-  const int first_m = grp * group_m;
-  const int gm = min(tiles_m - first_m, group_m);
-  const int within = L - grp * gsz;
-  const int64_t m0 = (int64_t)(first_m + within % gm) * BM;
-  const int64_t n0 = (int64_t)(within / gm) * BN;
 
   // Global -> LDS: buffer loads that write straight into LDS (no staging
   // registers).  One instruction moves 8 rows x 128 bytes: lane i lands at
@@ -327,6 +319,82 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
 }
 
 template <int QK, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int64_t M, int64_t N,
+    int64_t KB, int tiles_m, int tiles_n, int group_m, Epi e) {
+  // Tile coordinates: XCD-contiguous remap, then a grouped raster.
+  const int nblk = tiles_m * tiles_n;
+  int L = blockIdx.x;
+  if ((nblk & 7) == 0) L = (L & 7) * (nblk >> 3) + (L >> 3);
+  const int gsz = group_m * tiles_n;
+  const int grp = L / gsz;
+  const int first_m = grp * group_m;
+  const int gm = min(tiles_m - first_m, group_m);
+  const int within = L - grp * gsz;
+  const int64_t m0 = (int64_t)(first_m + within % gm) * BM;
+  const int64_t n0 = (int64_t)(within / gm) * BN;
+  tile_body<QK, BM, BN, WM, WN>(A, B, M, N, KB, m0, n0, e);
+}
+
+// The t-th BM-row tile of a token-sorted grouped layer, in expert order:
+// expert x's segment [lo, hi) (offsets clamped into [0, M], an end below
+// its start empty) holds tiles ceil((hi - lo) / BM); x = -1 when there are
+// at most t tiles.  Each wave computes it alone: 64 experts at a time, a
+// prefix sum of their tile counts across the lanes, a ballot for the lane
+// whose range holds t.
+__device__ inline void kth_tile(const int* __restrict__ offsets, int E, int M, int bm, int t,
+                                int& x, int& lo, int& hi, int& r0) {
+  const int lane = threadIdx.x & 63;
+  x = -1; lo = 0; hi = 0; r0 = 0;
+  int run = 0;  // tiles of the experts before this group of 64
+  for (int base = 0; base < E; base += 64) {
+    const int i = base + lane;
+    int l = 0, h = 0;
+    if (i < E) {
+      l = min(max(offsets[i], 0), M);
+      h = min(max(offsets[i + 1], l), M);
+    }
+    const int c = (h - l + bm - 1) / bm;
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const int total = __shfl(incl, 63);
+    if (t < run + total) {
+      const bool here = run + incl - c <= t && t < run + incl;
+      const int src = __ffsll((unsigned long long)__ballot(here)) - 1;
+      x = __builtin_amdgcn_readfirstlane(base + src);
+      lo = __builtin_amdgcn_readfirstlane(__shfl(l, src));
+      hi = __builtin_amdgcn_readfirstlane(__shfl(h, src));
+      const int before = __builtin_amdgcn_readfirstlane(__shfl(incl - c, src));
+      r0 = lo + (t - run - before) * bm;
+      return;
+    }
+    run += total;
+  }
+}
+
+// Grouped (mixture-of-experts) form for segments of prefill size: workgroup
+// (blockIdx.x, blockIdx.y) computes n-tile blockIdx.x of the blockIdx.y-th
+// BM-row tile in expert order, against that expert's weight B[x] (N rows of
+// KB bytes), scales and bias.  The grid's y extent is a bound on the tile
+// count (ceil(M / BM) + min(E, M)); workgroups past the last tile return.
+template <int QK, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void grouped_tile_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+    const int* __restrict__ offsets, int E, int64_t M, int64_t N, int64_t KB, Epi e) {
+  constexpr int64_t XR = QK == QK_MXFP4 ? 4 : 1;
+  int x, lo, hi, r0;
+  kth_tile(offsets, E, (int)M, BM, (int)blockIdx.y, x, lo, hi, r0);
+  if (x < 0) return;
+  const int64_t rows = min((int64_t)BM, (int64_t)(hi - r0));
+  tile_body<QK, BM, BN, WM, WN>(A + (int64_t)r0 * KB * XR, B + x * N * KB, rows, N, KB, 0,
+                                (int64_t)blockIdx.x * BN, grouped_epi<QK>(e, x, r0, rows, KB));
+}
+
+template <int QK, int BM, int BN, int WM, int WN>
 hipError_t launch_t(const Variant& v, const Call& c, hipStream_t s) {
   using S = TileShape<BM, BN, WM, WN, QK == QK_MXFP4 ? 32 : ROWB>;
   const int tiles_m = (int)((c.M + BM - 1) / BM);
@@ -374,7 +442,61 @@ hipError_t launch_q(const Variant& v, const Call& c, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// Grouped tile shapes: one per segment-size class.
+#define LG_GROUPED_TILES(X) X(64, 128, 1, 4) X(128, 128, 2, 2) X(256, 256, 2, 4)
+
+template <int QK, int BM, int BN, int WM, int WN>
+hipError_t launch_gt(const Call& c, const int* offsets, int64_t E, hipStream_t s) {
+  using S = TileShape<BM, BN, WM, WN, QK == QK_MXFP4 ? 32 : ROWB>;
+  const size_t lds = 2 * (size_t)S::STAGE;
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t err = hipFuncSetAttribute((const void*)grouped_tile_kernel<QK, BM, BN, WM, WN>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    attr_done = true;
+  }
+  const int64_t tiles_n = (c.N + BN - 1) / BN;
+  const int64_t slots = (c.M + BM - 1) / BM + std::min<int64_t>(E, c.M);
+  if (slots > 65535 || tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((grouped_tile_kernel<QK, BM, BN, WM, WN>), dim3((unsigned)tiles_n, (unsigned)slots),
+                     dim3(S::NT), lds, s, (const uint8_t*)c.A, (const uint8_t*)c.B, offsets, (int)E,
+                     c.M, c.N, c.KB, c.epi);
+  return hipGetLastError();
+}
+
+template <int QK>
+hipError_t launch_gq(const Variant& v, const Call& c, const int* offsets, int64_t E,
+                     hipStream_t s) {
+#define LG_GTRY(b_m, b_n, w_m, w_n)                                         \
+  if (v.bm == b_m && v.bn == b_n && v.wm == w_m && v.wn == w_n)             \
+    return launch_gt<QK, b_m, b_n, w_m, w_n>(c, offsets, E, s);
+  LG_GROUPED_TILES(LG_GTRY)
+#undef LG_GTRY
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+bool grouped_tile_supported(int bm, int bn, int wm, int wn) {
+#define LG_GHAS(b_m, b_n, w_m, w_n) if (bm == b_m && bn == b_n && wm == w_m && wn == w_n) return true;
+  LG_GROUPED_TILES(LG_GHAS)
+#undef LG_GHAS
+  return false;
+}
+
+hipError_t launch_grouped_tile(const Variant& v, const Call& c, const int* offsets, int64_t E,
+                               hipStream_t s) {
+  switch (c.qk) {
+    case QK_BF16: return launch_gq<QK_BF16>(v, c, offsets, E, s);
+    case QK_FP16: return launch_gq<QK_FP16>(v, c, offsets, E, s);
+    case QK_FP8: return launch_gq<QK_FP8>(v, c, offsets, E, s);
+    case QK_I8: return launch_gq<QK_I8>(v, c, offsets, E, s);
+    case QK_FP8_BLOCK: return launch_gq<QK_FP8_BLOCK>(v, c, offsets, E, s);
+    case QK_MXFP4: return launch_gq<QK_MXFP4>(v, c, offsets, E, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 bool tile_supported(int qk, int bm, int bn, int wm, int wn) {
 #define LG_HAS(b_m, b_n, w_m, w_n) \

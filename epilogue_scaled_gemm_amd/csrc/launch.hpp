@@ -50,6 +50,13 @@ struct Call {
 bool tile_supported(int qk, int bm, int bn, int wm, int wn);
 hipError_t launch_tile(const Variant& v, const Call& c, hipStream_t s);
 
+// Grouped tile form (a mixture-of-experts layer with prefill-sized
+// segments): the tile kernel over every BM-row tile of every expert's
+// segment (offsets as in launch_grouped), tile shapes from a short list.
+bool grouped_tile_supported(int bm, int bn, int wm, int wn);
+hipError_t launch_grouped_tile(const Variant& v, const Call& c, const int* offsets, int64_t E,
+                               hipStream_t s);
+
 // Ping-pong family (kernels_pp.hip): bf16 / fp16 / int8 256x256 tiles and
 // block FP8 256x128 tiles with optional split-K over the scale blocks.
 bool pp_supported(int qk);

@@ -226,14 +226,18 @@ int lin_gemm_run_dynamic(lin_gemm_t h, const void *X, int x_dtype, const void *B
  *             segment covers are left unwritten.
  * max_rows is an upper bound on any expert's row count that the caller
  * knows (0 = M; for top-k routing over distinct experts, the token count).
- * It only shapes the launch: rows run in chunks of up to 16 tokens (32 when
- * min(max_rows, ceil(M / E)) > 16), each chunk streaming its expert's
- * weight, the grid holds min(E, M) rows of workgroups, each serving one
- * expert that has rows, and as many chunk slots as a segment of
- * min(max_rows, ceil(M / E)) rows needs; a workgroup loops over the
- * further chunks of a longer segment, so any segment lengths give the right
- * result.  The kernels are the decode family (swap orientation, no
- * split-K), meant for decode-sized segments.  Requirements: those of lin_gemm_run for N and K per mode
+ * It only shapes the launch, through the typical segment length
+ * L = min(max_rows, ceil(M / E)); any segment lengths give the right
+ * result.  L <= 4 (decode): the decode kernels (swap orientation, no
+ * split-K) run rows in chunks of up to 16 tokens (32 when L > 16), each
+ * chunk streaming its expert's weight; the grid holds min(E, M) rows of
+ * workgroups, each serving one expert that has rows, and as many chunk
+ * slots as a segment of L rows needs, and a workgroup loops over the
+ * further chunks of a longer segment; a forced "decode" variant keeps this
+ * path for any L.  L > 4: the tile kernels take every 64-row tile (256 when
+ * L > 256) of every segment; a forced "tile" variant from
+ * lin_gemm_set_force picks 64x128 (1x4 waves), 128x128 (2x2) or 256x256
+ * (2x4).  Requirements: those of lin_gemm_run for N and K per mode
  * (MXFP4: K % 256 == 0; no limit on M), E <= 65535, M < 2^31.  E == 0 or
  * M == 0 is a no-op.  No allocation; enqueued on `stream`. */
 int lin_gemm_run_grouped(lin_gemm_t h, const void *A, const void *B, const lin_scales_t *scales,

@@ -49,12 +49,13 @@ WORKLOADS = {
             Ms=(4096,), bias=True, residual=False, alpha=1.0, dist="normal"),
 }
 
-# Mixture-of-experts decode: 128 experts, each token routed to 8 distinct
+# Mixture-of-experts layer: 128 experts, each token routed to 8 distinct
 # experts drawn uniformly (seeded), hidden size K = 2048, expert width 768
 # with the gate and up projections stacked (N = 1536); FP8 dynamic scaling
-# as workload 2; T tokens give 8 T routed rows.
-MOE = dict(name="fp8_moe_decode", quant="fp8_dynamic", act="none", E=128, topk=8, N=1536,
-           K=2048, Ts=(1, 4, 16, 32))
+# as workload 2; T tokens give 8 T routed rows (decode up to 32 tokens, a
+# 512-token prefill chunk).
+MOE = dict(name="fp8_moe", quant="fp8_dynamic", act="none", E=128, topk=8, N=1536,
+           K=2048, Ts=(1, 4, 16, 32, 512))
 
 
 def moe_routing(T: int, E: int, topk: int, seed: int) -> np.ndarray:

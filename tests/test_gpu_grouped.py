@@ -58,7 +58,16 @@ SIZES = {
     "tiny": [1, 1, 0, 1],
     "wide": [40, 0, 7, 33],
     "deep": [70, 50],   # two 16-token tiles, two chunk slots, three chunks in the first
+    # more than 64 experts (two ballot groups), mostly tiny segments
+    "many": [int(v) for v in np.random.default_rng(8).choice([0, 0, 1, 2, 3], 100)],
 }
+# Prefill-sized segments (mean above 32 rows): the grouped tile kernels.
+PF_SIZES = {
+    "pf_mixed": [100, 0, 37, 300, 5, 64],
+    "pf_many": [int(v) for v in np.random.default_rng(9).choice([0, 33, 47, 80, 129], 70)],
+}
+TILE_SPECS = ["", "tile bm=64 bn=128 wm=1 wn=4", "tile bm=128 bn=128 wm=2 wn=2",
+              "tile bm=256 bn=256 wm=2 wn=4"]
 
 
 # The default grouped variant (no force), its staged form, and the
@@ -80,7 +89,7 @@ def h():
     ("block_fp8", "none", 256, 384),
     ("mxfp4", "gelu_tanh", 80, 512),
 ])
-@pytest.mark.parametrize("sizes", ["mixed", "tiny", "wide", "deep"])
+@pytest.mark.parametrize("sizes", ["mixed", "tiny", "wide", "deep", "many"])
 @pytest.mark.parametrize("spec", SPECS)
 def test_grouped_matches_oracle(h, quant, act, N, K, sizes, spec):
     g = synth.make_grouped(quant, act, SIZES[sizes], N, K,
@@ -137,7 +146,11 @@ def test_grouped_matches_per_expert_dense_calls(h):
     # The grouped call gives the same bits as lin_gemm_run on each segment
     # with the same variant (four waves, 32 rows, one token tile).
     g = synth.make_grouped("fp8_dynamic", "gelu_tanh", [5, 9, 0, 16], 192, 1024, seed=4)
-    grp = run(h, g, max_rows=16)
+    h.set_force("decode swap=1 waves=4 unroll=2 rows=32")
+    try:
+        grp = run(h, g, max_rows=16)
+    finally:
+        h.set_force(None)
     off = g["offsets"]
     for x in range(4):
         m0, m1 = off[x], off[x + 1]
@@ -152,3 +165,51 @@ def test_grouped_matches_per_expert_dense_calls(h):
             h.set_force(None)
         torch.cuda.synchronize()
         assert torch.equal(C.cpu(), grp[m0:m1])
+
+
+@pytest.mark.parametrize("quant,act,N,K", [
+    ("bf16", "gelu_tanh", 200, 256),
+    ("fp16", "none", 128, 136),
+    ("fp8_dynamic", "silu", 264, 512),
+    ("block_fp8", "gelu_tanh", 256, 384),
+    ("mxfp4", "silu", 192, 512),
+])
+@pytest.mark.parametrize("sizes", list(PF_SIZES))
+@pytest.mark.parametrize("spec", TILE_SPECS)
+def test_grouped_prefill_matches_oracle(h, quant, act, N, K, sizes, spec):
+    g = synth.make_grouped(quant, act, PF_SIZES[sizes], N, K,
+                           seed=zlib.crc32(f"pf/{quant}/{sizes}".encode()) % 1000, residual=True)
+    h.set_force(spec)
+    try:
+        got = bf16(run(h, g, alpha=1.5), quant)
+    finally:
+        h.set_force(None)
+    ref, _ = oracle.grouped_linear(quant, act, g["A"], g["Bs"], g["offsets"], sa=g["sa"],
+                                   sbs=g["sbs"], biases=g["biases"], residual=g["residual"],
+                                   alpha=1.5)
+    ok = oracle.within_tolerance(got, ref)
+    assert ok.all(), f"{(~ok).sum()} of {ok.size} outside tolerance"
+
+
+@pytest.mark.parametrize("sizes", list(PF_SIZES))
+@pytest.mark.parametrize("spec", TILE_SPECS)
+def test_grouped_prefill_int8_bit_exact(h, sizes, spec):
+    g = synth.make_grouped("w8a8_int8", "relu", PF_SIZES[sizes], 144, 1040, seed=6)
+    h.set_force(spec)
+    try:
+        acc = run(h, g, raw=True).numpy()
+    finally:
+        h.set_force(None)
+    _, racc = oracle.grouped_linear("w8a8_int8", "relu", g["A"], g["Bs"], g["offsets"],
+                                    sa=g["sa"], sbs=g["sbs"])
+    assert np.array_equal(acc, racc)
+
+
+def test_grouped_prefill_rejects_uncompiled_tile(h):
+    g = synth.make_grouped("bf16", "none", [40, 40], 64, 64, seed=1)
+    h.set_force("tile bm=256 bn=128 wm=2 wn=2")
+    try:
+        with pytest.raises(lg.LinGemmError):
+            run(h, g)
+    finally:
+        h.set_force(None)

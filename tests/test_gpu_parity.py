@@ -108,3 +108,44 @@ def test_e4m3_every_code_through_the_path(handle, spec):
         handle.set_force(None)
     want = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
     assert np.array_equal(C.cpu().numpy(), np.tile(want, (M, 1)))
+
+
+KMAX_I8 = 131056  # the largest K (a multiple of 16) the int8 mode accepts
+
+
+@pytest.mark.parametrize("M,spec", [
+    (2, None),
+    (2, "decode swap=1 split=4 reduce=atomic waves=8 unroll=2 rows=16"),
+    (2, "decode swap=1 split=8 reduce=twopass waves=4 unroll=4 rows=16"),
+    (2, "decode swap=0 split=2 reduce=lastwg waves=8 unroll=2"),
+    (40, "tile bm=64 bn=128 wm=1 wn=4"),
+    (256, "pp group=4"),
+])
+def test_int8_accumulator_at_maximum_k(handle, M, spec):
+    # +-127 codes at the largest K: accumulators reach +-127^2 K = +-2,113,802,224
+    # (just inside int32).  Rows 0 / 1 of A and B are all +127 / all -127,
+    # the rest random signs; raw int32 accumulators compared exactly, on every
+    # output for the small shapes and on sampled outputs for M = 256.
+    N, K = (64 if M < 256 else 256), KMAX_I8
+    rng = np.random.default_rng(M)
+    A = (rng.choice([-127, 127], (M, K))).astype(np.int8)
+    B = (rng.choice([-127, 127], (N, K))).astype(np.int8)
+    A[0], A[1], B[0], B[1] = 127, -127, 127, -127
+    ones_m, ones_n = np.ones(M, np.float32), np.ones(N, np.float32)
+    p = synth.Problem(quant="w8a8_int8", act="none", M=M, N=N, K=K, A=A, B=B, sa=ones_m,
+                      sb=ones_n)
+    print(f"[kmax] M={M} spec={spec}", flush=True)
+    try:
+        handle.set_force(spec)
+        C = run(handle, p, raw=True).cpu().numpy()
+    finally:
+        handle.set_force(None)
+    top = 127 * 127 * K
+    assert C[0, 0] == top and C[1, 1] == top and C[0, 1] == -top
+    if M < 256:
+        _, acc = oracle.linear("w8a8_int8", "none", A, B, ones_m, ones_n)
+        assert np.array_equal(C, acc)
+    else:
+        im, inn = sample_positions(M, N, 300, seed=3)
+        _, acc = oracle.linear_at("w8a8_int8", "none", A, B, im, inn, ones_m, ones_n)
+        assert np.array_equal(C[im, inn], acc)
