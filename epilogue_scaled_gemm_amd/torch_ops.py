@@ -6,6 +6,8 @@
   op traces, exports and captures like a built-in one.
 - ``torch.ops.lingemm.scaled_linear_dynamic``: the same layer on 16-bit
   activations quantized on the fly (lin_gemm_run_dynamic).
+- ``torch.ops.lingemm.scaled_linear_grouped``: the mixture-of-experts form
+  (lin_gemm_run_grouped): token-sorted rows, one weight per expert.
 - ``fuse_linear_epilogues(gm)``: a torch.fx pass that rewrites
   ``linear -> activation [-> * alpha] [-> + residual]`` chains of a traced
   module into single ``scaled_linear`` calls.
@@ -106,6 +108,35 @@ def _scaled_linear_dynamic_fake(x, weight, scale_b, bias=None, residual=None,
                                 quant="fp8_dynamic", act="none", alpha=1.0):
     torch._check(x.shape[-1] == weight.shape[1])
     return x.new_empty((*x.shape[:-1], weight.shape[0]), dtype=torch.bfloat16)
+
+
+@torch.library.custom_op("lingemm::scaled_linear_grouped", mutates_args=())
+def scaled_linear_grouped(x: torch.Tensor, weight: torch.Tensor, offsets: torch.Tensor,
+                          bias: Optional[torch.Tensor] = None,
+                          residual: Optional[torch.Tensor] = None,
+                          scale_a: Optional[torch.Tensor] = None,
+                          scale_b: Optional[torch.Tensor] = None, quant: str = "bf16",
+                          act: str = "none", alpha: float = 1.0, max_rows: int = 0) -> torch.Tensor:
+    """Mixture-of-experts layer: x [M, K] rows sorted by expert, weight
+    [E, N, K] (E, N, K/2 bytes for mxfp4), offsets int32 [E + 1] from 0 to M
+    on the GPU (expert e owns rows offsets[e] .. offsets[e+1]), bias [E, N],
+    residual [M, N], scale_b [E, N] (or the mode's per-expert layout).
+    Returns [M, N]."""
+    M = x.shape[0]
+    N = weight.shape[1]
+    out = torch.empty((M, N), dtype=out_dtype(quant), device=x.device)
+    handle_for(x.device).run_grouped(x.contiguous(), weight.contiguous(), out,
+                                     offsets.contiguous(), quant=quant, act=act, sa=scale_a,
+                                     sb=scale_b, alpha=alpha, bias=bias, residual=residual,
+                                     max_rows=max_rows)
+    return out
+
+
+@scaled_linear_grouped.register_fake
+def _scaled_linear_grouped_fake(x, weight, offsets, bias=None, residual=None, scale_a=None,
+                                scale_b=None, quant="bf16", act="none", alpha=1.0, max_rows=0):
+    torch._check(offsets.shape[0] == weight.shape[0] + 1)
+    return x.new_empty((x.shape[0], weight.shape[1]), dtype=out_dtype(quant))
 
 
 # --------------------------------------------------------------- FX rewrite

@@ -120,3 +120,28 @@ def test_graph_capture_of_decode_path_replays():
         torch.cuda.synchronize()
         for c, e in zip(captured, eager):
             assert torch.equal(c, e), f"replay {rep} differs from eager"
+
+
+@pytest.mark.parametrize("sizes", [[3, 0, 1, 2], [40, 9, 0, 70]])
+def test_grouped_op_matches_oracle(sizes):
+    # Decode-sized and prefill-sized segments through the custom operator.
+    g = synth.make_grouped("fp8_dynamic", "silu", sizes, 96, 512, seed=sum(sizes), residual=True)
+    y = torch.ops.lingemm.scaled_linear_grouped(
+        dev(g["A"]), dev(np.stack(g["Bs"])), dev(g["offsets"]),
+        bias=dev(np.stack(g["biases"])).view(torch.bfloat16),
+        residual=dev(g["residual"]).view(torch.bfloat16), scale_a=dev(g["sa"]),
+        scale_b=dev(np.stack(g["sbs"])), quant="fp8_dynamic", act="silu", alpha=0.5)
+    torch.cuda.synchronize()
+    ref, _ = oracle.grouped_linear("fp8_dynamic", "silu", g["A"], g["Bs"], g["offsets"],
+                                   sa=g["sa"], sbs=g["sbs"], biases=g["biases"],
+                                   residual=g["residual"], alpha=0.5)
+    assert_close(y.float().cpu().numpy(), ref, "scaled_linear_grouped")
+
+
+def test_opcheck_scaled_linear_grouped():
+    g = synth.make_grouped("bf16", "none", [5, 0, 11], 64, 128, seed=3)
+    args = (dev(g["A"]).view(torch.bfloat16), dev(np.stack(g["Bs"])).view(torch.bfloat16),
+            dev(g["offsets"]))
+    torch.library.opcheck(torch.ops.lingemm.scaled_linear_grouped.default, args,
+                          dict(bias=dev(np.stack(g["biases"])).view(torch.bfloat16)),
+                          test_utils=("test_schema", "test_faketensor"))

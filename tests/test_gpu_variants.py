@@ -126,10 +126,13 @@ TILE_PROBLEMS = [
     ("fp8_dynamic", "relu", 200, 300, 400, True, True, 1.0),
     ("w8a8_int8", "silu", 260, 136, 528, False, False, 1.0),
     ("block_fp8", "none", 270, 512, 384, True, True, 1.0),
+    # one and two K stages (pipeline prologue and tail)
+    ("bf16", "none", 70, 136, 64, True, False, 1.0),
+    ("fp16", "relu", 90, 72, 120, False, True, 1.0),
 ]
 
 
-@pytest.mark.parametrize("prob", TILE_PROBLEMS, ids=[p[0] for p in TILE_PROBLEMS])
+@pytest.mark.parametrize("prob", TILE_PROBLEMS, ids=[f"{p[0]}-K{p[4]}" for p in TILE_PROBLEMS])
 def test_tile_shapes_match_oracle(handle, prob):
     q, a, M, N, K, b, r, al = prob
     p = synth.make_custom(q, a, M, N, K, seed=M * 3 + K, bias=b, residual=r, alpha=al)

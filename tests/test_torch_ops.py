@@ -121,3 +121,14 @@ def test_fake_implementation_gives_shape_and_dtype():
     assert y.shape == (3, 5, 32) and y.dtype == torch.bfloat16
     with pytest.raises(Exception):
         torch.ops.lingemm.scaled_linear(x, torch.empty(96, 63, dtype=torch.bfloat16, device="meta"))
+
+
+def test_grouped_fake_implementation():
+    x = torch.empty(40, 64, dtype=torch.bfloat16, device="meta")
+    w = torch.empty(8, 96, 64, dtype=torch.bfloat16, device="meta")
+    off = torch.empty(9, dtype=torch.int32, device="meta")
+    y = torch.ops.lingemm.scaled_linear_grouped(x, w, off, quant="bf16", act="silu")
+    assert y.shape == (40, 96) and y.dtype == torch.bfloat16 and y.device.type == "meta"
+    with pytest.raises(Exception):
+        torch.ops.lingemm.scaled_linear_grouped(x, w, torch.empty(8, dtype=torch.int32,
+                                                                  device="meta"))
