@@ -34,6 +34,10 @@ struct lin_gemm_ctx {
   size_t counters_n = 0;
   void* dq = nullptr;         // staging of lin_gemm_run_dynamic: codes, then scales
   size_t dq_bytes = 0;
+  // Buffers replaced by bigger ones.  They stay allocated until the handle
+  // is destroyed: a graph captured before the growth still holds their
+  // addresses and may be replayed.
+  std::vector<void*> retired;
 };
 
 namespace {
@@ -45,6 +49,14 @@ int fail(lin_gemm_t h, int status, const std::string& msg) {
 
 int hip_fail(lin_gemm_t h, hipError_t e, const char* what) {
   return fail(h, LIN_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Sizes of handle-owned buffers grow in powers of two (at least 1 MiB), so
+// the retired ones add up to less than the live one.
+size_t grow_size(size_t need) {
+  size_t b = (size_t)1 << 20;
+  while (b < need) b <<= 1;
+  return b;
 }
 
 // Bytes per element of A (bf16 activations in the MXFP4 mode).
@@ -150,6 +162,10 @@ int resolve_split(const lg::Variant& v, const lg::Call& c) {
     while (split > 1 && split > blocks) split >>= 1;  // at least one scale block per slice
     return c.qk == lg::QK_FP8_BLOCK ? split : 1;
   }
+  if (v.kind == lg::V_TILE) {
+    int split = v.split > 0 ? v.split : lg::tile_auto_split(v, c);
+    return std::min(split, 16);
+  }
   if (v.kind != lg::V_DECODE) return 1;
   int split = v.split > 0 ? v.split : lg::decode_auto_split(c, v);
   const int64_t steps = (c.KB + 127) / 128;
@@ -161,19 +177,21 @@ int resolve_split(const lg::Variant& v, const lg::Call& c) {
 int ensure_workspace(lin_gemm_t h, const lg::Variant& v, const lg::Call& c, int split,
                      hipStream_t s) {
   const bool pp = v.kind == lg::V_PP;
-  const size_t need = pp ? lg::pp_ws_bytes(c, split) : lg::decode_ws_bytes(v, c, split);
+  const bool dec = v.kind == lg::V_DECODE;
+  const size_t need = pp ? lg::pp_ws_bytes(c, split)
+                         : (dec ? lg::decode_ws_bytes(v, c, split) : lg::tile_ws_bytes(c, split));
   const size_t ncnt = (size_t)((c.N + v.rows - 1) / v.rows);  // one per row group
   const bool grow_ws = need > h->ws_bytes;
-  const bool grow_cnt = !pp && split > 1 && ncnt > h->counters_n;
+  const bool grow_cnt = dec && split > 1 && ncnt > h->counters_n;
   if (grow_ws || grow_cnt) {
     hipError_t e = hipStreamSynchronize(s);  // in-flight calls may still use the old buffers
     if (e != hipSuccess) return hip_fail(h, e, "hipStreamSynchronize");
   }
   if (grow_ws) {
-    if (h->ws) hipFree(h->ws);
+    if (h->ws) h->retired.push_back(h->ws);
     h->ws = nullptr;
     h->ws_bytes = 0;
-    size_t bytes = (need + 255) & ~(size_t)255;
+    size_t bytes = grow_size(need);
     if (hipMalloc(&h->ws, bytes) != hipSuccess) {
       h->ws = nullptr;
       return fail(h, LIN_ERR_OOM, "split-K workspace allocation of " + std::to_string(bytes) + " bytes failed");
@@ -184,10 +202,10 @@ int ensure_workspace(lin_gemm_t h, const lg::Variant& v, const lg::Call& c, int 
     h->ws_zero = true;
   }
   if (grow_cnt) {
-    if (h->counters) hipFree(h->counters);
+    if (h->counters) h->retired.push_back(h->counters);
     h->counters = nullptr;
     h->counters_n = 0;
-    size_t n = (ncnt + 63) & ~(size_t)63;
+    size_t n = grow_size(ncnt * sizeof(int)) / sizeof(int);
     if (hipMalloc(&h->counters, n * sizeof(int)) != hipSuccess) {
       h->counters = nullptr;
       return fail(h, LIN_ERR_OOM, "split-K counter allocation failed");
@@ -196,7 +214,7 @@ int ensure_workspace(lin_gemm_t h, const lg::Variant& v, const lg::Call& c, int 
     hipError_t e = lg::launch_fill_zero(h->counters, n * sizeof(int), s);
     if (e != hipSuccess) return hip_fail(h, e, "counter zero fill");
   }
-  if (split > 1 && !pp) {
+  if (split > 1 && dec) {
     // The atomic reduction needs a zero accumulator; the others leave
     // partials behind, so zero again when switching to atomic.
     if (v.reduce == lg::R_ATOMIC && !h->ws_zero) {
@@ -205,7 +223,7 @@ int ensure_workspace(lin_gemm_t h, const lg::Variant& v, const lg::Call& c, int 
     }
     h->ws_zero = (v.reduce == lg::R_ATOMIC);
   }
-  if (split > 1 && pp) h->ws_zero = false;  // slices overwrite the workspace
+  if (split > 1 && !dec) h->ws_zero = false;  // slices overwrite the workspace
   return LIN_OK;
 }
 
@@ -260,6 +278,7 @@ int lin_gemm_destroy(lin_gemm_t h) {
   if (h->ws) hipFree(h->ws);
   if (h->counters) hipFree(h->counters);
   if (h->dq) hipFree(h->dq);
+  for (void* p : h->retired) hipFree(p);
   delete h;
   return LIN_OK;
 }
@@ -339,7 +358,11 @@ int lin_gemm_run(lin_gemm_t h, const void* A, const void* B, const lin_scales_t*
   if (rc != LIN_OK) return rc;
   hipError_t e;
   if (v.kind == lg::V_TILE) {
-    e = lg::launch_tile(v, c, s);
+    const int split = resolve_split(v, c);
+    rc = ensure_workspace(h, v, c, split, s);
+    if (rc != LIN_OK) return rc;
+    c.ws = h->ws;
+    e = lg::launch_tile(v, c, split, s);
   } else if (v.kind == lg::V_PP) {
     const int split = resolve_split(v, c);
     rc = ensure_workspace(h, v, c, split, s);
@@ -395,7 +418,7 @@ int lin_gemm_run_unfused(lin_gemm_t h, const void* A, const void* B, const void*
     e = lg::launch_pp(v, c, 1, s);
   } else {
     if (v.kind != lg::V_TILE) { v = lg::Variant(); v.kind = lg::V_TILE; }
-    e = lg::launch_tile(v, c, s);
+    e = lg::launch_tile(v, c, 1, s);
   }
   if (e != hipSuccess) return hip_fail(h, e, "GEMM launch");
   e = lg::launch_bias_act(T, bias, U, M, N, activation, f16, s);
@@ -484,10 +507,10 @@ int lin_gemm_run_dynamic(lin_gemm_t h, const void* X, int x_dtype, const void* B
   if (need > h->dq_bytes) {
     hipError_t e = hipStreamSynchronize(s);  // in-flight calls may still read the old staging
     if (e != hipSuccess) return hip_fail(h, e, "hipStreamSynchronize");
-    if (h->dq) hipFree(h->dq);
+    if (h->dq) h->retired.push_back(h->dq);
     h->dq = nullptr;
     h->dq_bytes = 0;
-    const size_t bytes = (need + 255) & ~(size_t)255;
+    const size_t bytes = grow_size(need);
     if (hipMalloc(&h->dq, bytes) != hipSuccess) {
       h->dq = nullptr;
       return fail(h, LIN_ERR_OOM, "staging allocation of " + std::to_string(bytes) + " bytes failed");

@@ -80,8 +80,8 @@ bool parse_variant(const std::string& spec, Variant* out, std::string* err) {
     *err = "tile shape not compiled: " + spec;
     return false;
   }
-  if (v.kind == V_PP && (v.split > 16 || (v.split & (v.split - 1)) != 0)) {
-    *err = "pp split must be 0 (auto) or a power of two <= 16: " + spec;
+  if ((v.kind == V_PP || v.kind == V_TILE) && (v.split > 16 || (v.split & (v.split - 1)) != 0)) {
+    *err = "tile / pp split must be 0 (auto) or a power of two <= 16: " + spec;
     return false;
   }
   if (v.kind == V_DECODE) {
@@ -103,6 +103,7 @@ std::string format_variant(const Variant& v, int split) {
   if (v.kind == V_TILE) {
     os << "tile bm=" << v.bm << " bn=" << v.bn << " wm=" << v.wm << " wn=" << v.wn
        << " group=" << v.group_m;
+    if (split > 1) os << " split=" << split;
   } else if (v.kind == V_PP) {
     os << "pp split=" << split << " group=" << v.group_m;
   } else {

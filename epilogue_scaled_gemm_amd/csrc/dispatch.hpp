@@ -13,6 +13,7 @@
 //   <quant|*> <m_lo> <m_hi|*> <N|*> <K|*> <variant spec>
 // where the variant spec is
 //   tile   bm=<tokens> bn=<weight rows> wm=<waves> wn=<waves> [group=<g>]
+//          [split=<0=auto|1..16>]   (K split across workgroups, two-pass)
 //   pp     [split=<0=auto|1..16>] [group=<g>]   (ping-pong tiles: 256x256 for
 //          bf16 / fp16 / int8, 256x128 for block FP8; split only for block FP8)
 //   decode swap=<0|1> split=<0=auto|1..256> reduce=<lastwg|atomic|twopass>

@@ -897,6 +897,9 @@ hipError_t launch_splitk_reduce(int qk, const void* ws, int split, const Epi& e,
     case QK_FP8_BLOCK:
       hipLaunchKernelGGL((splitk_reduce<QK_FP8_BLOCK>), grid, dim3(256), 0, s, ws, split, e);
       break;
+    case QK_MXFP4:
+      hipLaunchKernelGGL((splitk_reduce<QK_MXFP4>), grid, dim3(256), 0, s, ws, split, e);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

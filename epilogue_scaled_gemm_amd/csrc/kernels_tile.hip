@@ -27,6 +27,11 @@
 //    the operand panels it shares in its own L2.
 //  * Rows past M / N and 16-byte chunks past the end of K read as zero
 //    (buffer bounds); rows past M / N are masked on store.
+//  * Split-K (few output tiles, medium M): workgroup row y of the grid
+//    takes K stages [y * kt_per, (y + 1) * kt_per) and stores its raw fp32 /
+//    int32 tile into slice y of a [split][M][N] workspace; the decode
+//    family's two-pass reduction then sums the slices in order and applies
+//    the epilogue.
 //  * MXFP4 weights (4-bit E2M1 codes with an E8M0 scale per 32 K values)
 //    against bf16 activations: a stage is 64 K values, 128 bytes of an
 //    activation row and 32 bytes of a weight row.  Weight rows sit in LDS at
@@ -61,11 +66,15 @@ struct TileShape {
 __device__ inline int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // The body of the tile kernel: the workgroup computes the BM x BN output tile
-// at (m0, n0).
+// at (m0, n0) over K stages [kt0, kt1) (kt1 = -1: to the end of K); with
+// `part` it stores the raw accumulator tile there ([M][N]) instead of
+// running the epilogue.
 template <int QK, int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void tile_body(const uint8_t* __restrict__ A,
                                           const uint8_t* __restrict__ B, int64_t M, int64_t N,
-                                          int64_t KB, int64_t m0, int64_t n0, Epi e) {
+                                          int64_t KB, int64_t m0, int64_t n0, Epi e,
+                                          int kt0 = 0, int kt1 = -1,
+                                          typename QTraits<QK>::Acc* __restrict__ part = nullptr) {
   // MXFP4: KB is the weight row's bytes (K / 2); activation rows have
   // XR = 4 times as many bytes (bf16).
   constexpr bool MX = (QK == QK_MXFP4);
@@ -217,16 +226,16 @@ __device__ __forceinline__ void tile_body(const uint8_t* __restrict__ A,
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = C{0, 0, 0, 0};
 
-  const int KT = (int)((KB + RB - 1) / RB);
-  dload(0, 0);
-  sload(0, sa_cur, sb_cur);
-  mload(0, msc_cur);
+  const int KT = kt1 < 0 ? (int)((KB + RB - 1) / RB) : kt1;
+  dload(kt0, 0);
+  sload(kt0, sa_cur, sb_cur);
+  mload(kt0, msc_cur);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const uint8_t* base = lds + (kt & 1) * S::STAGE;
+  for (int kt = kt0; kt < KT; ++kt) {
+    const uint8_t* base = lds + ((kt - kt0) & 1) * S::STAGE;
     if (kt + 1 < KT) {
-      dload(kt + 1, (kt + 1) & 1);
+      dload(kt + 1, (kt + 1 - kt0) & 1);
       sload(kt + 1, sa_nxt, sb_nxt);
       mload(kt + 1, msc_nxt);
     }
@@ -300,6 +309,35 @@ __device__ __forceinline__ void tile_body(const uint8_t* __restrict__ A,
     __syncthreads();
   }
 
+  // Split-K slice: the raw tile, 4 FN consecutive columns per lane and row.
+  if (part) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = m0 + fa_row[i];
+      const int64_t nb = n0 + wave_n * TN + g * 4 * FN;
+      if (m >= M) continue;
+      AccT* row = part + m * N + nb;
+      if (nb + 4 * FN <= N && N % 4 == 0) {
+#pragma unroll
+        for (int q = 0; q < FN; ++q) {
+          typedef __attribute__((ext_vector_type(4))) AccT acc4;
+          acc4 w;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int c = 4 * q + t;  // column nb + c holds acc[i][c % FN][c / FN]
+            w[t] = (AccT)acc[i][c % FN][c / FN];
+          }
+          *(acc4*)(row + 4 * q) = w;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4 * FN; ++c)
+          if (nb + c < N) row[c] = (AccT)acc[i][c % FN][c / FN];
+      }
+    }
+    return;
+  }
+
   // Fused epilogue straight from the accumulator registers.
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -321,7 +359,8 @@ __device__ __forceinline__ void tile_body(const uint8_t* __restrict__ A,
 template <int QK, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int64_t M, int64_t N,
-    int64_t KB, int tiles_m, int tiles_n, int group_m, Epi e) {
+    int64_t KB, int tiles_m, int tiles_n, int group_m, Epi e, int split, int kt_per,
+    void* __restrict__ ws) {
   // Tile coordinates: XCD-contiguous remap, then a grouped raster.
   const int nblk = tiles_m * tiles_n;
   int L = blockIdx.x;
@@ -333,7 +372,25 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
   const int within = L - grp * gsz;
   const int64_t m0 = (int64_t)(first_m + within % gm) * BM;
   const int64_t n0 = (int64_t)(within / gm) * BN;
-  tile_body<QK, BM, BN, WM, WN>(A, B, M, N, KB, m0, n0, e);
+  using AccT = typename QTraits<QK>::Acc;
+  int kt0 = 0, kt1 = -1;
+  AccT* part = nullptr;
+  if (split > 1) {
+    constexpr int RB = QK == QK_MXFP4 ? 32 : ROWB;
+    const int KT = (int)((KB + RB - 1) / RB);
+    kt0 = (int)blockIdx.y * kt_per;
+    kt1 = min(kt0 + kt_per, KT);
+    part = (AccT*)ws + (int64_t)blockIdx.y * M * N;
+    if (kt0 >= kt1) {
+      // An empty slice (K shorter than split x kt_per): its partials are zero.
+      for (int64_t t = threadIdx.x; t < (int64_t)BM * BN; t += blockDim.x) {
+        const int64_t m = m0 + t / BN, n = n0 + t % BN;
+        if (m < M && n < N) part[m * N + n] = 0;
+      }
+      return;
+    }
+  }
+  tile_body<QK, BM, BN, WM, WN>(A, B, M, N, KB, m0, n0, e, kt0, kt1, part);
 }
 
 // The t-th BM-row tile of a token-sorted grouped layer, in expert order:
@@ -395,7 +452,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_tile_kernel(
 }
 
 template <int QK, int BM, int BN, int WM, int WN>
-hipError_t launch_t(const Variant& v, const Call& c, hipStream_t s) {
+hipError_t launch_t(const Variant& v, const Call& c, int split, hipStream_t s) {
   using S = TileShape<BM, BN, WM, WN, QK == QK_MXFP4 ? 32 : ROWB>;
   const int tiles_m = (int)((c.M + BM - 1) / BM);
   const int tiles_n = (int)((c.N + BN - 1) / BN);
@@ -408,10 +465,14 @@ hipError_t launch_t(const Variant& v, const Call& c, hipStream_t s) {
     attr_done = true;
   }
   const int group_m = v.group_m > 0 ? v.group_m : 4;
-  hipLaunchKernelGGL((tile_kernel<QK, BM, BN, WM, WN>), dim3(tiles_m * tiles_n), dim3(S::NT),
-                     lds, s, (const uint8_t*)c.A, (const uint8_t*)c.B, c.M, c.N, c.KB, tiles_m,
-                     tiles_n, group_m, c.epi);
-  return hipGetLastError();
+  const int KT = (int)((c.KB + (QK == QK_MXFP4 ? 32 : ROWB) - 1) / (QK == QK_MXFP4 ? 32 : ROWB));
+  const int kt_per = (KT + split - 1) / split;
+  hipLaunchKernelGGL((tile_kernel<QK, BM, BN, WM, WN>), dim3(tiles_m * tiles_n, split),
+                     dim3(S::NT), lds, s, (const uint8_t*)c.A, (const uint8_t*)c.B, c.M, c.N,
+                     c.KB, tiles_m, tiles_n, group_m, c.epi, split, kt_per, c.ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || split == 1) return err;
+  return launch_splitk_reduce(QK, c.ws, split, c.epi, s);
 }
 
 // The compiled tile shapes: (BM, BN, WM, WN).
@@ -431,11 +492,11 @@ hipError_t launch_t(const Variant& v, const Call& c, hipStream_t s) {
 constexpr bool mx_shape_ok(int bn, int wm, int wn) { return bn % (32 * wm * wn) == 0; }
 
 template <int QK>
-hipError_t launch_q(const Variant& v, const Call& c, hipStream_t s) {
+hipError_t launch_q(const Variant& v, const Call& c, int split, hipStream_t s) {
 #define LG_TRY(b_m, b_n, w_m, w_n)                                          \
   if constexpr (QK != QK_MXFP4 || mx_shape_ok(b_n, w_m, w_n)) {              \
     if (v.bm == b_m && v.bn == b_n && v.wm == w_m && v.wn == w_n)           \
-      return launch_t<QK, b_m, b_n, w_m, w_n>(v, c, s);                     \
+      return launch_t<QK, b_m, b_n, w_m, w_n>(v, c, split, s);              \
   }
   LG_TILE_SHAPES(LG_TRY)
 #undef LG_TRY
@@ -506,14 +567,35 @@ bool tile_supported(int qk, int bm, int bn, int wm, int wn) {
   return false;
 }
 
-hipError_t launch_tile(const Variant& v, const Call& c, hipStream_t s) {
+// Split K while the grid has fewer than 512 workgroups, every slice keeps at
+// least 8 K stages, and the partials' round trip (split x M x N x 8 bytes)
+// stays within the weight's bytes (N x KB).  Measured on MI355X (fp8, bf16,
+// block e4m3, MXFP4; N 4096-6144, K 4096-12288): M = 64-128 runs 1.5-3x
+// faster split 2-8 ways; at M = 512 with 8-bit weights splitting loses.
+int tile_auto_split(const Variant& v, const Call& c) {
+  const int64_t tiles = ((c.M + v.bm - 1) / v.bm) * ((c.N + v.bn - 1) / v.bn);
+  const int rb = c.qk == QK_MXFP4 ? 32 : ROWB;
+  const int64_t KT = (c.KB + rb - 1) / rb;
+  int split = 1;
+  while (split < 8 && tiles * split < 512 && KT >= 8 * (int64_t)split * 2 &&
+         (int64_t)split * 2 * c.M * 8 <= c.KB)
+    split *= 2;
+  return split;
+}
+
+size_t tile_ws_bytes(const Call& c, int split) {
+  return split <= 1 ? 0 : (size_t)split * (size_t)c.M * (size_t)c.N * 4;
+}
+
+hipError_t launch_tile(const Variant& v, const Call& c, int split, hipStream_t s) {
+  if (split < 1 || split > 16 || (split > 1 && !c.ws)) return hipErrorInvalidValue;
   switch (c.qk) {
-    case QK_BF16: return launch_q<QK_BF16>(v, c, s);
-    case QK_FP16: return launch_q<QK_FP16>(v, c, s);
-    case QK_FP8: return launch_q<QK_FP8>(v, c, s);
-    case QK_I8: return launch_q<QK_I8>(v, c, s);
-    case QK_FP8_BLOCK: return launch_q<QK_FP8_BLOCK>(v, c, s);
-    case QK_MXFP4: return launch_q<QK_MXFP4>(v, c, s);
+    case QK_BF16: return launch_q<QK_BF16>(v, c, split, s);
+    case QK_FP16: return launch_q<QK_FP16>(v, c, split, s);
+    case QK_FP8: return launch_q<QK_FP8>(v, c, split, s);
+    case QK_I8: return launch_q<QK_I8>(v, c, split, s);
+    case QK_FP8_BLOCK: return launch_q<QK_FP8_BLOCK>(v, c, split, s);
+    case QK_MXFP4: return launch_q<QK_MXFP4>(v, c, split, s);
   }
   return hipErrorInvalidValue;
 }

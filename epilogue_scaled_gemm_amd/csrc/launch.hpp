@@ -46,9 +46,13 @@ struct Call {
   int* counters;    // arrival counters, one per workgroup row group
 };
 
-// Tile family (kernels_tile.hip).
+// Tile family (kernels_tile.hip).  split > 1: K split across workgroups
+// into c.ws ([split][M][N] fp32 / int32, tile_ws_bytes), then the two-pass
+// reduction with the epilogue.
 bool tile_supported(int qk, int bm, int bn, int wm, int wn);
-hipError_t launch_tile(const Variant& v, const Call& c, hipStream_t s);
+int tile_auto_split(const Variant& v, const Call& c);
+size_t tile_ws_bytes(const Call& c, int split);
+hipError_t launch_tile(const Variant& v, const Call& c, int split, hipStream_t s);
 
 // Grouped tile form (a mixture-of-experts layer with prefill-sized
 // segments): the tile kernel over every BM-row tile of every expert's

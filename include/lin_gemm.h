@@ -62,7 +62,9 @@
  * shape-keyed variant table.  Calls that share a handle must not run
  * concurrently on different streams (they share the workspace); use one
  * handle per stream.  Warm each shape up once before capturing calls into a
- * hipGraph, so no allocation happens during capture.
+ * hipGraph, so no allocation happens during capture.  A buffer that grows
+ * is replaced, not freed: the old one stays allocated until
+ * lin_gemm_destroy, so graphs captured before the growth remain valid.
  */
 #ifndef LIN_GEMM_H
 #define LIN_GEMM_H

@@ -96,6 +96,10 @@ def test_mx_tile_shapes_match_oracle(handle, case):
         print(f"[mx] {act} {M}x{N}x{K} {spec}", flush=True)
         C = run(handle, p, spec)
         assert_close(decode_out(C, "mxfp4"), ref, f"mxfp4 {M}x{N}x{K} [{spec}]")
+    for spec in ("tile bm=64 bn=128 wm=1 wn=4 group=4 split=4",
+                 "tile bm=128 bn=128 wm=2 wn=2 group=4 split=2"):
+        C = run(handle, p, spec)
+        assert_close(decode_out(C, "mxfp4"), ref, f"mxfp4 {M}x{N}x{K} [{spec}]")
     C = run(handle, p)  # the table's choice
     assert_close(decode_out(C, "mxfp4"), ref, f"mxfp4 {M}x{N}x{K} [default]")
 

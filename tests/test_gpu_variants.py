@@ -10,7 +10,7 @@ import torch
 
 import synth
 import oracle
-from gpu_util import assert_close, decode_out, reference, run, upload
+from gpu_util import assert_close, decode_out, reference, run, sample_positions, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -119,7 +119,10 @@ TILE_SPECS = ["tile bm=256 bn=256 wm=2 wn=2", "tile bm=128 bn=256 wm=2 wn=2",
               "tile bm=256 bn=128 wm=2 wn=2", "tile bm=128 bn=128 wm=2 wn=2",
               "tile bm=64 bn=128 wm=1 wn=4", "tile bm=64 bn=64 wm=2 wn=2",
               "tile bm=256 bn=256 wm=2 wn=4", "tile bm=256 bn=128 wm=2 wn=4",
-              "tile bm=128 bn=128 wm=2 wn=4"]
+              "tile bm=128 bn=128 wm=2 wn=4",
+              # split-K over workgroups (split 8 leaves empty slices on short K)
+              "tile bm=64 bn=128 wm=1 wn=4 split=2", "tile bm=128 bn=128 wm=2 wn=2 split=4",
+              "tile bm=64 bn=64 wm=2 wn=2 split=8"]
 TILE_PROBLEMS = [
     ("bf16", "gelu_tanh", 300, 520, 264, True, True, 0.5),
     ("fp16", "silu", 130, 264, 200, True, False, 1.0),
@@ -211,3 +214,25 @@ def test_pp_rejects_per_channel_fp8(handle):
             run(handle, p, d)
     finally:
         handle.set_force(None)
+
+
+@pytest.mark.parametrize("quant,M", [("fp8_dynamic", 128), ("w8a8_int8", 200), ("block_fp8", 64),
+                                     ("bf16", 96)])
+def test_tile_auto_split_medium_m(handle, quant, M):
+    # Medium M with few output tiles: the table's tile variant splits K
+    # across workgroups on its own; sampled outputs against the oracle and,
+    # for int8, every raw accumulator.
+    K = 4096 if quant != "block_fp8" else 12288
+    N = 6144 if quant != "block_fp8" else 4096
+    p = synth.make_custom(quant, "silu", M, N, K, seed=M + 1, bias=True, residual=True)
+    v = handle.describe(quant, M, N, K)
+    print(f"[variant] {quant} M={M}: {v}", flush=True)
+    assert v.startswith("tile") and "split=" in v
+    d = upload(p)
+    C = run(handle, p, d)
+    im, inn = sample_positions(M, N, 2000, seed=M)
+    r, _ = reference(p, (im, inn))
+    assert_close(decode_out(C, quant)[im, inn], r, f"{quant} M={M} [{v}]")
+    if quant == "w8a8_int8":
+        _, acc = oracle.linear_at(quant, "none", p.A, p.B, im, inn, p.sa, p.sb)
+        assert np.array_equal(run(handle, p, d, raw=True).cpu().numpy()[im, inn], acc)
