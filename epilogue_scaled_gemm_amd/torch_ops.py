@@ -7,7 +7,8 @@
 - ``torch.ops.lingemm.scaled_linear_dynamic``: the same layer on 16-bit
   activations quantized on the fly (lin_gemm_run_dynamic).
 - ``torch.ops.lingemm.scaled_linear_grouped``: the mixture-of-experts form
-  (lin_gemm_run_grouped): token-sorted rows, one weight per expert.
+  (lin_gemm_run_grouped): token-sorted rows, one weight per expert; and
+  ``scaled_linear_grouped_dynamic`` for 16-bit activations quantized first.
 - ``fuse_linear_epilogues(gm)``: a torch.fx pass that rewrites
   ``linear -> activation [-> * alpha] [-> + residual]`` chains of a traced
   module into single ``scaled_linear`` calls.
@@ -137,6 +138,42 @@ def _scaled_linear_grouped_fake(x, weight, offsets, bias=None, residual=None, sc
                                 scale_b=None, quant="bf16", act="none", alpha=1.0, max_rows=0):
     torch._check(offsets.shape[0] == weight.shape[0] + 1)
     return x.new_empty((x.shape[0], weight.shape[1]), dtype=out_dtype(quant))
+
+
+_DQ_OF = {"fp8_dynamic": ("fp8_token", torch.float8_e4m3fn), "w8a8_int8": ("int8_token", torch.int8),
+          "block_fp8": ("fp8_block", torch.float8_e4m3fn)}
+
+
+@torch.library.custom_op("lingemm::scaled_linear_grouped_dynamic", mutates_args=())
+def scaled_linear_grouped_dynamic(x: torch.Tensor, weight: torch.Tensor, offsets: torch.Tensor,
+                                  scale_b: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                                  residual: Optional[torch.Tensor] = None,
+                                  quant: str = "fp8_dynamic", act: str = "none",
+                                  alpha: float = 1.0, max_rows: int = 0) -> torch.Tensor:
+    """The grouped layer on 16-bit activations x [M, K]: per-token (or 1x128
+    block) quantization (lin_gemm_quantize), then lin_gemm_run_grouped on the
+    codes.  The per-token scales follow their rows, so quantizing before the
+    grouping gives the same codes as quantizing each expert's rows."""
+    kind, code_dtype = _DQ_OF[quant]
+    M, K = x.shape
+    h = handle_for(x.device)
+    q = torch.empty((M, K), dtype=code_dtype, device=x.device)
+    ns = M * (K // 128) if kind == "fp8_block" else M
+    sa = torch.empty(ns, dtype=torch.float32, device=x.device)
+    xc = x.contiguous()
+    h.quantize(xc, q, sa, kind=kind, x_dtype="fp16" if x.dtype == torch.float16 else "bf16")
+    out = torch.empty((M, weight.shape[1]), dtype=torch.bfloat16, device=x.device)
+    h.run_grouped(q, weight.contiguous(), out, offsets.contiguous(), quant=quant, act=act,
+                  sa=sa, sb=scale_b, alpha=alpha, bias=bias, residual=residual,
+                  max_rows=max_rows)
+    return out
+
+
+@scaled_linear_grouped_dynamic.register_fake
+def _scaled_linear_grouped_dynamic_fake(x, weight, offsets, scale_b, bias=None, residual=None,
+                                        quant="fp8_dynamic", act="none", alpha=1.0, max_rows=0):
+    torch._check(offsets.shape[0] == weight.shape[0] + 1)
+    return x.new_empty((x.shape[0], weight.shape[1]), dtype=torch.bfloat16)
 
 
 # --------------------------------------------------------------- FX rewrite

@@ -145,3 +145,22 @@ def test_opcheck_scaled_linear_grouped():
     torch.library.opcheck(torch.ops.lingemm.scaled_linear_grouped.default, args,
                           dict(bias=dev(np.stack(g["biases"])).view(torch.bfloat16)),
                           test_utils=("test_schema", "test_faketensor"))
+
+
+@pytest.mark.parametrize("quant,kind", [("fp8_dynamic", "fp8_token"), ("w8a8_int8", "int8_token"),
+                                        ("block_fp8", "fp8_block")])
+def test_grouped_dynamic_op_matches_oracle(quant, kind):
+    # 16-bit activations quantized per token (or 1x128 block) by the oracle,
+    # then the oracle's grouped layer; against the op that does both on the GPU.
+    sizes = [3, 0, 40, 9]
+    g = synth.make_grouped(quant, "silu", sizes, 128, 256, seed=31)
+    Xh = synth.activations16(int(sum(sizes)), 256, seed=32)
+    Q, S = oracle.dynamic_quant(kind, Xh)
+    ref, _ = oracle.grouped_linear(quant, "silu", Q, g["Bs"], g["offsets"], sa=S,
+                                   sbs=g["sbs"], biases=g["biases"])
+    y = torch.ops.lingemm.scaled_linear_grouped_dynamic(
+        dev(Xh).view(torch.bfloat16), dev(np.stack(g["Bs"])), dev(g["offsets"]),
+        dev(np.stack(g["sbs"])), bias=dev(np.stack(g["biases"])).view(torch.bfloat16),
+        quant=quant, act="silu")
+    torch.cuda.synchronize()
+    assert_close(y.float().cpu().numpy(), ref, f"scaled_linear_grouped_dynamic {quant}")

@@ -132,3 +132,11 @@ def test_grouped_fake_implementation():
     with pytest.raises(Exception):
         torch.ops.lingemm.scaled_linear_grouped(x, w, torch.empty(8, dtype=torch.int32,
                                                                   device="meta"))
+
+
+def test_grouped_dynamic_fake_implementation():
+    x = torch.empty(40, 256, dtype=torch.bfloat16, device="meta")
+    w = torch.empty(4, 96, 256, dtype=torch.float8_e4m3fn, device="meta")
+    off = torch.empty(5, dtype=torch.int32, device="meta")
+    y = torch.ops.lingemm.scaled_linear_grouped_dynamic(x, w, off, torch.empty(4, 96, device="meta"))
+    assert y.shape == (40, 96) and y.dtype == torch.bfloat16
