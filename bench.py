@@ -194,7 +194,7 @@ def shape_row(name, quant, M, N, K, t, nbytes, flops, variant, kernel_calls=1):
 def per_shape_table(torch, h, reps):
     import synth
     rows = []
-    for cfg in (1, 2, 3, 4, 5, 6, 7):
+    for cfg in (1, 2, 3, 4, 5, 6, 7, 8):
         c = synth.WORKLOADS[cfg]
         wl = Workload(torch, cfg, c["Ms"])
         for M in c["Ms"]:

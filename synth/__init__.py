@@ -47,6 +47,8 @@ WORKLOADS = {
             Ms=(1, 2, 4, 8, 16, 24, 32), bias=True, residual=False, alpha=1.0, dist="normal"),
     7: dict(name="mxfp4_prefill", quant="mxfp4", act="none", N=6144, K=4096,
             Ms=(4096,), bias=True, residual=False, alpha=1.0, dist="normal"),
+    8: dict(name="bf16_decode", quant="bf16", act="none", N=6144, K=4096,
+            Ms=(1, 2, 4, 8, 16, 24, 32), bias=True, residual=False, alpha=1.0, dist="normal"),
 }
 
 # Mixture-of-experts layer: 128 experts, each token routed to 8 distinct
