@@ -82,8 +82,8 @@ bool decode_dq_supported(const Variant& v, const Call& c, int split);
 // unroll / tiles from a short list).
 bool decode_mx_supported(const Variant& v);
 // Decode with activations staged through LDS (AM_STAGE): e4m3, int8, block
-// e4m3 and MXFP4 weights, swap, M <= 32, the variants compiled with it, LDS within the
-// device limit.
+// e4m3, MXFP4 and bf16 weights, swap, M <= 32, the variants compiled with
+// it, LDS within the device limit.
 bool decode_xs_supported(const Variant& v, const Call& c);
 hipError_t launch_decode_xs(const Variant& v, const Call& c, int split, hipStream_t s);
 hipError_t launch_decode_dq(const Variant& v, const Call& c, hipStream_t s);

@@ -184,7 +184,7 @@ def sweep(workloads, out_path, reps, log=print, max_m=None, all_m=False, dynamic
             ncopy = max(2, min(32, -(-ROTATION_BYTES // p.B.nbytes)))
             Bs = [ops["B"]] + [ops["B"].clone() for _ in range(ncopy - 1)]
             cands = DECODE_CANDIDATES if M <= 32 else TILE_CANDIDATES
-            if p.quant in ("fp8_dynamic", "mxfp4", "w8a8_int8", "block_fp8"):
+            if p.quant in ("fp8_dynamic", "mxfp4", "w8a8_int8", "block_fp8", "bf16"):
                 cands = cands + XS_CANDIDATES
             # Warm every candidate first (the handle's split-K workspace only
             # grows, so it reaches its final size before any graph is

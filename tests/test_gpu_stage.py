@@ -25,9 +25,12 @@ CASES = [("fp8_dynamic", "none", 1, 1040, 4096, True, False),
          ("mxfp4", "relu", 5, 528, 256, False, True),
          ("mxfp4", "silu", 16, 272, 512, True, False),
          ("w8a8_int8", "silu", 4, 2064, 4096, False, False),
-         ("block_fp8", "none", 3, 512, 3072, False, True)]
+         ("block_fp8", "none", 3, 512, 3072, False, True),
+         ("bf16", "gelu_tanh", 1, 1040, 4096, True, False),
+         ("bf16", "silu", 9, 528, 1032, False, True)]
 I8_SHAPES = [(4, 4, 16), (8, 2, 16), (8, 4, 24)]
 BLOCK_SHAPES = [(12, 1, 16), (8, 1, 16), (16, 1, 16)]
+BF16_SHAPES = [(8, 1, 24), (8, 1, 16), (8, 2, 12)]
 
 
 @pytest.fixture(scope="module")
@@ -55,8 +58,8 @@ def test_staged_activations_match(handle, case):
     p = synth.make_custom(quant, act, M, N, K, seed=3 * M + N + K, bias=b, residual=r)
     ref, _ = oracle.linear(quant, act, p.A, p.B, sa=p.sa, sb=p.sb, bias=p.bias,
                            residual=p.residual, alpha=p.alpha)
-    shapes = {"mxfp4": MX_SHAPES, "w8a8_int8": I8_SHAPES, "block_fp8": BLOCK_SHAPES}.get(
-        quant, FP8_SHAPES)
+    shapes = {"mxfp4": MX_SHAPES, "w8a8_int8": I8_SHAPES, "block_fp8": BLOCK_SHAPES,
+              "bf16": BF16_SHAPES}.get(quant, FP8_SHAPES)
     specs = [f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} rows={rows}"
              for w, u, rows in shapes]
     specs.append("decode swap=1 split=2 reduce=lastwg waves=8 unroll=1 rows=16")
@@ -89,7 +92,8 @@ def test_staged_activations_match(handle, case):
 TWO_TILE = [("fp8_dynamic", "none", 24, 1040, 4096, True, False, [(8, 1, 24), (8, 1, 32), (8, 4, 24)]),
             ("w8a8_int8", "silu", 32, 528, 1024, False, False, [(4, 2, 32)]),
             ("mxfp4", "gelu_tanh", 20, 272, 512, True, True, [(4, 2, 32), (8, 1, 24)]),
-            ("block_fp8", "none", 17, 256, 1024, False, True, [(8, 2, 32)])]
+            ("block_fp8", "none", 17, 256, 1024, False, True, [(8, 2, 32)]),
+            ("bf16", "relu", 30, 272, 1032, True, True, [(8, 1, 24), (8, 1, 32)])]
 
 
 @pytest.mark.parametrize("case", TWO_TILE, ids=[f"{c[0]}-M{c[2]}" for c in TWO_TILE])
