@@ -930,7 +930,7 @@ hipError_t launch_mx(const Variant& v, const Call& c, int split, hipStream_t s) 
 }
 
 // Variants with staged activations (AM_STAGE; swap; one or two token
-// tiles): e4m3, int8, block e4m3, MXFP4 and bf16 weights.
+// tiles): e4m3, int8, block e4m3, MXFP4, bf16 and fp16 weights.
 #define LG_DECODE_XS(X)                                                                \
   X(QK_FP8, 1, 8, 1, 1) X(QK_FP8, 1, 8, 2, 1) X(QK_FP8, 1, 8, 4, 1) X(QK_FP8, 1, 8, 4, 2) \
   X(QK_FP8, 1, 12, 1, 1) X(QK_MXFP4, 1, 8, 1, 1) X(QK_MXFP4, 1, 8, 2, 1)                 \
@@ -939,7 +939,8 @@ hipError_t launch_mx(const Variant& v, const Call& c, int split, hipStream_t s) 
   X(QK_FP8_BLOCK, 1, 16, 1, 1) X(QK_FP8, 2, 8, 1, 2) X(QK_FP8, 2, 8, 4, 2)              \
   X(QK_I8, 2, 4, 2, 2) X(QK_MXFP4, 2, 4, 2, 2) X(QK_MXFP4, 2, 8, 1, 2)                 \
   X(QK_FP8_BLOCK, 2, 8, 2, 2) X(QK_BF16, 1, 8, 1, 2) X(QK_BF16, 1, 8, 1, 1)             \
-  X(QK_BF16, 1, 8, 2, 1) X(QK_BF16, 2, 8, 1, 2)
+  X(QK_BF16, 1, 8, 2, 1) X(QK_BF16, 2, 8, 1, 2) X(QK_FP16, 1, 8, 1, 2)                   \
+  X(QK_FP16, 1, 8, 1, 1) X(QK_FP16, 1, 8, 2, 1) X(QK_FP16, 2, 8, 1, 2)
 
 bool decode_xs_supported(const Variant& v, const Call& c) {
   if (v.kind != V_DECODE || v.swap != 1 || c.M < 1 || c.M > 32) return false;

@@ -82,7 +82,7 @@ bool decode_dq_supported(const Variant& v, const Call& c, int split);
 // unroll / tiles from a short list).
 bool decode_mx_supported(const Variant& v);
 // Decode with activations staged through LDS (AM_STAGE): e4m3, int8, block
-// e4m3, MXFP4 and bf16 weights, swap, M <= 32, the variants compiled with
+// e4m3, MXFP4, bf16 and fp16 weights, swap, M <= 32, the variants compiled with
 // it, LDS within the device limit.
 bool decode_xs_supported(const Variant& v, const Call& c);
 hipError_t launch_decode_xs(const Variant& v, const Call& c, int split, hipStream_t s);

@@ -149,7 +149,7 @@ def merge_ranges(entries):
 
 
 def sweep(workloads, out_path, reps, log=print, max_m=None, all_m=False, dynamic=False,
-          emit_inc=None):
+          emit_inc=None, quant=None):
     import torch
     import synth
     import epilogue_scaled_gemm_amd as lg
@@ -179,12 +179,12 @@ def sweep(workloads, out_path, reps, log=print, max_m=None, all_m=False, dynamic
         for M in ms:
             if max_m is not None and M > max_m:
                 continue
-            p = synth.make(cfg, M)
+            p = synth.make(cfg, M, quant)
             ops = {k: _dev(torch, v) for k, v in p.operands().items() if k != "alpha"}
             ncopy = max(2, min(32, -(-ROTATION_BYTES // p.B.nbytes)))
             Bs = [ops["B"]] + [ops["B"].clone() for _ in range(ncopy - 1)]
             cands = DECODE_CANDIDATES if M <= 32 else TILE_CANDIDATES
-            if p.quant in ("fp8_dynamic", "mxfp4", "w8a8_int8", "block_fp8", "bf16"):
+            if p.quant in ("fp8_dynamic", "mxfp4", "w8a8_int8", "block_fp8", "bf16", "fp16"):
                 cands = cands + XS_CANDIDATES
             # Warm every candidate first (the handle's split-K workspace only
             # grows, so it reaches its final size before any graph is
@@ -277,10 +277,12 @@ def main():
     ap.add_argument("--dynamic", action="store_true",
                     help="choose the quantization prologue (dq=1) where it is faster")
     ap.add_argument("--emit-inc", default=None, help="write the measured entries as C++ include")
+    ap.add_argument("--quant", default=None,
+                    help="run the workloads in this quant mode (same draws), e.g. fp16")
     a = ap.parse_args()
     sweep([int(x) for x in a.workloads.split(",")], a.out, a.reps,
           log=lambda s: print(s, flush=True), max_m=a.max_m, all_m=a.all_m, dynamic=a.dynamic,
-          emit_inc=a.emit_inc)
+          emit_inc=a.emit_inc, quant=a.quant)
 
 
 if __name__ == "__main__":

@@ -27,7 +27,8 @@ CASES = [("fp8_dynamic", "none", 1, 1040, 4096, True, False),
          ("w8a8_int8", "silu", 4, 2064, 4096, False, False),
          ("block_fp8", "none", 3, 512, 3072, False, True),
          ("bf16", "gelu_tanh", 1, 1040, 4096, True, False),
-         ("bf16", "silu", 9, 528, 1032, False, True)]
+         ("bf16", "silu", 9, 528, 1032, False, True),
+         ("fp16", "relu", 5, 272, 520, True, True)]
 I8_SHAPES = [(4, 4, 16), (8, 2, 16), (8, 4, 24)]
 BLOCK_SHAPES = [(12, 1, 16), (8, 1, 16), (16, 1, 16)]
 BF16_SHAPES = [(8, 1, 24), (8, 1, 16), (8, 2, 12)]
@@ -59,7 +60,7 @@ def test_staged_activations_match(handle, case):
     ref, _ = oracle.linear(quant, act, p.A, p.B, sa=p.sa, sb=p.sb, bias=p.bias,
                            residual=p.residual, alpha=p.alpha)
     shapes = {"mxfp4": MX_SHAPES, "w8a8_int8": I8_SHAPES, "block_fp8": BLOCK_SHAPES,
-              "bf16": BF16_SHAPES}.get(quant, FP8_SHAPES)
+              "bf16": BF16_SHAPES, "fp16": BF16_SHAPES}.get(quant, FP8_SHAPES)
     specs = [f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} rows={rows}"
              for w, u, rows in shapes]
     specs.append("decode swap=1 split=2 reduce=lastwg waves=8 unroll=1 rows=16")
