@@ -29,7 +29,7 @@ CASES = [("fp8_dynamic", "none", 1, 1040, 4096, True, False),
          ("bf16", "gelu_tanh", 1, 1040, 4096, True, False),
          ("bf16", "silu", 9, 528, 1032, False, True),
          ("fp16", "relu", 5, 272, 520, True, True)]
-I8_SHAPES = [(4, 4, 16), (8, 2, 16), (8, 4, 24)]
+I8_SHAPES = [(4, 4, 16), (8, 2, 16), (8, 4, 24), (4, 2, 32), (8, 1, 24)]
 BLOCK_SHAPES = [(12, 1, 16), (8, 1, 16), (16, 1, 16)]
 BF16_SHAPES = [(8, 1, 24), (8, 1, 16), (8, 2, 12)]
 
