@@ -941,7 +941,8 @@ hipError_t launch_mx(const Variant& v, const Call& c, int split, hipStream_t s) 
   X(QK_FP8_BLOCK, 2, 8, 2, 2) X(QK_BF16, 1, 8, 1, 2) X(QK_BF16, 1, 8, 1, 1)             \
   X(QK_BF16, 1, 8, 2, 1) X(QK_BF16, 2, 8, 1, 2) X(QK_FP16, 1, 8, 1, 2)                   \
   X(QK_FP16, 1, 8, 1, 1) X(QK_FP16, 1, 8, 2, 1) X(QK_FP16, 2, 8, 1, 2)                   \
-  X(QK_I8, 1, 4, 2, 2) X(QK_I8, 1, 8, 1, 2)
+  X(QK_I8, 1, 4, 2, 2) X(QK_I8, 1, 8, 1, 2) X(QK_FP8_BLOCK, 2, 8, 1, 2)                  \
+  X(QK_FP8_BLOCK, 2, 12, 1, 1) X(QK_FP8_BLOCK, 2, 16, 1, 1) X(QK_FP8_BLOCK, 2, 4, 2, 2)
 
 bool decode_xs_supported(const Variant& v, const Call& c) {
   if (v.kind != V_DECODE || v.swap != 1 || c.M < 1 || c.M > 32) return false;
