@@ -248,3 +248,21 @@ def test_grouped_graph_capture_replays(h, sizes):
         call(eager)
         torch.cuda.synchronize()
         assert torch.equal(C, eager)
+
+
+def test_grouped_many_experts_scan():
+    # 1000 experts: the expert scan runs over several 256-expert groups
+    # (decode path) and the tile scan over many 64-expert groups.
+    sizes = [int(v) for v in np.random.default_rng(12).choice([0, 0, 0, 1, 2], 1000)]
+    g = synth.make_grouped("fp8_dynamic", "none", sizes, 32, 128, seed=13, bias=True)
+    with lg.Handle() as hh:
+        for spec in ("", "tile bm=64 bn=128 wm=1 wn=4"):
+            hh.set_force(spec)
+            try:
+                got = bf16(run(hh, g), "fp8_dynamic")
+            finally:
+                hh.set_force(None)
+            ref, _ = oracle.grouped_linear("fp8_dynamic", "none", g["A"], g["Bs"], g["offsets"],
+                                           sa=g["sa"], sbs=g["sbs"], biases=g["biases"])
+            ok = oracle.within_tolerance(got, ref)
+            assert ok.all(), f"[{spec}] {(~ok).sum()} of {ok.size} outside tolerance"

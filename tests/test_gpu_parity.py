@@ -149,3 +149,15 @@ def test_int8_accumulator_at_maximum_k(handle, M, spec):
         im, inn = sample_positions(M, N, 300, seed=3)
         _, acc = oracle.linear_at("w8a8_int8", "none", A, B, im, inn, ones_m, ones_n)
         assert np.array_equal(C[im, inn], acc)
+
+
+def test_large_m_default_path(handle):
+    # 65536 tokens through the default prefill choice (the ping-pong family,
+    # 256 row tiles of one column tile): sampled outputs, corners and the last
+    # row against the oracle.
+    p = synth.make_custom("bf16", "gelu_tanh", 65536, 256, 64, seed=17, bias=True, residual=True)
+    print(f"[parity] {p.name} variant={handle.describe(p.quant, p.M, p.N, p.K)}", flush=True)
+    C = run(handle, p)
+    im, inn = sample_positions(p.M, p.N, 4000, seed=17)
+    r, _ = reference(p, (im, inn))
+    assert_close(decode_out(C, p.quant)[im, inn], r, p.name)
