@@ -357,6 +357,58 @@ def moe_rows(torch, h, reps, ncopy=16):
     return rows
 
 
+def vendor_rows(torch, reps):
+    """Context, not a target: the same shapes through torch's own bf16 GEMM
+    (hipBLASLt / rocBLAS behind torch.mm / torch.addmm), timed the same
+    way (graph replay over rotating weight copies).  Prefill: the plain GEMM
+    and the GEMM followed by torch's bias / tanh-GELU / x0.5 / residual ops;
+    decode: the bf16 6144 x 4096 layer at M = 1, 8, 32."""
+    import torch.nn.functional as F
+    rows = []
+    gen = torch.Generator(device="cuda").manual_seed(5)
+
+    def timed(fn, ncopy, M, N, K, name, variant, nbytes):
+        fn(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(ncopy):
+                fn(r)
+        t = time_graphs(torch, [g], max(3, reps))[0] / ncopy
+        row = shape_row(name, "bf16", M, N, K, t, nbytes, 2 * M * N * K, variant)
+        print(f"[shape] {row}", file=sys.stderr, flush=True)
+        del g
+        return row
+
+    M = N = K = 4096
+    A = torch.randn(M, K, device="cuda", generator=gen).to(torch.bfloat16)
+    Bw = [torch.randn(N, K, device="cuda", generator=gen).mul_(0.02).to(torch.bfloat16)
+          for _ in range(2)]
+    bias = torch.rand(N, device="cuda", generator=gen).sub_(0.5).to(torch.bfloat16)
+    res = torch.randn(M, N, device="cuda", generator=gen).to(torch.bfloat16)
+    out = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+    rows.append(timed(lambda r: torch.mm(A, Bw[r % 2].t(), out=out), 2, M, N, K,
+                      "vendor_bf16_gemm_4096", "torch.mm", 2 * (M * K + N * K + M * N)))
+    rows.append(timed(lambda r: F.gelu(torch.addmm(bias, A, Bw[r % 2].t(), out=out),
+                                       approximate="tanh").mul_(0.5).add_(res), 2, M, N, K,
+                      "vendor_bf16_prefill_epilogue_4096", "torch.addmm + gelu + mul_ + add_",
+                      2 * (M * K + N * K + N + 2 * M * N)))
+    del A, Bw, res, out
+    N, K, ncopy = 6144, 4096, 8
+    Bw = [torch.randn(N, K, device="cuda", generator=gen).mul_(0.02).to(torch.bfloat16)
+          for _ in range(ncopy)]
+    bias = torch.rand(N, device="cuda", generator=gen).sub_(0.5).to(torch.bfloat16)
+    for M in (1, 8, 32):
+        A = torch.randn(M, K, device="cuda", generator=gen).to(torch.bfloat16)
+        out = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+        rows.append(timed(lambda r: torch.addmm(bias, A, Bw[r].t(), out=out), ncopy, M, N, K,
+                          "vendor_bf16_decode", "torch.addmm",
+                          2 * (M * K + N * K + N + M * N)))
+    del Bw
+    torch.cuda.empty_cache()
+    return rows
+
+
 def unfused_graph(torch, h, wl, M):
     """A HIP graph of the three-kernel path on the prefill problem (GEMM -> T,
     bias+GELU -> U, 0.5*U + residual -> C) over the weight rotation."""
@@ -517,7 +569,7 @@ def main():
     shapes = None
     if not args.no_shapes:
         shapes = (per_shape_table(torch, h, args.reps) + dynamic_quant_rows(torch, h, args.reps)
-                  + moe_rows(torch, h, args.reps))
+                  + moe_rows(torch, h, args.reps) + vendor_rows(torch, args.reps))
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
     out = {
