@@ -154,6 +154,9 @@ def scaled_linear_grouped_dynamic(x: torch.Tensor, weight: torch.Tensor, offsets
     block) quantization (lin_gemm_quantize), then lin_gemm_run_grouped on the
     codes.  The per-token scales follow their rows, so quantizing before the
     grouping gives the same codes as quantizing each expert's rows."""
+    if quant not in _DQ_OF:
+        raise ValueError(f"scaled_linear_grouped_dynamic quantizes for {sorted(_DQ_OF)}, "
+                         f"not {quant!r}")
     kind, code_dtype = _DQ_OF[quant]
     M, K = x.shape
     h = handle_for(x.device)

@@ -239,7 +239,7 @@ int lin_gemm_run_dynamic(lin_gemm_t h, const void *X, int x_dtype, const void *B
  * path for any L.  L > 4: the tile kernels take every 64-row tile (256 when
  * L > 256) of every segment; a forced "tile" variant from
  * lin_gemm_set_force picks 64x128 (1x4 waves), 128x128 (2x2) or 256x256
- * (2x4).  Requirements: those of lin_gemm_run for N and K per mode
+ * (2x4); its split factor is ignored (grouped launches do not split K).  Requirements: those of lin_gemm_run for N and K per mode
  * (MXFP4: K % 256 == 0; no limit on M), E <= 65535, M < 2^31.  E == 0 or
  * M == 0 is a no-op.  No allocation; enqueued on `stream`. */
 int lin_gemm_run_grouped(lin_gemm_t h, const void *A, const void *B, const lin_scales_t *scales,

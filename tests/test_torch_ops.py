@@ -140,3 +140,12 @@ def test_grouped_dynamic_fake_implementation():
     off = torch.empty(5, dtype=torch.int32, device="meta")
     y = torch.ops.lingemm.scaled_linear_grouped_dynamic(x, w, off, torch.empty(4, 96, device="meta"))
     assert y.shape == (40, 96) and y.dtype == torch.bfloat16
+
+
+def test_grouped_dynamic_rejects_unquantised_modes():
+    # The mode check comes before any device work, so CPU tensors suffice.
+    x = torch.empty(4, 256, dtype=torch.bfloat16)
+    w = torch.empty(2, 8, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tops.scaled_linear_grouped_dynamic(x, w, torch.zeros(3, dtype=torch.int32),
+                                           torch.ones(2, 8), quant="bf16")
