@@ -12,8 +12,11 @@ wrappers.  See oracle.c for the definition and the passages it follows.
 
 Parity pins (tests/test_oracle_*.py): exhaustive e4m3 decode against torch's
 CPU cast, bf16/fp16 decode and bf16 rounding against torch/numpy casts, exact
-Fraction brute force on tiny shapes for every quant mode, the GELU-tanh and
-SiLU closed forms and their odd-part identity, identity and permutation
+Fraction brute force on tiny shapes for every quant mode (epilogue through
+torch's fp64 activations), the activations against torch's own fp64
+gelu(approximate="tanh") / silu / relu on a dense grid, the listing's two GELU
+constants recovered from the oracle's outputs, the SiLU logit identity and the
+odd-part identity, identity and permutation
 weights, the block-scale closed form, the transpose (swap-AB) identity, and
 the 32 MiB size of a 4096x4096 16-bit intermediate; for the dynamic
 quantization, every e4m3 code and every midpoint between neighbours against
