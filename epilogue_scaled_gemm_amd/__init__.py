@@ -34,7 +34,7 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "HIP error",
 EXPORTS = ("lin_gemm_create", "lin_gemm_run", "lin_gemm_destroy", "lin_gemm_strerror",
            "lin_gemm_last_error", "lin_gemm_set_force", "lin_gemm_describe",
            "lin_gemm_run_unfused", "lin_gemm_quantize", "lin_gemm_run_dynamic",
-           "lin_gemm_run_grouped")
+           "lin_gemm_run_grouped", "lin_gemm_run_noalloc")
 DQ_KIND = {"fp8_token": 0, "int8_token": 1, "fp8_block": 2}
 X_DTYPE = {"bf16": 0, "fp16": 1}
 
@@ -66,6 +66,8 @@ def library():
     lib.lin_gemm_create.restype = I
     lib.lin_gemm_run.argtypes = [P, P, P, ctypes.POINTER(_Scales), P, P, P, I64, I64, I64, I, I, P]
     lib.lin_gemm_run.restype = I
+    lib.lin_gemm_run_noalloc.argtypes = lib.lin_gemm_run.argtypes
+    lib.lin_gemm_run_noalloc.restype = I
     lib.lin_gemm_destroy.argtypes = [P]
     lib.lin_gemm_destroy.restype = I
     lib.lin_gemm_strerror.argtypes = [I]

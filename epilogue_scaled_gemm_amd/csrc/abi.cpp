@@ -14,6 +14,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <fstream>
+#include <mutex>
 #include <sstream>
 #include <string>
 #include <vector>
@@ -244,6 +245,143 @@ lg::Epi make_epi(const lin_scales_t* scales, const void* bias, const void* resid
   return e;
 }
 
+// ------------------------------------------------ static scratch (no-alloc)
+//
+// lin_gemm_run_noalloc keeps its split-K partials and arrival counters in
+// this array instead of handle buffers, for callers that cannot allocate.
+// Each device that loads the library holds its own copy until the process
+// ends.  In host code `scratch` only names the symbol: its device address
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is handed to kernels and fill launches.
+constexpr size_t kScratchCounterBytes = (size_t)256 << 10;  // arrival counters
+constexpr size_t kScratchWsBytes = (size_t)64 << 20;        // split-K partials
+static __device__ __align__(256) unsigned char scratch[kScratchCounterBytes + kScratchWsBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_base(lin_gemm_t h, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(h, e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(h, LIN_ERR_UNSUPPORTED, "device index beyond " + std::to_string(kMaxDevices));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(h, e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(h, LIN_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LIN_OK;
+}
+
+// Point c.ws / c.counters into the device's scratch array and clear what
+// the kernels expect to find at zero: the arrival counters of a cross-
+// workgroup decode split (kept at zero by each finishing call, cleared
+// again here because the array is shared by every call and handle on the
+// device) and the accumulator of the atomic reduction.  The other split-K
+// forms overwrite their slices.  Clearing uses a fill kernel, so a caller
+// may capture the call into a graph.
+int scratch_workspace(lin_gemm_t h, const lg::Variant& v, lg::Call& c, int split,
+                      hipStream_t s) {
+  const bool pp = v.kind == lg::V_PP;
+  const bool dec = v.kind == lg::V_DECODE;
+  const size_t need = pp ? lg::pp_ws_bytes(c, split)
+                         : (dec ? lg::decode_ws_bytes(v, c, split) : lg::tile_ws_bytes(c, split));
+  const size_t ncnt = dec && split > 1 ? (size_t)((c.N + v.rows - 1) / v.rows) : 0;
+  if (need > kScratchWsBytes || ncnt * sizeof(int) > kScratchCounterBytes)
+    return fail(h, LIN_ERR_UNSUPPORTED,
+                "lin_gemm_run_noalloc: this call's split-K partials need " +
+                    std::to_string(need) + " bytes and " + std::to_string(ncnt) +
+                    " counters; the static scratch holds " + std::to_string(kScratchWsBytes) +
+                    " bytes and " + std::to_string(kScratchCounterBytes / sizeof(int)) +
+                    " counters");
+  void* base = nullptr;
+  if (need > 0 || ncnt > 0) {
+    int rc = scratch_base(h, &base);
+    if (rc != LIN_OK) return rc;
+  }
+  c.counters = base ? (int*)base : nullptr;
+  c.ws = base ? (void*)((char*)base + kScratchCounterBytes) : nullptr;
+  if (ncnt > 0) {
+    hipError_t e = lg::launch_fill_zero(c.counters, ncnt * sizeof(int), s);
+    if (e != hipSuccess) return hip_fail(h, e, "scratch counter clear");
+  }
+  if (dec && split > 1 && v.reduce == lg::R_ATOMIC) {
+    hipError_t e = lg::launch_fill_zero(c.ws, need, s);
+    if (e != hipSuccess) return hip_fail(h, e, "scratch accumulator clear");
+  }
+  return LIN_OK;
+}
+
+// lin_gemm_run and lin_gemm_run_noalloc: the same checks, variant choice
+// and kernels.  noalloc == false: split-K partials and arrival counters live
+// in handle-owned buffers (grown on demand).  noalloc == true: they live in
+// the device's static scratch array; a call that needs more than it holds
+// is rejected before anything is enqueued.
+int run_impl(lin_gemm_t h, const void* A, const void* B, const lin_scales_t* scales,
+             const void* bias, const void* residual, void* C, int64_t M, int64_t N, int64_t K,
+             int quant_mode, int activation, void* stream, bool noalloc) {
+  if (!h) return LIN_ERR_INVALID_ARG;
+  h->last_error.clear();
+  int rc = check_shape(h, quant_mode, M, N, K);
+  if (rc != LIN_OK || M == 0) return rc;
+  if (!A || !B || !C) return fail(h, LIN_ERR_INVALID_ARG, "A, B and C must be non-null");
+  if (!(activation >= LIN_ACT_NONE && activation <= LIN_ACT_SILU) && activation != LIN_ACT_RAW_ACC)
+    return fail(h, LIN_ERR_INVALID_ARG, "unknown activation " + std::to_string(activation));
+  const bool quantised = quant_mode >= LIN_Q_FP8_DYNAMIC && quant_mode != LIN_Q_MXFP4;
+  if (quantised && (!scales || !scales->a || !scales->b))
+    return fail(h, LIN_ERR_INVALID_ARG, "quantised modes need scales->a and scales->b");
+  if (quant_mode == LIN_Q_MXFP4 && (!scales || !scales->b))
+    return fail(h, LIN_ERR_INVALID_ARG, "MXFP4 weights need scales->b (E8M0 bytes)");
+  if (misaligned(A) || misaligned(B) || misaligned(C) || misaligned(bias) || misaligned(residual))
+    return fail(h, LIN_ERR_UNSUPPORTED, "A, B, C, bias and residual must be 16-byte aligned");
+  if (scales && (misaligned(scales->a) || misaligned(scales->b)))
+    return fail(h, LIN_ERR_UNSUPPORTED, "scale arrays must be 16-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  lg::Call c{};
+  c.A = A; c.B = B; c.M = M; c.N = N; c.K = K;
+  c.KB = b_row_bytes(quant_mode, K);
+  c.qk = qkind(quant_mode);
+  c.epi = make_epi(scales, bias, residual, C, M, N, quant_mode, activation);
+
+  lg::Variant v;
+  rc = select_variant(h, quant_mode, M, N, K, &v);
+  if (rc != LIN_OK) return rc;
+  hipError_t e;
+  const int split = resolve_split(v, c);
+  if (noalloc) {
+    rc = scratch_workspace(h, v, c, split, s);
+  } else {
+    rc = ensure_workspace(h, v, c, split, s);
+    c.ws = h->ws;
+    c.counters = h->counters;
+  }
+  if (rc != LIN_OK) return rc;
+  if (v.kind == lg::V_TILE) {
+    e = lg::launch_tile(v, c, split, s);
+  } else if (v.kind == lg::V_PP) {
+    e = lg::launch_pp(v, c, split, s);
+  } else {
+    e = v.xs && lg::decode_xs_supported(v, c) ? lg::launch_decode_xs(v, c, split, s)
+                                               : lg::launch_decode(v, c, split, s);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
+  if (std::getenv("LIN_GEMM_LOG")) {
+    lg::Call cc = c;
+    std::fprintf(stderr, "lin_gemm: quant=%d M=%lld N=%lld K=%lld -> %s\n", quant_mode,
+                 (long long)M, (long long)N, (long long)K,
+                 lg::format_variant(v, resolve_split(v, cc)).c_str());
+  }
+  return LIN_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -329,63 +467,15 @@ int lin_gemm_describe(lin_gemm_t h, int quant_mode, int64_t M, int64_t N, int64_
 int lin_gemm_run(lin_gemm_t h, const void* A, const void* B, const lin_scales_t* scales,
                  const void* bias, const void* residual, void* C, int64_t M, int64_t N, int64_t K,
                  int quant_mode, int activation, void* stream) {
-  if (!h) return LIN_ERR_INVALID_ARG;
-  h->last_error.clear();
-  int rc = check_shape(h, quant_mode, M, N, K);
-  if (rc != LIN_OK || M == 0) return rc;
-  if (!A || !B || !C) return fail(h, LIN_ERR_INVALID_ARG, "A, B and C must be non-null");
-  if (!(activation >= LIN_ACT_NONE && activation <= LIN_ACT_SILU) && activation != LIN_ACT_RAW_ACC)
-    return fail(h, LIN_ERR_INVALID_ARG, "unknown activation " + std::to_string(activation));
-  const bool quantised = quant_mode >= LIN_Q_FP8_DYNAMIC && quant_mode != LIN_Q_MXFP4;
-  if (quantised && (!scales || !scales->a || !scales->b))
-    return fail(h, LIN_ERR_INVALID_ARG, "quantised modes need scales->a and scales->b");
-  if (quant_mode == LIN_Q_MXFP4 && (!scales || !scales->b))
-    return fail(h, LIN_ERR_INVALID_ARG, "MXFP4 weights need scales->b (E8M0 bytes)");
-  if (misaligned(A) || misaligned(B) || misaligned(C) || misaligned(bias) || misaligned(residual))
-    return fail(h, LIN_ERR_UNSUPPORTED, "A, B, C, bias and residual must be 16-byte aligned");
-  if (scales && (misaligned(scales->a) || misaligned(scales->b)))
-    return fail(h, LIN_ERR_UNSUPPORTED, "scale arrays must be 16-byte aligned");
+  return run_impl(h, A, B, scales, bias, residual, C, M, N, K, quant_mode, activation, stream,
+                  false);
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  lg::Call c{};
-  c.A = A; c.B = B; c.M = M; c.N = N; c.K = K;
-  c.KB = b_row_bytes(quant_mode, K);
-  c.qk = qkind(quant_mode);
-  c.epi = make_epi(scales, bias, residual, C, M, N, quant_mode, activation);
-
-  lg::Variant v;
-  rc = select_variant(h, quant_mode, M, N, K, &v);
-  if (rc != LIN_OK) return rc;
-  hipError_t e;
-  if (v.kind == lg::V_TILE) {
-    const int split = resolve_split(v, c);
-    rc = ensure_workspace(h, v, c, split, s);
-    if (rc != LIN_OK) return rc;
-    c.ws = h->ws;
-    e = lg::launch_tile(v, c, split, s);
-  } else if (v.kind == lg::V_PP) {
-    const int split = resolve_split(v, c);
-    rc = ensure_workspace(h, v, c, split, s);
-    if (rc != LIN_OK) return rc;
-    c.ws = h->ws;
-    e = lg::launch_pp(v, c, split, s);
-  } else {
-    const int split = resolve_split(v, c);
-    rc = ensure_workspace(h, v, c, split, s);
-    if (rc != LIN_OK) return rc;
-    c.ws = h->ws;
-    c.counters = h->counters;
-    e = v.xs && lg::decode_xs_supported(v, c) ? lg::launch_decode_xs(v, c, split, s)
-                                               : lg::launch_decode(v, c, split, s);
-  }
-  if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
-  if (std::getenv("LIN_GEMM_LOG")) {
-    lg::Call cc = c;
-    std::fprintf(stderr, "lin_gemm: quant=%d M=%lld N=%lld K=%lld -> %s\n", quant_mode,
-                 (long long)M, (long long)N, (long long)K,
-                 lg::format_variant(v, resolve_split(v, cc)).c_str());
-  }
-  return LIN_OK;
+int lin_gemm_run_noalloc(lin_gemm_t h, const void* A, const void* B, const lin_scales_t* scales,
+                         const void* bias, const void* residual, void* C, int64_t M, int64_t N,
+                         int64_t K, int quant_mode, int activation, void* stream) {
+  return run_impl(h, A, B, scales, bias, residual, C, M, N, K, quant_mode, activation, stream,
+                  true);
 }
 
 int lin_gemm_run_unfused(lin_gemm_t h, const void* A, const void* B, const void* bias,

@@ -133,6 +133,26 @@ int lin_gemm_run(lin_gemm_t h, const void *A, const void *B, const lin_scales_t 
                  const void *bias, const void *residual, void *C, int64_t M, int64_t N,
                  int64_t K, int quant_mode, int activation, void *stream);
 
+/* lin_gemm_run for callers that cannot allocate device memory: code under
+ * hipGraph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, checks, variant choice, kernels and results as
+ * lin_gemm_run, but the split-K partials and arrival counters live in a
+ * static device array of the library (64 MiB of partials and 65536 counters
+ * per device, held from the first such call on a device until the process
+ * ends) instead of handle buffers; nothing is allocated or freed, and the
+ * handle's own buffers are not touched.  A call whose chosen variant needs
+ * more partials or counters than that gets LIN_ERR_UNSUPPORTED before
+ * anything is enqueued (lin_gemm_describe names the variant; a forced
+ * smaller split, or lin_gemm_run, avoids it).  Counters and the atomic
+ * reduction's accumulator are cleared by a fill kernel at the start of each
+ * call that uses them.  Every call on a device shares that one array: calls
+ * that overlap in time on one device (two streams, two host threads, or a
+ * graph replay alongside an eager call) race on it and give wrong results;
+ * calls ordered on one stream do not. */
+int lin_gemm_run_noalloc(lin_gemm_t h, const void *A, const void *B, const lin_scales_t *scales,
+                         const void *bias, const void *residual, void *C, int64_t M, int64_t N,
+                         int64_t K, int quant_mode, int activation, void *stream);
+
 /* Release the handle and its device workspace.  NULL is accepted. */
 int lin_gemm_destroy(lin_gemm_t h);
 
