@@ -44,13 +44,17 @@ def traced(dtype=torch.bfloat16):
     return m, torch.fx.symbolic_trace(m)
 
 
+def x_like(dtype=torch.bfloat16, *shape):
+    return torch.zeros(*(shape or (2, 3, 64)), dtype=dtype)
+
+
 def ops_in(gm):
     return [n for n in gm.graph.nodes if n.op == "call_function" and n.target is OP]
 
 
 def test_pass_fuses_the_kernel_chains_and_keeps_the_rest():
     _, gm = traced()
-    n = tops.fuse_linear_epilogues(gm)
+    n = tops.fuse_linear_epilogues(gm, (x_like(),))
     fused = ops_in(gm)
     assert n == len(fused) == 4
     by_act = {f.kwargs["act"]: f for f in fused}
@@ -80,7 +84,8 @@ def test_pass_fuses_scale_and_residual_without_activation():
             return self.down(h) * 0.5 + x
 
     gm = torch.fx.symbolic_trace(Down().to(torch.bfloat16))
-    assert tops.fuse_linear_epilogues(gm) == 1
+    assert tops.fuse_linear_epilogues(gm, (x_like(torch.bfloat16, 4, 32),
+                                           x_like(torch.bfloat16, 4, 16))) == 1
     (f,) = ops_in(gm)
     assert f.kwargs["act"] == "none" and f.kwargs["alpha"] == 0.5
     assert f.kwargs["residual"].name == "x"
@@ -90,7 +95,7 @@ def test_pass_fuses_scale_and_residual_without_activation():
 
 def test_pass_skips_fp32_weights_and_plain_linears():
     _, gm = traced(torch.float32)
-    assert tops.fuse_linear_epilogues(gm) == 0      # the kernel takes bf16 / fp16 weights
+    assert tops.fuse_linear_epilogues(gm, (x_like(torch.float32),)) == 0  # bf16 / fp16 weights only
 
     class Plain(nn.Module):
         def __init__(self):
@@ -101,7 +106,131 @@ def test_pass_skips_fp32_weights_and_plain_linears():
             return self.l(x)
 
     gm = torch.fx.symbolic_trace(Plain().to(torch.bfloat16))
-    assert tops.fuse_linear_epilogues(gm) == 0
+    assert tops.fuse_linear_epilogues(gm, (x_like(torch.bfloat16, 2, 16),)) == 0
+
+
+class AfterAct(nn.Module):
+    """A [N] vector added after the activation is not a residual: the kernel
+    would read M x N values from it."""
+
+    def __init__(self):
+        super().__init__()
+        self.fc = nn.Linear(32, 16)
+        self.b2 = nn.Parameter(torch.zeros(16))
+
+    def forward(self, x, r):
+        return F.gelu(self.fc(x), approximate="tanh") + self.b2 + r
+
+
+def test_pass_skips_broadcast_residual():
+    gm = torch.fx.symbolic_trace(AfterAct().to(torch.bfloat16))
+    assert tops.fuse_linear_epilogues(gm, (x_like(torch.bfloat16, 4, 32),
+                                           x_like(torch.bfloat16, 4, 16))) == 1
+    (f,) = ops_in(gm)
+    assert f.kwargs["act"] == "gelu_tanh" and f.kwargs["residual"] is None
+    adds = [n for n in gm.graph.nodes if n.op == "call_function" and n.target is operator.add]
+    assert len(adds) == 2                        # + b2 and + r stay in the graph
+
+
+def test_pass_skips_residual_of_another_dtype_or_unknown_shape():
+    class Down(nn.Module):
+        def __init__(self):
+            super().__init__()
+            self.down = nn.Linear(32, 16)
+
+        def forward(self, h, x):
+            return self.down(h) * 0.5 + x
+
+    m = Down().to(torch.bfloat16)
+    gm = torch.fx.symbolic_trace(m)
+    # fp32 residual: the add promotes to fp32; the kernel reads bf16.
+    assert tops.fuse_linear_epilogues(gm, (x_like(torch.bfloat16, 4, 32),
+                                           x_like(torch.float32, 4, 16))) == 1
+    (f,) = ops_in(gm)
+    assert f.kwargs["residual"] is None and f.kwargs["alpha"] == 0.5
+    # No example inputs and no metadata: the residual's shape is unknown.
+    gm = torch.fx.symbolic_trace(m)
+    assert tops.fuse_linear_epilogues(gm) == 1
+    (f,) = ops_in(gm)
+    assert f.kwargs["residual"] is None
+    # A residual that broadcasts over the tokens ([1, 16] against [4, 16]).
+    gm = torch.fx.symbolic_trace(m)
+    assert tops.fuse_linear_epilogues(gm, (x_like(torch.bfloat16, 4, 32),
+                                           x_like(torch.bfloat16, 1, 16))) == 1
+    (f,) = ops_in(gm)
+    assert f.kwargs["residual"] is None
+
+
+class PagesBlock(nn.Module):
+    """The forward pass the pages fuse: gelu(matmul(x, w) + b) with the tanh
+    GELU, w a [K, N] weight ("Совместная работа Helion и TorchInductor",
+    sections on the TorchInductor integration and on checking the fusion)."""
+
+    def __init__(self, K=64, N=48, op="matmul"):
+        super().__init__()
+        self.w = nn.Parameter(torch.randn(K, N))
+        self.b = nn.Parameter(torch.randn(N))
+        self.op = op
+
+    def forward(self, x):
+        if self.op == "matmul":
+            y = torch.matmul(x, self.w)
+        elif self.op == "at":
+            y = x @ self.w
+        else:
+            y = torch.mm(x, self.w)
+        return F.gelu(y + self.b, approximate="tanh")
+
+
+@pytest.mark.parametrize("op", ["matmul", "at", "mm"])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_pass_fuses_the_pages_matmul_chain(op, dtype):
+    m = PagesBlock(op=op).to(dtype)
+    gm = torch.fx.symbolic_trace(m)
+    assert tops.fuse_linear_epilogues(gm, (x_like(dtype, 5, 64),)) == 1
+    (f,) = ops_in(gm)
+    assert f.kwargs["act"] == "gelu_tanh" and f.kwargs["alpha"] == 1.0
+    assert f.kwargs["quant"] == ("fp16" if dtype == torch.float16 else "bf16")
+    w_nk = getattr(gm, f.args[1].target)
+    assert w_nk.shape == (48, 64) and torch.equal(w_nk, m.w.detach().t())
+    assert f.kwargs["bias"].target == "b"
+    left = {n.target for n in gm.graph.nodes if n.op == "call_function"}
+    assert not left & {torch.matmul, operator.matmul, torch.mm, operator.add, F.gelu}
+
+
+def test_pass_fuses_the_aten_pattern_of_make_fx():
+    # The same chain as aten.mm -> aten.add -> aten.gelu(approximate="tanh"),
+    # the form an Inductor joint-graph pattern sees; make_fx keeps the
+    # parameters as attributes and records fake values in the metadata.
+    from torch.fx.experimental.proxy_tensor import make_fx
+    m = PagesBlock(op="mm").to(torch.bfloat16)
+    gm = make_fx(m)(x_like(torch.bfloat16, 5, 64))
+    targets = {n.target for n in gm.graph.nodes if n.op == "call_function"}
+    assert torch.ops.aten.mm.default in targets and torch.ops.aten.gelu.default in targets
+    assert tops.fuse_linear_epilogues(gm) == 1
+    (f,) = ops_in(gm)
+    assert f.kwargs["act"] == "gelu_tanh" and f.kwargs["bias"] is not None
+
+
+def test_pass_treats_a_full_shape_addend_as_residual_before_the_activation():
+    # matmul(x, w) + R with R of the full output shape is no bias: the kernel
+    # adds a residual after its activation, so only matmul + R is fused and
+    # the GELU stays a separate op.  A [1, N] addend is neither.
+    class Full(PagesBlock):
+        def forward(self, x):
+            return F.gelu(torch.matmul(x, self.w) + self.rb, approximate="tanh")
+
+    m = Full()
+    m.rb = nn.Parameter(torch.randn(5, 48))
+    gm = torch.fx.symbolic_trace(m.to(torch.bfloat16))
+    assert tops.fuse_linear_epilogues(gm, (x_like(torch.bfloat16, 5, 64),)) == 1
+    (f,) = ops_in(gm)
+    assert f.kwargs["act"] == "none" and f.kwargs["bias"] is None
+    assert f.kwargs["residual"].target == "rb"
+    assert [n for n in gm.graph.nodes if n.op == "call_function" and n.target is F.gelu]
+    m.rb = nn.Parameter(torch.randn(1, 48))
+    gm = torch.fx.symbolic_trace(m.to(torch.bfloat16))
+    assert tops.fuse_linear_epilogues(gm, (x_like(torch.bfloat16, 5, 64),)) == 0
 
 
 def test_fake_implementation_gives_shape_and_dtype():
@@ -117,10 +246,39 @@ def test_fake_implementation_gives_shape_and_dtype():
     y = torch.ops.lingemm.scaled_linear(xq, wq, scale_a=s, scale_b=torch.empty(32, device="meta"),
                                         quant="fp8_dynamic")
     assert y.shape == (7, 32) and y.dtype == torch.bfloat16
-    y = torch.ops.lingemm.scaled_linear_dynamic(x, wq, torch.empty(96, device="meta"))
+    y = torch.ops.lingemm.scaled_linear_dynamic(x, wq, torch.empty(32, device="meta"))
     assert y.shape == (3, 5, 32) and y.dtype == torch.bfloat16
     with pytest.raises(Exception):
         torch.ops.lingemm.scaled_linear(x, torch.empty(96, 63, dtype=torch.bfloat16, device="meta"))
+
+
+@pytest.mark.parametrize("bad", ["broadcast_residual", "fp32_residual", "bias_shape",
+                                 "bias_dtype", "scale_a_count", "scale_b_dtype", "x_dtype"])
+def test_op_rejects_bad_operands_on_meta(bad):
+    x = torch.empty(4, 64, dtype=torch.bfloat16, device="meta")
+    w = torch.empty(32, 64, dtype=torch.bfloat16, device="meta")
+    kw = dict(quant="bf16")
+    if bad == "broadcast_residual":
+        kw["residual"] = torch.empty(32, dtype=torch.bfloat16, device="meta")
+    elif bad == "fp32_residual":
+        kw["residual"] = torch.empty(4, 32, dtype=torch.float32, device="meta")
+    elif bad == "bias_shape":
+        kw["bias"] = torch.empty(1, 32, dtype=torch.bfloat16, device="meta")
+    elif bad == "bias_dtype":
+        kw["bias"] = torch.empty(32, dtype=torch.float32, device="meta")
+    elif bad in ("scale_a_count", "scale_b_dtype"):
+        x = torch.empty(4, 64, dtype=torch.float8_e4m3fn, device="meta")
+        w = torch.empty(32, 64, dtype=torch.float8_e4m3fn, device="meta")
+        kw = dict(quant="fp8_dynamic", scale_a=torch.empty(4, device="meta"),
+                  scale_b=torch.empty(32, device="meta"))
+        if bad == "scale_a_count":
+            kw["scale_a"] = torch.empty(1, device="meta")
+        else:
+            kw["scale_b"] = torch.empty(32, dtype=torch.float16, device="meta")
+    elif bad == "x_dtype":
+        x = torch.empty(4, 64, dtype=torch.float16, device="meta")
+    with pytest.raises(ValueError):
+        torch.ops.lingemm.scaled_linear(x, w, **kw)
 
 
 def test_grouped_fake_implementation():
