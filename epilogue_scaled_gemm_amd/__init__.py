@@ -116,6 +116,45 @@ def _code(table, key):
     return table[key]
 
 
+_QNAME = {v: k for k, v in QUANT.items()}
+
+
+def _need(name, t, count, esize):
+    """t must hold at least `count` elements of `esize` bytes: the kernels
+    read that many from its address.  (The library sees only pointers, so
+    these checks are the binding's part of argument marshalling.)"""
+    if t is None or count <= 0:
+        return
+    if t.element_size() != esize:
+        raise ValueError(f"{name}: elements must be {esize} bytes, got {t.dtype}")
+    if t.numel() < count:
+        raise ValueError(f"{name}: needs {count} elements, got {t.numel()} "
+                         f"(shape {tuple(t.shape)}; no broadcasting)")
+
+
+def _check_layer(quant, act, M, N, K, A=None, B=None, C=None, sa=None, sb=None, bias=None,
+                 residual=None, a16=False):
+    """Byte sizes of a layer call's operands (layouts of include/lin_gemm.h)."""
+    q = _QNAME.get(quant, quant) if isinstance(quant, int) else quant
+    a_es = 2 if (a16 or q in ("bf16", "fp16", "mxfp4")) else 1
+    kb = K // 2 if q == "mxfp4" else K * (2 if q in ("bf16", "fp16") else 1)
+    for name, t, nbytes in (("A", A, M * K * a_es), ("B", B, N * kb)):
+        if t is not None and t.numel() * t.element_size() < nbytes:
+            raise ValueError(f"{name}: needs {nbytes} bytes, got {t.numel() * t.element_size()}")
+    raw = act in ("raw_acc", 255)
+    _need("C", C, M * N, 4 if raw else 2)
+    _need("bias", bias, N, 2)
+    _need("residual", residual, M * N, 2)
+    if q in ("fp8_dynamic", "w8a8_int8"):
+        _need("sa", sa, M, 4)
+        _need("sb", sb, N, 4)
+    elif q == "block_fp8":
+        _need("sa", sa, M * (K // 128), 4)
+        _need("sb", sb, (N // 128) * (K // 128), 4)
+    elif q == "mxfp4":
+        _need("sb (E8M0 bytes)", sb, N * (K // 32), 1)
+
+
 class Handle:
     """One lin_gemm handle (variant table + split-K workspace)."""
 
@@ -142,6 +181,7 @@ class Handle:
         kb = K // 2 if quant in ("mxfp4", 5) else K  # 4-bit weights: two codes per byte
         if B.shape[1] != kb:
             raise ValueError(f"inner dimensions differ: A has K={K}, B rows have {B.shape[1]}")
+        _check_layer(quant, act, M, N, K, A, B, C, sa, sb, bias, residual)
         sc = _Scales(None if sa is None else _ptr(sa).value,
                      None if sb is None else _ptr(sb).value, float(alpha))
         rc = self._lib.lin_gemm_run(self._h, _ptr(A), _ptr(B), ctypes.byref(sc), _ptr(bias),
@@ -178,6 +218,7 @@ class Handle:
         N = B.shape[0]
         if B.shape[1] != K:
             raise ValueError(f"inner dimensions differ: X has K={K}, B has {B.shape[1]}")
+        _check_layer(quant, act, M, N, K, X, B, C, None, sb, bias, residual, a16=True)
         rc = self._lib.lin_gemm_run_dynamic(self._h, _ptr(X), _code(X_DTYPE, x_dtype), _ptr(B),
                                             _ptr(sb), float(alpha), _ptr(bias), _ptr(residual),
                                             _ptr(C), M, N, K, _code(QUANT, quant),

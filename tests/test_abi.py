@@ -262,3 +262,36 @@ def _raw_grouped(h, A=FAKE, B=FAKE, C=FAKE, offsets=FAKE, E=4, M=8, N=16, K=64, 
 ])
 def test_grouped_argument_errors(cpu_handle, kw, status):
     assert _raw_grouped(cpu_handle, **kw) == status
+
+
+@pytest.mark.parametrize("bad", ["residual_row", "residual_fp32", "bias_fp32", "sa_short",
+                                 "C_short", "B_short"])
+def test_binding_rejects_undersized_operands(bad):
+    # The binding checks byte sizes before calling the library (which sees
+    # only pointers); CPU tensors suffice since nothing is launched.
+    M, N, K = 4, 32, 64
+    t = dict(A=torch.zeros(M, K, dtype=torch.uint8), B=torch.zeros(N, K, dtype=torch.uint8),
+             C=torch.zeros(M, N, dtype=torch.int16), sa=torch.ones(M), sb=torch.ones(N),
+             bias=torch.zeros(N, dtype=torch.bfloat16),
+             residual=torch.zeros(M, N, dtype=torch.bfloat16))
+    if bad == "residual_row":
+        t["residual"] = torch.zeros(N, dtype=torch.bfloat16)
+    elif bad == "residual_fp32":
+        t["residual"] = torch.zeros(M, N, dtype=torch.float32)
+    elif bad == "bias_fp32":
+        t["bias"] = torch.zeros(N, dtype=torch.float32)
+    elif bad == "sa_short":
+        t["sa"] = torch.ones(1)
+    elif bad == "C_short":
+        t["C"] = torch.zeros(M - 1, N, dtype=torch.int16)
+    elif bad == "B_short":
+        t["B"] = torch.zeros(N - 1, K, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        lg._check_layer("fp8_dynamic", "none", M, N, K, t["A"], t["B"], t["C"], t["sa"], t["sb"],
+                        t["bias"], t["residual"])
+    # the same operands with nothing wrong pass
+    good = dict(A=torch.zeros(M, K, dtype=torch.uint8), B=torch.zeros(N, K, dtype=torch.uint8),
+                C=torch.zeros(M, N, dtype=torch.int16), sa=torch.ones(M), sb=torch.ones(N),
+                bias=torch.zeros(N, dtype=torch.bfloat16),
+                residual=torch.zeros(M, N, dtype=torch.bfloat16))
+    lg._check_layer("fp8_dynamic", "none", M, N, K, *good.values())
