@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 --pmc passes: the headline graphs for two "
                          "steps, then a plain 256 MiB device copy that calibrates the counters")
+    ap.add_argument("--counters-shapes", default=None, metavar="CFG:M[,M...][;CFG:M...]",
+                    help="counter run: three calls of each listed workload shape (two weight "
+                         "copies), then the 256 MiB copy; e.g. 4:512,2048;2:1,32")
     ap.add_argument("--counters-prefill", action="store_true",
                     help="short run for rocprofv3 --pmc passes on the 4096^3 bf16 prefill: two "
                          "fused calls, two unfused three-kernel calls, then the 256 MiB copy")
@@ -89,6 +92,28 @@ def counters_prefill(torch, h):
     print(json.dumps({"counters_run": "prefill", "copy_bytes": 256 << 20,
                       "fused_algorithmic_bytes": wl.bytes(M),
                       "tensor_bytes": 2 * M * wl.N, "M": M, "N": wl.N, "K": wl.K}), flush=True)
+
+
+def counters_shapes(torch, h, spec):
+    """Three calls of each workload shape in `spec` ("cfg:M,M;cfg:M") over two
+    weight copies, then the calibration copy; for rocprofv3 counter passes."""
+    import synth
+    out = []
+    for part in spec.split(";"):
+        cfg, ms = part.split(":")
+        cfg, ms = int(cfg), [int(m) for m in ms.split(",")]
+        wl = Workload(torch, cfg, ms, ncopy=2)
+        for M in ms:
+            for r in range(3):
+                wl.call(h, M, r)
+            torch.cuda.synchronize()
+            out.append(dict(cfg=cfg, M=M, N=wl.N, K=wl.K, variant=h.describe(wl.quant, M, wl.N, wl.K),
+                            algorithmic_bytes=wl.bytes(M), flops=wl.flops(M)))
+        del wl
+        torch.cuda.empty_cache()
+    counters_copy(torch)
+    print(json.dumps({"counters_run": "shapes", "copy_bytes": 256 << 20, "shapes": out}),
+          flush=True)
 
 
 def source_digest():
@@ -189,6 +214,55 @@ def shape_row(name, quant, M, N, K, t, nbytes, flops, variant, kernel_calls=1):
                 hbm_frac=round(tbs / HBM_PEAK, 4), mfma_frac=round(tfs / MFMA_PEAK[quant], 4),
                 bound=bound, kernels_per_call=kernel_calls,
                 roof_frac=round((tbs / HBM_PEAK) if bound == "hbm" else (tfs / MFMA_PEAK[quant]), 4))
+
+
+CEILING_MIB = (12, 24, 48, 96)                       # the decode workloads' weight sizes
+CEILING_LAUNCH = [(g, u) for g in (512, 1024, 2048, 4096) for u in (4, 8, 16)]
+
+
+def stream_ceiling(torch, h, reps):
+    """Measured HBM read ceiling: lin_gemm_stream_read (a kernel that only
+    reads) over the same kind of rotation as the decode rows (copies of the
+    buffer totalling >= 384 MiB, one call per copy per graph replay), for
+    each weight size of the decode workloads and a few launch shapes; the
+    fastest launch shape is the ceiling for that byte count."""
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    out = []
+    for mib in CEILING_MIB:
+        nb = mib << 20
+        ncopy = max(2, min(32, -(-NCOPY_TARGET_BYTES // nb)))
+        bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
+        for b in bufs:
+            b.fill_(1)
+        graphs = []
+        for grid, unroll in CEILING_LAUNCH:
+            h.stream_read(bufs[0], sink, grid, unroll)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for b in bufs:
+                    h.stream_read(b, sink, grid, unroll)
+            graphs.append(g)
+        ts = [t / ncopy for t in time_graphs(torch, graphs, max(5, reps))]
+        i = int(np.argmin(ts))
+        row = dict(MiB=mib, bytes=nb, copies=ncopy, us=round(ts[i] * 1e6, 3),
+                   TBps=round(nb / ts[i] / 1e12, 4), hbm_frac=round(nb / ts[i] / HBM_PEAK, 4),
+                   grid=CEILING_LAUNCH[i][0], unroll=CEILING_LAUNCH[i][1],
+                   all_us={f"{g}x{u}": round(t * 1e6, 3) for (g, u), t in zip(CEILING_LAUNCH, ts)})
+        out.append(row)
+        print(f"[ceiling] {row}", file=sys.stderr, flush=True)
+        del graphs, bufs
+    torch.cuda.empty_cache()
+    return out
+
+
+def ceiling_us(ceiling, weight_bytes):
+    """The measured read time of the ceiling entry for exactly this byte
+    count, else None."""
+    for c in ceiling or []:
+        if c["bytes"] == weight_bytes:
+            return c["us"]
+    return None
 
 
 def per_shape_table(torch, h, reps):
@@ -483,6 +557,10 @@ def main():
         counters_prefill(torch, h)
         h.close()
         return
+    if args.counters_shapes:
+        counters_shapes(torch, h, args.counters_shapes)
+        h.close()
+        return
     c = synth.WORKLOADS[HEAD_CFG]
     Ms = list(c["Ms"])
     wl = Workload(torch, HEAD_CFG, Ms)
@@ -563,13 +641,29 @@ def main():
                        TBps=round(wl.bytes(M) * R * args.steps / per_M[M] / 1e12, 4),
                        hbm_frac=round(wl.bytes(M) * R * args.steps / per_M[M] / HBM_PEAK, 4),
                        variant=h.describe(wl.quant, M, wl.N, wl.K)) for M in Ms]
+    wbytes = wl.B[0].numel() * wl.B[0].element_size()
     del graphs, wl
     torch.cuda.empty_cache()
+
+    ceiling = stream_ceiling(torch, h, args.reps)
+    head_ceil = ceiling_us(ceiling, wbytes)
+    if head_ceil:
+        roofline["stream_ceiling_us"] = head_ceil
+        roofline["of_stream_ceiling"] = round(head_ceil / roofline["avg_launch_us"], 4)
+        for r in per_m_rows:
+            r["of_stream_ceiling"] = round(head_ceil / r["us_per_call"], 4)
 
     shapes = None
     if not args.no_shapes:
         shapes = (per_shape_table(torch, h, args.reps) + dynamic_quant_rows(torch, h, args.reps)
                   + moe_rows(torch, h, args.reps) + vendor_rows(torch, args.reps))
+        for r in shapes:
+            if r.get("bound") == "hbm" and r.get("N") and r.get("M", 0) <= 32:
+                wb = r["N"] * (r["K"] // 2 if r["quant"] == "mxfp4" else
+                               r["K"] * (2 if r["quant"] in ("bf16", "fp16") else 1))
+                cu = ceiling_us(ceiling, wb)
+                if cu and r["shape"].startswith(("fp8", "w8a8", "block", "mxfp4", "bf16")):
+                    r["of_stream_ceiling"] = round(cu / r["us"], 4)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
     out = {
@@ -593,6 +687,7 @@ def main():
         "roofline": roofline,
         "per_M": per_m_rows,
         "cpu_baseline": cpu,
+        "hbm_stream_ceiling": ceiling,
         "shapes": shapes,
         "source_digest": digest,
     }

@@ -34,7 +34,7 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "HIP error",
 EXPORTS = ("lin_gemm_create", "lin_gemm_run", "lin_gemm_destroy", "lin_gemm_strerror",
            "lin_gemm_last_error", "lin_gemm_set_force", "lin_gemm_describe",
            "lin_gemm_run_unfused", "lin_gemm_quantize", "lin_gemm_run_dynamic",
-           "lin_gemm_run_grouped", "lin_gemm_run_noalloc")
+           "lin_gemm_run_grouped", "lin_gemm_run_noalloc", "lin_gemm_stream_read")
 DQ_KIND = {"fp8_token": 0, "int8_token": 1, "fp8_block": 2}
 X_DTYPE = {"bf16": 0, "fp16": 1}
 
@@ -81,6 +81,8 @@ def library():
     lib.lin_gemm_run_unfused.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, ctypes.c_float,
                                          I, I, P]
     lib.lin_gemm_run_unfused.restype = I
+    lib.lin_gemm_stream_read.argtypes = [P, P, I64, I, I, P, P]
+    lib.lin_gemm_stream_read.restype = I
     lib.lin_gemm_quantize.argtypes = [P, P, I, I64, I64, I, P, P, P]
     lib.lin_gemm_quantize.restype = I
     lib.lin_gemm_run_dynamic.argtypes = [P, P, I, P, P, ctypes.c_float, P, P, P, I64, I64, I64,
@@ -201,6 +203,17 @@ class Handle:
                                             _code(QUANT, quant), _code(ACT, act), _stream(stream))
         self._check(rc, "lin_gemm_run_unfused")
         return C
+
+    def stream_read(self, src, sink, grid=0, unroll=8, nbytes=None, stream=None):
+        """Measurement only: a plain streaming read of src (its bytes, or the
+        first nbytes); sink is an int32 CUDA tensor of at least 256 entries."""
+        nb = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+        if nb > src.numel() * src.element_size():
+            raise ValueError("nbytes beyond the tensor")
+        _need("sink", sink, 256, 4)
+        rc = self._lib.lin_gemm_stream_read(self._h, _ptr(src), nb, int(grid), int(unroll),
+                                            _ptr(sink), _stream(stream))
+        self._check(rc, "lin_gemm_stream_read")
 
     def quantize(self, X, Q, scales, kind="fp8_token", x_dtype="bf16", stream=None):
         """Dynamic activation quantization of X[M,K] into Q[M,K] and scales."""

@@ -30,7 +30,6 @@ struct lin_gemm_ctx {
   std::string last_error;
   void* ws = nullptr;         // split-K workspace
   size_t ws_bytes = 0;
-  bool ws_zero = true;        // workspace all zero (needed by the atomic reduction)
   int* counters = nullptr;    // per-16-row-group arrival counters (kept at zero between calls)
   size_t counters_n = 0;
   void* dq = nullptr;         // staging of lin_gemm_run_dynamic: codes, then scales
@@ -146,6 +145,11 @@ int select_variant(lin_gemm_t h, int quant, int64_t M, int64_t N, int64_t K, lg:
     if (h->forced) return fail(h, LIN_ERR_UNSUPPORTED, "tile shape not compiled for this mode");
     v->bm = 128; v->bn = 128; v->wm = 2; v->wn = 2;
   }
+  if (v->kind == lg::V_TILE && v->sk > 0 &&
+      !lg::tile_sk_supported(qkind(quant), v->bm, v->bn, v->wm, v->wn)) {
+    if (h->forced) return fail(h, LIN_ERR_UNSUPPORTED, "tile shape not compiled in stream-K form");
+    v->sk = 0;
+  }
   // Block scales are uniform over a decode workgroup's rows only when the
   // rows sit inside one 128-row scale block.
   if (v->kind == lg::V_DECODE && quant == LIN_Q_BLOCK_FP8 && 128 % v->rows != 0) {
@@ -164,6 +168,7 @@ int resolve_split(const lg::Variant& v, const lg::Call& c) {
     return c.qk == lg::QK_FP8_BLOCK ? split : 1;
   }
   if (v.kind == lg::V_TILE) {
+    if (v.sk > 0) return 1;
     int split = v.split > 0 ? v.split : lg::tile_auto_split(v, c);
     return std::min(split, 16);
   }
@@ -180,7 +185,7 @@ int ensure_workspace(lin_gemm_t h, const lg::Variant& v, const lg::Call& c, int 
   const bool pp = v.kind == lg::V_PP;
   const bool dec = v.kind == lg::V_DECODE;
   const size_t need = pp ? lg::pp_ws_bytes(c, split)
-                         : (dec ? lg::decode_ws_bytes(v, c, split) : lg::tile_ws_bytes(c, split));
+                         : (dec ? lg::decode_ws_bytes(v, c, split) : lg::tile_ws_bytes(v, c, split));
   const size_t ncnt = (size_t)((c.N + v.rows - 1) / v.rows);  // one per row group
   const bool grow_ws = need > h->ws_bytes;
   const bool grow_cnt = dec && split > 1 && ncnt > h->counters_n;
@@ -198,9 +203,6 @@ int ensure_workspace(lin_gemm_t h, const lg::Variant& v, const lg::Call& c, int 
       return fail(h, LIN_ERR_OOM, "split-K workspace allocation of " + std::to_string(bytes) + " bytes failed");
     }
     h->ws_bytes = bytes;
-    hipError_t e = lg::launch_fill_zero(h->ws, bytes, s);
-    if (e != hipSuccess) return hip_fail(h, e, "workspace zero fill");
-    h->ws_zero = true;
   }
   if (grow_cnt) {
     if (h->counters) h->retired.push_back(h->counters);
@@ -215,16 +217,15 @@ int ensure_workspace(lin_gemm_t h, const lg::Variant& v, const lg::Call& c, int 
     hipError_t e = lg::launch_fill_zero(h->counters, n * sizeof(int), s);
     if (e != hipSuccess) return hip_fail(h, e, "counter zero fill");
   }
-  if (split > 1 && dec) {
-    // The atomic reduction needs a zero accumulator; the others leave
-    // partials behind, so zero again when switching to atomic.
-    if (v.reduce == lg::R_ATOMIC && !h->ws_zero) {
-      hipError_t e = lg::launch_fill_zero(h->ws, h->ws_bytes, s);
-      if (e != hipSuccess) return hip_fail(h, e, "workspace zero fill");
-    }
-    h->ws_zero = (v.reduce == lg::R_ATOMIC);
+  if (split > 1 && dec && v.reduce == lg::R_ATOMIC) {
+    // The atomic reduction needs a zero accumulator.  Its last arrival
+    // re-zeroes what it used, but other split-K forms (and other shapes)
+    // leave partials in the same workspace, and a graph captured now must
+    // not depend on what eager calls do between its replays: the fill is
+    // enqueued with every atomic call.
+    hipError_t e = lg::launch_fill_zero(h->ws, need, s);
+    if (e != hipSuccess) return hip_fail(h, e, "workspace zero fill");
   }
-  if (split > 1 && !dec) h->ws_zero = false;  // slices overwrite the workspace
   return LIN_OK;
 }
 
@@ -291,7 +292,7 @@ int scratch_workspace(lin_gemm_t h, const lg::Variant& v, lg::Call& c, int split
   const bool pp = v.kind == lg::V_PP;
   const bool dec = v.kind == lg::V_DECODE;
   const size_t need = pp ? lg::pp_ws_bytes(c, split)
-                         : (dec ? lg::decode_ws_bytes(v, c, split) : lg::tile_ws_bytes(c, split));
+                         : (dec ? lg::decode_ws_bytes(v, c, split) : lg::tile_ws_bytes(v, c, split));
   const size_t ncnt = dec && split > 1 ? (size_t)((c.N + v.rows - 1) / v.rows) : 0;
   if (need > kScratchWsBytes || ncnt * sizeof(int) > kScratchCounterBytes)
     return fail(h, LIN_ERR_UNSUPPORTED,
@@ -515,6 +516,25 @@ int lin_gemm_run_unfused(lin_gemm_t h, const void* A, const void* B, const void*
   if (e != hipSuccess) return hip_fail(h, e, "bias+activation launch");
   e = lg::launch_scale_residual(U, residual, C, M, N, alpha, f16, s);
   if (e != hipSuccess) return hip_fail(h, e, "scale+residual launch");
+  return LIN_OK;
+}
+
+int lin_gemm_stream_read(lin_gemm_t h, const void* src, int64_t bytes, int grid, int unroll,
+                         int* sink, void* stream) {
+  if (!h) return LIN_ERR_INVALID_ARG;
+  h->last_error.clear();
+  if (bytes < 0) return fail(h, LIN_ERR_INVALID_ARG, "negative size");
+  if (bytes == 0) return LIN_OK;
+  if (!src || !sink) return fail(h, LIN_ERR_INVALID_ARG, "src and sink must be non-null");
+  if (bytes % 16 != 0 || misaligned(src) || (reinterpret_cast<uintptr_t>(sink) & 3))
+    return fail(h, LIN_ERR_UNSUPPORTED, "bytes % 16 == 0, src 16-byte and sink 4-byte aligned");
+  if (grid == 0) grid = 1024;
+  if (grid < 1 || grid > (1 << 20))
+    return fail(h, LIN_ERR_INVALID_ARG, "grid must be in 1 .. 2^20 (0 = 1024)");
+  if (unroll != 4 && unroll != 8 && unroll != 16)
+    return fail(h, LIN_ERR_INVALID_ARG, "unroll must be 4, 8 or 16");
+  hipError_t e = lg::launch_stream_read(src, bytes, grid, unroll, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(h, e, "stream read launch");
   return LIN_OK;
 }
 

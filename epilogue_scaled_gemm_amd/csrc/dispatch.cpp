@@ -74,10 +74,15 @@ bool parse_variant(const std::string& spec, Variant* out, std::string* err) {
     else if (k == "rows") v.rows = xi;
     else if (k == "dq") v.dq = xi ? 1 : 0;
     else if (k == "xs") v.xs = xi ? 1 : 0;
+    else if (k == "sk") v.sk = xi;
     else { *err = "unknown key '" + k + "'"; return false; }
   }
   if (v.kind == V_TILE && !tile_supported(0, v.bm, v.bn, v.wm, v.wn)) {
     *err = "tile shape not compiled: " + spec;
+    return false;
+  }
+  if (v.kind == V_TILE && v.sk > 8) {
+    *err = "stream-K sk must be 0 (off) or 1..8 workgroups per CU: " + spec;
     return false;
   }
   if ((v.kind == V_PP || v.kind == V_TILE) && (v.split > 16 || (v.split & (v.split - 1)) != 0)) {
@@ -103,7 +108,8 @@ std::string format_variant(const Variant& v, int split) {
   if (v.kind == V_TILE) {
     os << "tile bm=" << v.bm << " bn=" << v.bn << " wm=" << v.wm << " wn=" << v.wn
        << " group=" << v.group_m;
-    if (split > 1) os << " split=" << split;
+    if (v.sk > 0) os << " sk=" << v.sk;
+    else if (split > 1) os << " split=" << split;
   } else if (v.kind == V_PP) {
     os << "pp split=" << split << " group=" << v.group_m;
   } else {

@@ -274,6 +274,12 @@ __device__ __forceinline__ void decode_body(
   // bytes (lanes out of range write zeros).
   constexpr int XSB = STEPB * XR;
   const int xs_chunks = (int)M * (XSB / 16);  // 16-byte chunks per step
+  // With 8 pieces of 16 bytes per token and step, piece p of token t sits at
+  // position p ^ xsw(t): the 16 lanes that read one piece of 16 tokens (and
+  // the 32 lanes of two lane groups) then hit distinct bank groups instead
+  // of the same few (token rows are 128 bytes apart).
+  constexpr bool XSW = XSB == 128;
+  auto xsw = [](int t) { return XSW ? (t & 7) ^ (((t >> 3) & 1) * 7) : 0; };
   const int XSL = (xs_chunks + 63) / 64 * 1024;
   uint8_t* xsl = dq_lds + (int64_t)wave * U * XSL;
   const __amdgpu_buffer_rsrc_t xrs =
@@ -341,7 +347,7 @@ __device__ __forceinline__ void decode_body(
         xok[u][1] = ok1;
         for (int i = 0; i * 64 < xs_chunks; ++i) {
           const int q = i * 64 + lane;
-          const int tq = q / (XSB / 16), pq = q - tq * (XSB / 16);
+          const int tq = q / (XSB / 16), pq = (q - tq * (XSB / 16)) ^ xsw(tq);
           const int voff = q < xs_chunks ? (int)(tq * KB * XR + (int64_t)st * XSB + pq * 16)
                                          : 0x7FFFFFF0;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -392,13 +398,16 @@ __device__ __forceinline__ void decode_body(
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
         const int64_t tok = min((int64_t)(tt * 16 + l16), M - 1);
-        const uint8_t* xr = xsl + (int64_t)u * XSL + tok * XSB + g * 32 * XR;
         if constexpr (MX) {
+          const uint8_t* xr = xsl + (int64_t)u * XSL + tok * XSB + g * 32 * XR;
 #pragma unroll
           for (int j = 0; j < 8; ++j)
             xb[u][tt].v[j] = ld16(xr + 16 * j, j < 4 ? xok[u][0] : xok[u][1]);
         } else {
-          xb[u][tt] = cat(ld16(xr, xok[u][0]), ld16(xr + 16, xok[u][1]));
+          const uint8_t* xt = xsl + (int64_t)u * XSL + tok * XSB;
+          const int sw = xsw((int)tok);
+          xb[u][tt] = cat(ld16(xt + (((2 * g) ^ sw) << 4), xok[u][0]),
+                          ld16(xt + (((2 * g + 1) ^ sw) << 4), xok[u][1]));
         }
       }
   };

@@ -1,5 +1,6 @@
 // kernels_misc.hip -- the two elementwise kernels of the unfused three-kernel
-// path (measurement baseline) and a zero-fill kernel.
+// path (measurement baseline), a plain streaming read (the measured HBM read
+// ceiling) and a zero-fill kernel.
 //
 // The unfused path is the one the opacity-barrier section of "Совместная
 // работа Helion и TorchInductor: слияние операторов" describes and its
@@ -7,6 +8,10 @@
 // a separate bias + GELU kernel whose output is materialised again, then
 // re-read to scale and add the residual.  It exists to measure the HBM bytes
 // the fused epilogue saves; it is not used by lin_gemm_run.
+#include <mutex>
+#include <set>
+#include <utility>
+
 #include "launch.hpp"
 
 namespace lg {
@@ -87,6 +92,31 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(i32x4* __restrict__ p, i
 
 inline unsigned blocks_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
 
+// A plain streaming read (measurement only): the HBM read rate the weight
+// stream of a decode call is compared with.  Thread t of the grid reads the
+// 16-byte chunks t, t + T, t + 2T, ... (T threads in all; consecutive
+// threads read consecutive chunks), U of them issued before any is used,
+// and folds them with XOR.  The result is stored only when it equals one
+// fixed value, so the loads cannot be dropped and nothing is written in
+// practice.
+template <int U>
+__global__ __launch_bounds__(256) void stream_read_kernel(const i32x4* __restrict__ src,
+                                                          int64_t n16, int* __restrict__ sink) {
+  const int64_t T = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  i32x4 x = {0, 0, 0, 0};
+  for (; i + (U - 1) * T < n16; i += U * T) {
+    i32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[i + u * T];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u];
+  }
+  for (; i < n16; i += T) x ^= src[i];
+  const int r = x[0] ^ x[1] ^ x[2] ^ x[3];
+  if (r == 0x2545F491) sink[threadIdx.x] = r;
+}
+
 }  // namespace
 
 hipError_t launch_bias_act(const void* T, const void* bias, void* U, int64_t M, int64_t N,
@@ -125,6 +155,34 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   if (threads == 0) return hipSuccess;
   hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks_for(threads)), dim3(256), 0, s, (i32x4*)p,
                      n16, tail, ntail);
+  return hipGetLastError();
+}
+
+hipError_t opt_in_lds(const void* fn, size_t bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({fn, dev})) return hipSuccess;
+  err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (err == hipSuccess) done.insert({fn, dev});
+  return err;
+}
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, int grid, int unroll, int* sink,
+                              hipStream_t s) {
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const dim3 g((unsigned)grid), b(256);
+  const i32x4* p = (const i32x4*)src;
+  switch (unroll) {
+    case 4: hipLaunchKernelGGL(stream_read_kernel<4>, g, b, 0, s, p, n16, sink); break;
+    case 8: hipLaunchKernelGGL(stream_read_kernel<8>, g, b, 0, s, p, n16, sink); break;
+    case 16: hipLaunchKernelGGL(stream_read_kernel<16>, g, b, 0, s, p, n16, sink); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -48,8 +48,13 @@ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 // 64-byte rows (4 chunks): distinct for any 16 consecutive rows under both a
 // 128-byte and a 256-byte LDS access width.
 __device__ inline int swz4(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
-// 128-byte rows (8 chunks).
-__device__ inline int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// 128-byte rows (8 chunks), read as chunk 4 h + g by lane group g (h the
+// half stage): rows r and r + 8 use complementary patterns, so the 32 lanes
+// of two lane groups (16 rows x 2 chunks) fall on 32 distinct 16-byte bank
+// groups of a 512-byte window as well as 16 lanes on 16 of a 256-byte one.
+// (r & 7) ^ (r >> 3 & 1) measured 4 bank-conflict cycles per fragment read
+// (SQ_LDS_BANK_CONFLICT = 4 x SQ_INSTS_LDS on the 2048-token block FP8 call).
+__device__ inline int swz8(int r) { return (r & 7) ^ (((r >> 3) & 1) * 7); }
 
 __device__ inline void tile_coords(int tiles_m, int tiles_n, int group_m, int BM, int BN, int64_t* m0,
                                    int64_t* n0) {
@@ -366,19 +371,10 @@ __global__ __launch_bounds__(512, 1) void bpp_kernel(const uint8_t* __restrict__
   }
 }
 
-template <typename F>
-hipError_t set_lds(F* fn, size_t bytes, bool* done) {
-  if (*done) return hipSuccess;
-  hipError_t err = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (err == hipSuccess) *done = true;
-  return err;
-}
-
 template <int QK>
 hipError_t launch_pp_q(const Variant& v, const Call& c, hipStream_t s) {
   constexpr size_t lds = 3 * (256 + 256) * 64;
-  static bool done = false;
-  hipError_t err = set_lds(pp_kernel<QK>, lds, &done);
+  hipError_t err = opt_in_lds((const void*)pp_kernel<QK>, lds);
   if (err != hipSuccess) return err;
   const int tiles_m = (int)((c.M + 255) / 256), tiles_n = (int)((c.N + 255) / 256);
   const int group_m = v.group_m > 0 ? v.group_m : 4;
@@ -422,8 +418,7 @@ hipError_t launch_pp(const Variant& v, const Call& c, int split, hipStream_t s) 
     case QK_I8: return launch_pp_q<QK_I8>(v, c, s);
     case QK_FP8_BLOCK: {
       constexpr size_t lds = 3 * (256 + 128) * 128;
-      static bool done = false;
-      hipError_t err = set_lds(bpp_kernel, lds, &done);
+      hipError_t err = opt_in_lds((const void*)bpp_kernel, lds);
       if (err != hipSuccess) return err;
       const int tiles_m = (int)((c.M + 255) / 256), tiles_n = (int)((c.N + 127) / 128);
       const int group_m = v.group_m > 0 ? v.group_m : 4;

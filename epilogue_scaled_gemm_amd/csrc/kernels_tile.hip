@@ -393,6 +393,110 @@ __global__ __launch_bounds__(WM * WN * 64) void tile_kernel(
   tile_body<QK, BM, BN, WM, WN>(A, B, M, N, KB, m0, n0, e, kt0, kt1, part);
 }
 
+// ---------------------------------------------------------------- stream-K
+//
+// For shapes whose tile count leaves CUs idle (or gives an uneven last wave
+// of tiles), the stream-K form of the split-K idea in
+// "helion-vllm-linear-backend" (sections "Зачем трогать линейные слои" and
+// "Одно ядро вместо трёх вариантов"): the tiles' K stages form one sequence
+// of T x KT units, and P persistent workgroups take equal contiguous runs of
+// it, so every CU has the same amount of MFMA work whatever T is.  Tiles
+// [0, T_dp) go whole to one workgroup each first (data-parallel part); the
+// remaining tiles' units are divided among the other P workgroups.  A tile
+// that one workgroup covers entirely gets the fused epilogue at once; a
+// tile split between workgroups gets each piece's raw accumulator written
+// to slice (workgroup - first workgroup of the tile) of a [slices][M][N]
+// workspace, and the fix-up kernel sums the slices in order and runs the
+// epilogue (deterministic, no waiting between workgroups).
+
+// First unit of stream-K workgroup j of P over `total` units.
+__device__ __host__ inline int64_t sk_begin(int64_t j, int64_t total, int64_t P) {
+  return j * total / P;
+}
+
+// The stream-K workgroup whose run holds unit u.
+__device__ inline int64_t sk_owner(int64_t u, int64_t total, int64_t P) {
+  int64_t j = u * P / total;
+  while (j + 1 < P && sk_begin(j + 1, total, P) <= u) ++j;
+  while (j > 0 && sk_begin(j, total, P) > u) --j;
+  return j;
+}
+
+__device__ inline void sk_tile_coords(int t, int tiles_m, int tiles_n, int group_m, int BM, int BN,
+                                      int64_t* m0, int64_t* n0) {
+  const int gsz = group_m * tiles_n;
+  const int grp = t / gsz;
+  const int first_m = grp * group_m;
+  const int gm = min(tiles_m - first_m, group_m);
+  const int within = t - grp * gsz;
+  *m0 = (int64_t)(first_m + within % gm) * BM;
+  *n0 = (int64_t)(within / gm) * BN;
+}
+
+template <int QK, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void tile_sk_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, int64_t M, int64_t N,
+    int64_t KB, int tiles_m, int tiles_n, int group_m, Epi e, int KT, int t_dp, int P,
+    void* __restrict__ ws) {
+  using AccT = typename QTraits<QK>::Acc;
+  const int T = tiles_m * tiles_n;
+  // Units: tile t's K stages are t KT .. t KT + KT - 1.  Workgroup g < t_dp
+  // takes data-parallel tile g whole; workgroup t_dp + j takes run j of the
+  // stream-K units [t_dp KT, T KT).  One tile_body call site (it is large).
+  const int64_t j = (int64_t)blockIdx.x - t_dp;
+  const int64_t sk0 = (int64_t)t_dp * KT, total = (int64_t)(T - t_dp) * KT;
+  int64_t u0, u1;
+  if (j < 0) {
+    u0 = (int64_t)blockIdx.x * KT;
+    u1 = u0 + KT;
+  } else {
+    u0 = sk0 + sk_begin(j, total, P);
+    u1 = sk0 + sk_begin(j + 1, total, P);
+  }
+  for (int64_t u = u0; u < u1;) {
+    const int t = (int)(u / KT);
+    const int64_t tb = (int64_t)t * KT;
+    const int k0 = (int)(u - tb), k1 = (int)(min(u1, tb + KT) - tb);
+    int64_t m0, n0;
+    sk_tile_coords(t, tiles_m, tiles_n, group_m, BM, BN, &m0, &n0);
+    AccT* part = nullptr;
+    if (k0 != 0 || k1 != KT) part = (AccT*)ws + (j - sk_owner(tb - sk0, total, P)) * M * N;
+    if (u != u0) __syncthreads();  // the previous tile is done with the LDS
+    tile_body<QK, BM, BN, WM, WN>(A, B, M, N, KB, m0, n0, e, k0, k1, part);
+    u = tb + k1;
+  }
+}
+
+// Fix-up: workgroup t sums the slices of stream-K tile t (if it was split)
+// in slice order, four consecutive columns per thread, then the epilogue.
+template <int QK, int BM, int BN>
+__global__ __launch_bounds__(256) void tile_sk_fixup(const void* __restrict__ ws, int tiles_m,
+                                                     int tiles_n, int group_m, int KT, int t_dp,
+                                                     int P, Epi e) {
+  using AccT = typename QTraits<QK>::Acc;
+  const int T = tiles_m * tiles_n;
+  const int t = blockIdx.x;
+  const int64_t total = (int64_t)(T - t_dp) * KT;
+  const int64_t tb = (int64_t)t * KT;
+  const int64_t g0 = sk_owner(tb, total, P), g1 = sk_owner(tb + KT - 1, total, P);
+  if (g0 == g1) return;  // one workgroup ran the whole tile and its epilogue
+  int64_t m0, n0;
+  sk_tile_coords(t_dp + t, tiles_m, tiles_n, group_m, BM, BN, &m0, &n0);
+  const AccT* w = (const AccT*)ws;
+  for (int q = threadIdx.x; q < BM * (BN / 4); q += 256) {
+    const int64_t m = m0 + q / (BN / 4), n = n0 + (q % (BN / 4)) * 4;
+    if (m >= e.M || n >= e.N) continue;
+    AccT v[4] = {0, 0, 0, 0};
+    for (int64_t sg = 0; sg <= g1 - g0; ++sg) {
+      const AccT* row = w + (sg * e.M + m) * e.N;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (n + i < e.N) v[i] += row[n + i];
+    }
+    epilogue_run<4, QTraits<QK>::out_f16>(e, m, n, v);
+  }
+}
+
 // The t-th BM-row tile of a token-sorted grouped layer, in expert order:
 // expert x's segment [lo, hi) (offsets clamped into [0, M], an end below
 // its start empty) holds tiles ceil((hi - lo) / BM); x = -1 when there are
@@ -451,18 +555,76 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_tile_kernel(
                                 (int64_t)blockIdx.x * BN, grouped_epi<QK>(e, x, r0, rows, KB));
 }
 
+// Stream-K launch geometry: P = sk x (CUs of the device) workgroups for the
+// stream-K part; the first T_dp tiles go whole to their own workgroups when
+// the tile count exceeds P (all but the last P..2P tiles), the rest split.
+struct SkPlan {
+  int tiles_m = 0, tiles_n = 0, KT = 0, t_dp = 0, P = 0, slices = 0;
+};
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+SkPlan sk_plan(const Variant& v, const Call& c) {
+  SkPlan p;
+  const int rb = c.qk == QK_MXFP4 ? 32 : ROWB;
+  p.tiles_m = (int)((c.M + v.bm - 1) / v.bm);
+  p.tiles_n = (int)((c.N + v.bn - 1) / v.bn);
+  p.KT = (int)((c.KB + rb - 1) / rb);
+  const int T = p.tiles_m * p.tiles_n;
+  const int P0 = std::max(1, v.sk * device_cus());
+  p.t_dp = T > 2 * P0 ? (T / P0 - 1) * P0 : 0;
+  const int64_t total = (int64_t)(T - p.t_dp) * p.KT;
+  // No workgroup without units: then every run holds at least upw >= 1
+  // units, a tile meets at most ceil(KT / upw) + 1 runs (and at most KT),
+  // and that bounds the slice index a piece is written to.
+  p.P = (int)std::min<int64_t>(P0, total);
+  const int64_t upw = total / p.P;
+  p.slices = (int)std::min<int64_t>(p.KT, (p.KT + upw - 1) / upw + 1);
+  return p;
+}
+
+template <int QK, int BM, int BN, int WM, int WN>
+hipError_t launch_t_sk(const Variant& v, const Call& c, hipStream_t s) {
+  using S = TileShape<BM, BN, WM, WN, QK == QK_MXFP4 ? 32 : ROWB>;
+  const size_t lds = 2 * (size_t)S::STAGE;
+  {
+    hipError_t err = opt_in_lds((const void*)tile_sk_kernel<QK, BM, BN, WM, WN>, lds);
+    if (err != hipSuccess) return err;
+  }
+  const SkPlan p = sk_plan(v, c);
+  const int group_m = v.group_m > 0 ? v.group_m : 4;
+  const int T = p.tiles_m * p.tiles_n;
+  const int grid = p.t_dp + p.P;
+  hipLaunchKernelGGL((tile_sk_kernel<QK, BM, BN, WM, WN>), dim3(grid), dim3(S::NT), lds, s,
+                     (const uint8_t*)c.A, (const uint8_t*)c.B, c.M, c.N, c.KB, p.tiles_m,
+                     p.tiles_n, group_m, c.epi, p.KT, p.t_dp, p.P, c.ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((tile_sk_fixup<QK, BM, BN>), dim3(T - p.t_dp), dim3(256), 0, s,
+                     (const void*)c.ws, p.tiles_m, p.tiles_n, group_m, p.KT, p.t_dp, p.P, c.epi);
+  return hipGetLastError();
+}
+
 template <int QK, int BM, int BN, int WM, int WN>
 hipError_t launch_t(const Variant& v, const Call& c, int split, hipStream_t s) {
   using S = TileShape<BM, BN, WM, WN, QK == QK_MXFP4 ? 32 : ROWB>;
   const int tiles_m = (int)((c.M + BM - 1) / BM);
   const int tiles_n = (int)((c.N + BN - 1) / BN);
   const size_t lds = 2 * (size_t)S::STAGE;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t err = hipFuncSetAttribute((const void*)tile_kernel<QK, BM, BN, WM, WN>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    hipError_t err = opt_in_lds((const void*)tile_kernel<QK, BM, BN, WM, WN>, lds);
     if (err != hipSuccess) return err;
-    attr_done = true;
   }
   const int group_m = v.group_m > 0 ? v.group_m : 4;
   const int KT = (int)((c.KB + (QK == QK_MXFP4 ? 32 : ROWB) - 1) / (QK == QK_MXFP4 ? 32 : ROWB));
@@ -491,8 +653,26 @@ hipError_t launch_t(const Variant& v, const Call& c, int split, hipStream_t s) {
 // of 32 times the wave count.
 constexpr bool mx_shape_ok(int bn, int wm, int wn) { return bn % (32 * wm * wn) == 0; }
 
+// The tile shapes compiled in stream-K form.
+#define LG_SK_SHAPES(X) \
+  X(128, 128, 2, 2)     \
+  X(64, 128, 1, 4)      \
+  X(128, 128, 2, 4)     \
+  X(256, 128, 2, 4)     \
+  X(256, 256, 2, 4)
+
 template <int QK>
 hipError_t launch_q(const Variant& v, const Call& c, int split, hipStream_t s) {
+  if (v.sk > 0) {
+#define LG_SK_TRY(b_m, b_n, w_m, w_n)                                         \
+    if constexpr (QK != QK_MXFP4 || mx_shape_ok(b_n, w_m, w_n)) {              \
+      if (v.bm == b_m && v.bn == b_n && v.wm == w_m && v.wn == w_n)           \
+        return launch_t_sk<QK, b_m, b_n, w_m, w_n>(v, c, s);                  \
+    }
+    LG_SK_SHAPES(LG_SK_TRY)
+#undef LG_SK_TRY
+    return hipErrorInvalidValue;
+  }
 #define LG_TRY(b_m, b_n, w_m, w_n)                                          \
   if constexpr (QK != QK_MXFP4 || mx_shape_ok(b_n, w_m, w_n)) {              \
     if (v.bm == b_m && v.bn == b_n && v.wm == w_m && v.wn == w_n)           \
@@ -510,12 +690,9 @@ template <int QK, int BM, int BN, int WM, int WN>
 hipError_t launch_gt(const Call& c, const int* offsets, int64_t E, hipStream_t s) {
   using S = TileShape<BM, BN, WM, WN, QK == QK_MXFP4 ? 32 : ROWB>;
   const size_t lds = 2 * (size_t)S::STAGE;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t err = hipFuncSetAttribute((const void*)grouped_tile_kernel<QK, BM, BN, WM, WN>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    hipError_t err = opt_in_lds((const void*)grouped_tile_kernel<QK, BM, BN, WM, WN>, lds);
     if (err != hipSuccess) return err;
-    attr_done = true;
   }
   const int64_t tiles_n = (c.N + BN - 1) / BN;
   const int64_t slots = (c.M + BM - 1) / BM + std::min<int64_t>(E, c.M);
@@ -567,6 +744,14 @@ bool tile_supported(int qk, int bm, int bn, int wm, int wn) {
   return false;
 }
 
+bool tile_sk_supported(int qk, int bm, int bn, int wm, int wn) {
+#define LG_HAS(b_m, b_n, w_m, w_n) \
+  if (bm == b_m && bn == b_n && wm == w_m && wn == w_n) return qk != QK_MXFP4 || mx_shape_ok(bn, wm, wn);
+  LG_SK_SHAPES(LG_HAS)
+#undef LG_HAS
+  return false;
+}
+
 // Split K while the grid has fewer than 512 workgroups, every slice keeps at
 // least 8 K stages, and the partials' round trip (split x M x N x 8 bytes)
 // stays within the weight's bytes (N x KB).  Measured on MI355X (fp8, bf16,
@@ -583,12 +768,15 @@ int tile_auto_split(const Variant& v, const Call& c) {
   return split;
 }
 
-size_t tile_ws_bytes(const Call& c, int split) {
+size_t tile_ws_bytes(const Variant& v, const Call& c, int split) {
+  if (v.sk > 0) return (size_t)sk_plan(v, c).slices * (size_t)c.M * (size_t)c.N * 4;
   return split <= 1 ? 0 : (size_t)split * (size_t)c.M * (size_t)c.N * 4;
 }
 
 hipError_t launch_tile(const Variant& v, const Call& c, int split, hipStream_t s) {
-  if (split < 1 || split > 16 || (split > 1 && !c.ws)) return hipErrorInvalidValue;
+  if (split < 1 || split > 16 || ((split > 1 || v.sk > 0) && !c.ws)) return hipErrorInvalidValue;
+  if (v.sk > 0 && (v.sk > 8 || (int64_t)((c.M + v.bm - 1) / v.bm) * ((c.N + v.bn - 1) / v.bn) > 0x7FFFFFFF / 2))
+    return hipErrorInvalidValue;
   switch (c.qk) {
     case QK_BF16: return launch_q<QK_BF16>(v, c, split, s);
     case QK_FP16: return launch_q<QK_FP16>(v, c, split, s);

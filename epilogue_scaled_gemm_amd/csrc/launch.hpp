@@ -20,6 +20,9 @@ struct Variant {
   // (the ping-pong family has a fixed tile per quant mode and uses only
   // group_m and split; split = 0 picks the split-K factor from the shape)
   int bm = 128, bn = 128, wm = 2, wn = 2, group_m = 4;
+  // tile family: sk > 0 = stream-K over sk x (CU count) persistent
+  // workgroups (split is then unused), 0 = one workgroup per tile / split
+  int sk = 0;
   // decode family (M <= 32): swap-AB orientation, split-K factor across
   // workgroups (0 = choose from the shape), reduction, waves per workgroup
   // (the in-workgroup K split), steps of 128 bytes loaded per batch, and
@@ -50,8 +53,12 @@ struct Call {
 // into c.ws ([split][M][N] fp32 / int32, tile_ws_bytes), then the two-pass
 // reduction with the epilogue.
 bool tile_supported(int qk, int bm, int bn, int wm, int wn);
+// Whether the tile shape is compiled in stream-K form (v.sk > 0).
+bool tile_sk_supported(int qk, int bm, int bn, int wm, int wn);
 int tile_auto_split(const Variant& v, const Call& c);
-size_t tile_ws_bytes(const Call& c, int split);
+// Workspace of a tile call: split-K slices [split][M][N], or the stream-K
+// slices [slices][M][N] (v.sk > 0), of fp32 / int32 partials.
+size_t tile_ws_bytes(const Variant& v, const Call& c, int split);
 hipError_t launch_tile(const Variant& v, const Call& c, int split, hipStream_t s);
 
 // Grouped tile form (a mixture-of-experts layer with prefill-sized
@@ -108,6 +115,16 @@ hipError_t launch_bias_act(const void* T, const void* bias, void* U, int64_t M, 
 hipError_t launch_scale_residual(const void* U, const void* residual, void* C, int64_t M,
                                  int64_t N, float alpha, bool f16, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// Raise kernel fn's dynamic-LDS limit to `bytes` on the current device, once
+// per (kernel, device): the attribute is held per device, so a process
+// that launches on several GPUs sets it on each (kernels_misc.hip).
+hipError_t opt_in_lds(const void* fn, size_t bytes);
+// Measurement only: read `bytes` (a multiple of 16) at src with `grid`
+// workgroups of 256 threads, `unroll` (4, 8 or 16) 16-byte loads in flight
+// per thread; sink (256 ints) is written only in the practically impossible
+// case that the XOR of the data equals a fixed value.
+hipError_t launch_stream_read(const void* src, int64_t bytes, int grid, int unroll, int* sink,
+                              hipStream_t s);
 // Dynamic activation quantization (kernels_quant.hip): X[M][K] 16-bit floats
 // -> Q[M][K] codes and fp32 scales, per token ([M]) or per 1x128 block
 // ([M][K/128]).  K % 16 == 0 (K % 128 == 0 for blocks), M >= 1.

@@ -1,5 +1,6 @@
 """Offline sweep: time candidate variants per shape on the GPU and write the
-shape-keyed variant table (configs/mi355x.cfg).
+shape-keyed variant table (a text table for lin_gemm_create / LIN_GEMM_CONFIG
+with --out, and the built-in csrc/table_mi355x.inc with --emit-inc).
 
 The per-shape search of the vLLM linear-backend write-up (sections "Одно
 ядро вместо трёх вариантов" and "Как автотюнер ищет конфиги") benchmarks
@@ -13,7 +14,9 @@ over a rotation of weight copies larger than the 256 MB MALL.
         [--all-m] [--dynamic] [--emit-inc PATH]
 
 --all-m sweeps every token count 1..32 of the decode workloads (not only the
-workloads' own list); --dynamic also times lin_gemm_run_dynamic with the
+workloads' own list); --ms sweeps a given token list instead (each swept count
+then covers the counts above the previous one up to itself); --merge with --emit-inc replaces only the overlapping entries of the
+existing include; --dynamic also times lin_gemm_run_dynamic with the
 winning decode variant with and without the quantization prologue (dq=1)
 and keeps the prologue where it is faster; --emit-inc writes the measured
 entries as the C++ include that the library compiles in as its built-in
@@ -57,6 +60,11 @@ TILE_CANDIDATES = ["tile bm=256 bn=256 wm=2 wn=2", "tile bm=128 bn=256 wm=2 wn=2
                    "tile bm=256 bn=256 wm=2 wn=4", "tile bm=256 bn=128 wm=2 wn=4",
                    "tile bm=128 bn=128 wm=2 wn=4", "pp split=1 group=4", "pp split=2 group=4",
                    "pp split=4 group=4", "pp split=8 group=4"]
+# Stream-K tile variants (sk = persistent workgroups per CU).
+SK_CANDIDATES = [f"tile bm={bm} bn={bn} wm={wm} wn={wn} sk={sk}"
+                 for bm, bn, wm, wn in ((128, 128, 2, 2), (64, 128, 1, 4), (128, 128, 2, 4),
+                                        (256, 128, 2, 4), (256, 256, 2, 4))
+                 for sk in (1, 2)]
 
 
 def _dev(torch, a):
@@ -148,8 +156,58 @@ def merge_ranges(entries):
     return out
 
 
+def sparse_ranges(entries):
+    """Entries of a sweep over a sparse token list (e.g. 64, 128, ... 2048 above
+    the decode range): each swept count M covers the counts above the
+    previous swept one up to M (the first from 33, or from itself at or below
+    32); counts above the largest keep the table's other entries."""
+    out = []
+    by = {}
+    for q, M, N, K, spec, t in entries:
+        by.setdefault((q, N, K), []).append((M, spec, t))
+    for (q, N, K), rows in by.items():
+        rows.sort()
+        prev = None
+        for i, (M, spec, t) in enumerate(rows):
+            lo = (prev + 1) if prev is not None else (33 if M > 32 else M)
+            hi = M
+            out.append((q, lo, hi, N, K, spec, [t]))
+            prev = M
+    return out
+
+
+def merge_inc(path, new_lines, log=print):
+    """Rewrite the table include at `path`: the new entries replace existing
+    ones of the same (quant, N, K) whose token ranges overlap them; the
+    other existing entries stay, in their order, before the new ones."""
+    def key(line):
+        f = line.split("#", 1)[0].split()
+        if len(f) < 6:
+            return None
+        hi = 1 << 40 if f[2] == "*" else int(f[2])
+        return f[0], int(f[1]), hi, f[3], f[4]
+    text = open(path).read() if os.path.exists(path) else ""
+    body = text.split('R"TABLE(', 1)[1].split(')TABLE"', 1)[0] if 'R"TABLE(' in text else ""
+    old = [l for l in body.splitlines() if l.strip() and not l.lstrip().startswith("#")]
+    new_keys = [key(l) for l in new_lines]
+    kept = []
+    for l in old:
+        k = key(l)
+        if k and any(k[0] == n[0] and k[3] == n[3] and k[4] == n[4] and k[1] <= n[2] and n[1] <= k[2]
+                     for n in new_keys):
+            continue
+        kept.append(l)
+    with open(path, "w") as f:
+        f.write("// Measured entries of the built-in variant table, written by\n"
+                "// epilogue_scaled_gemm_amd.sweep (graph replay over rotating weight\n"
+                "// copies on an MI355X); microseconds per call in the comments.\n"
+                "R\"TABLE(\n# quant        m_lo  m_hi  N      K      variant\n"
+                + "\n".join(kept + list(new_lines)) + "\n)TABLE\"\n")
+    log(f"merged {len(new_lines)} entries into {path} ({len(kept)} kept)")
+
+
 def sweep(workloads, out_path, reps, log=print, max_m=None, all_m=False, dynamic=False,
-          emit_inc=None, quant=None):
+          emit_inc=None, quant=None, ms=None, merge=False):
     import torch
     import synth
     import epilogue_scaled_gemm_amd as lg
@@ -173,17 +231,17 @@ def sweep(workloads, out_path, reps, log=print, max_m=None, all_m=False, dynamic
         del src, dst
     for cfg in workloads:
         c = synth.WORKLOADS[cfg]
-        ms = list(c["Ms"])
-        if all_m and min(ms) <= 32:
-            ms = sorted(set(ms) | set(range(1, 33)))
-        for M in ms:
+        ms_w = list(c["Ms"]) if not ms else list(ms)
+        if all_m and min(ms_w) <= 32:
+            ms_w = sorted(set(ms_w) | set(range(1, 33)))
+        for M in ms_w:
             if max_m is not None and M > max_m:
                 continue
             p = synth.make(cfg, M, quant)
             ops = {k: _dev(torch, v) for k, v in p.operands().items() if k != "alpha"}
             ncopy = max(2, min(32, -(-ROTATION_BYTES // p.B.nbytes)))
             Bs = [ops["B"]] + [ops["B"].clone() for _ in range(ncopy - 1)]
-            cands = DECODE_CANDIDATES if M <= 32 else TILE_CANDIDATES
+            cands = DECODE_CANDIDATES if M <= 32 else TILE_CANDIDATES + SK_CANDIDATES
             if p.quant in ("fp8_dynamic", "mxfp4", "w8a8_int8", "block_fp8", "bf16", "fp16"):
                 cands = cands + XS_CANDIDATES
             # Warm every candidate first (the handle's split-K workspace only
@@ -234,11 +292,13 @@ def sweep(workloads, out_path, reps, log=print, max_m=None, all_m=False, dynamic
             del Bs, ops
             torch.cuda.empty_cache()
     h.close()
-    merged = merge_ranges(entries)
+    merged = sparse_ranges(entries) if ms else merge_ranges(entries)
     measured = [f"{q:<12} {lo:<5} {hi:<5} {N:<6} {K:<6} {spec}   # "
                 + ", ".join(f"{t * 1e6:.2f}" for t in ts) + " us"
                 for q, lo, hi, N, K, spec, ts in merged]
-    if emit_inc:
+    if emit_inc and merge:
+        merge_inc(emit_inc, measured, log)
+    elif emit_inc:
         with open(emit_inc, "w") as f:
             f.write("// Measured entries of the built-in variant table, written by\n"
                     "// epilogue_scaled_gemm_amd.sweep (graph replay over rotating weight\n"
@@ -279,10 +339,17 @@ def main():
     ap.add_argument("--emit-inc", default=None, help="write the measured entries as C++ include")
     ap.add_argument("--quant", default=None,
                     help="run the workloads in this quant mode (same draws), e.g. fp16")
+    ap.add_argument("--merge", action="store_true",
+                    help="with --emit-inc: replace only the overlapping entries of the existing "
+                         "include, keep the rest")
+    ap.add_argument("--ms", default=None,
+                    help="token counts to sweep instead of each workload's own list, e.g. "
+                         "64,128,256,512,1024,2048")
     a = ap.parse_args()
     sweep([int(x) for x in a.workloads.split(",")], a.out, a.reps,
           log=lambda s: print(s, flush=True), max_m=a.max_m, all_m=a.all_m, dynamic=a.dynamic,
-          emit_inc=a.emit_inc, quant=a.quant)
+          emit_inc=a.emit_inc, quant=a.quant,
+          ms=[int(x) for x in a.ms.split(",")] if a.ms else None, merge=a.merge)
 
 
 if __name__ == "__main__":

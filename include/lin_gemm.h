@@ -183,6 +183,21 @@ int lin_gemm_run_unfused(lin_gemm_t h, const void *A, const void *B, const void 
                          int64_t N, int64_t K, float alpha, int quant_mode, int activation,
                          void *stream);
 
+/* Measurement only (like lin_gemm_run_unfused): a plain streaming read of
+ * `bytes` bytes of device memory at src, the HBM read rate that the weight
+ * stream of a decode call is measured against.  The section "Зачем трогать
+ * линейные слои" of "helion-vllm-linear-backend" describes small-M linear
+ * layers as bound by reading the weight; this gives the rate a kernel that
+ * does nothing but read reaches for the same byte count.  grid workgroups
+ * of 256 threads (0 = 1024), each thread keeping `unroll` (4, 8 or 16)
+ * 16-byte loads in flight; consecutive threads read consecutive 16-byte
+ * chunks.  sink: 256 ints of caller device memory, written only in the
+ * practically impossible case that the XOR of the data equals one fixed
+ * value.  bytes % 16 == 0, src 16-byte aligned (else LIN_ERR_UNSUPPORTED);
+ * bytes == 0 is a no-op.  Enqueued on `stream`; no allocation. */
+int lin_gemm_stream_read(lin_gemm_t h, const void *src, int64_t bytes, int grid, int unroll,
+                         int *sink, void *stream);
+
 /* Dynamic activation quantization: the step that produces A and the
  * activation scales of the quantised modes from 16-bit activations at run
  * time.  "helion-vllm-linear-backend", section "Одно ядро вместо трёх

@@ -156,12 +156,36 @@ def test_table_file(tmp_path):
         lg.Handle(str(tmp_path / "missing.cfg"))
 
 
-def test_shipped_table_parses():
-    path = os.path.join(os.path.dirname(lg.__file__), "configs", "mi355x.cfg")
-    if not os.path.exists(path):
-        pytest.skip("no shipped table yet")
-    h = lg.Handle(path)
-    h.close()
+def test_built_in_table_parses_as_a_text_table(tmp_path, cpu_handle):
+    # The sweep-written entries compiled into the library (csrc/table_mi355x.inc)
+    # load through lin_gemm_create as a text table too, and every entry is
+    # what lin_gemm_describe reports for its first token count.
+    inc = os.path.join(os.path.dirname(lg.__file__), "csrc", "table_mi355x.inc")
+    text = open(inc).read()
+    body = text.split('R"TABLE(', 1)[1].split(')TABLE"', 1)[0]
+    cfg = tmp_path / "table.cfg"
+    cfg.write_text(body)
+    h = lg.Handle(str(cfg))
+    try:
+        n = 0
+        for line in body.splitlines():
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            q, lo, hi, N, K, *spec = line.split()
+            got = h.describe(q, int(lo), int(N), int(K))
+            want = " ".join(spec)
+            # describe drops staging / prefetching where the shape cannot use
+            # it and prints the split it resolves to; the kernel family and
+            # the launch shape must match.
+            assert got.split()[0] == want.split()[0]
+            for key in ("waves", "unroll", "rows", "bm", "bn"):
+                if f"{key}=" in want:
+                    assert f"{key}={want.split(key + '=')[1].split()[0]}" in got, (line, got)
+            n += 1
+        assert n > 10
+    finally:
+        h.close()
 
 
 def _raw_quantize(h, X=FAKE, x_dtype=0, M=4, K=256, kind=0, Q=FAKE, S=FAKE):

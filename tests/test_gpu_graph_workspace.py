@@ -51,3 +51,48 @@ def test_captured_graph_survives_workspace_growth(small_spec, big_spec):
     finally:
         h.set_force(None)
         h.close()
+
+
+def test_atomic_replay_after_other_split_calls():
+    # A graph holding an atomic-reduction decode call, replayed after eager
+    # split-K calls (tile and two-pass) have left partials in the same
+    # handle workspace: the zero fill travels with the captured call, so
+    # every replay still matches the oracle.
+    h = lg.Handle()
+    try:
+        dec = synth.make_custom("fp8_dynamic", "silu", 8, 1024, 4096, seed=5, bias=True)
+        til = synth.make_custom("fp8_dynamic", "none", 96, 1024, 4096, seed=6)
+        dd, dt = upload(dec), upload(til)
+        Cd = torch.empty((dec.M, dec.N), dtype=torch.int16, device="cuda")
+        Ct = torch.empty((til.M, til.N), dtype=torch.int16, device="cuda")
+
+        def call(p, d, C):
+            h.run(d["A"], d["B"], C, quant=p.quant, act=p.act, sa=d["sa"], sb=d["sb"],
+                  alpha=p.alpha, bias=d["bias"], residual=d["residual"])
+
+        # size the workspace for the largest user first, so nothing grows later
+        h.set_force("tile bm=64 bn=128 wm=1 wn=4 split=8")
+        call(til, dt, Ct)
+        atomic = "decode swap=1 split=4 reduce=atomic waves=8 unroll=2 rows=16"
+        h.set_force(atomic)
+        call(dec, dd, Cd)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call(dec, dd, Cd)
+        ref, _ = reference(dec)
+        for spec in ("tile bm=64 bn=128 wm=1 wn=4 split=8",
+                     "decode swap=1 split=4 reduce=twopass waves=8 unroll=2 rows=16"):
+            h.set_force(spec)
+            call(til if spec.startswith("tile") else dec, dt if spec.startswith("tile") else dd,
+                 Ct if spec.startswith("tile") else Cd)
+            torch.cuda.synchronize()
+            Cd.fill_(0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert_close(decode_out(Cd, dec.quant), ref, f"atomic replay after [{spec}]")
+        del g
+    finally:
+        h.set_force(None)
+        h.close()
