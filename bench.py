@@ -37,6 +37,7 @@ HBM_PEAK = 8.0e12                                     # bytes/s
 MFMA_PEAK = {"bf16": 2.5e15, "fp16": 2.5e15, "fp8_dynamic": 5.0e15, "block_fp8": 5.0e15,
              "w8a8_int8": 5.0e15, "mxfp4": 2.5e15}
 RIDGE = {q: MFMA_PEAK[q] / HBM_PEAK for q in MFMA_PEAK}
+E4M3_WIDENED = ("fp8_dynamic", "block_fp8")            # contracted by the bf16 MFMA
 HEAD_CFG = 2
 NCOPY_TARGET_BYTES = 384 << 20                        # rotation footprint > 256 MB MALL
 METRIC = "TFLOP/s & HBM TB/s (fraction of roofline) per shape, M∈{1..32} and M=4096"
@@ -209,11 +210,16 @@ def shape_row(name, quant, M, N, K, t, nbytes, flops, variant, kernel_calls=1):
     ai = flops / nbytes
     bound = "mfma" if ai > RIDGE[quant] else "hbm"
     tbs, tfs = nbytes / t, flops / t
-    return dict(shape=name, quant=quant, M=M, N=N, K=K, variant=variant, us=round(t * 1e6, 3),
-                TBps=round(tbs / 1e12, 4), TFLOPs=round(tfs / 1e12, 3),
-                hbm_frac=round(tbs / HBM_PEAK, 4), mfma_frac=round(tfs / MFMA_PEAK[quant], 4),
-                bound=bound, kernels_per_call=kernel_calls,
-                roof_frac=round((tbs / HBM_PEAK) if bound == "hbm" else (tfs / MFMA_PEAK[quant]), 4))
+    row = dict(shape=name, quant=quant, M=M, N=N, K=K, variant=variant, us=round(t * 1e6, 3),
+               TBps=round(tbs / 1e12, 4), TFLOPs=round(tfs / 1e12, 3),
+               hbm_frac=round(tbs / HBM_PEAK, 4), mfma_frac=round(tfs / MFMA_PEAK[quant], 4),
+               bound=bound, kernels_per_call=kernel_calls,
+               roof_frac=round((tbs / HBM_PEAK) if bound == "hbm" else (tfs / MFMA_PEAK[quant]), 4))
+    if quant in E4M3_WIDENED:
+        # e4m3 operands are widened exactly to bf16 and multiplied by the
+        # bf16 MFMA: the rate the kernels can reach is the bf16 one.
+        row["mfma_frac_bf16_rate"] = round(tfs / MFMA_PEAK["bf16"], 4)
+    return row
 
 
 CEILING_MIB = (12, 24, 48, 96)                       # the decode workloads' weight sizes

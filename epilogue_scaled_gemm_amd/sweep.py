@@ -45,7 +45,11 @@ DECODE_CANDIDATES = [
     for sp in (1, 2) for w, u, r in DECODE_SHAPES
 ] + ["decode swap=0 split=1 reduce=twopass waves=8 unroll=2",
      "decode swap=1 split=2 reduce=lastwg waves=8 unroll=1 rows=32",
-     "decode swap=1 split=2 reduce=atomic waves=8 unroll=1 rows=32"]
+     "decode swap=1 split=2 reduce=atomic waves=8 unroll=1 rows=32"] + [
+    # wider row groups split over K with the in-kernel reduction: fewer
+    # workgroups re-read each token's activations (larger token counts)
+    f"decode swap=1 split={sp} reduce=lastwg waves={w} unroll=1 rows={r}"
+    for sp in (2, 4) for w, r in ((8, 64), (4, 64), (8, 32))]
 # Staged activations (xs=1), compiled for some shapes per weight format
 # (a shape without it runs unstaged and simply times the same).
 XS_SHAPES = [(8, 1, 12), (8, 1, 16), (8, 2, 16), (8, 4, 12), (8, 4, 24), (12, 1, 16),

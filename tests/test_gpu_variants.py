@@ -102,6 +102,25 @@ def test_deterministic_reductions_repeat_bitwise(handle, reduce):
         handle.set_force(None)
 
 
+@pytest.mark.parametrize("reduce", ["lastwg", "atomic"])
+def test_cross_workgroup_arrival_exact_over_repeats(handle, reduce):
+    # The last-arrival protocol (partials stored and read at device scope, a
+    # wait for the stores' acknowledgement before the arrival increment): int8
+    # accumulators are exact whatever the summation order, so any partial
+    # that the last workgroup read before it was visible would show up as a
+    # wrong value.  Twenty calls, each compared with the oracle exactly.
+    p = synth.make(3, 16)
+    d = upload(p)
+    _, acc = oracle.linear(p.quant, "none", p.A, p.B, p.sa, p.sb)
+    try:
+        handle.set_force(f"decode swap=1 split=8 reduce={reduce} waves=8 unroll=1 rows=32")
+        for i in range(20):
+            C = run(handle, p, d, raw=True)
+            assert np.array_equal(C.cpu().numpy(), acc), f"{reduce}: call {i} differs"
+    finally:
+        handle.set_force(None)
+
+
 def test_swap_ab_equals_direct(handle):
     p = synth.make(3, 8)
     d = upload(p)
