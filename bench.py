@@ -619,12 +619,23 @@ def main():
     # tile up to M = 16, two up to 32), swap-AB, waves, unroll, 16-row weight
     # tiles per workgroup (1 up to 16 rows, 2 up to 32, else 4) and the
     # activation mode (0: every lane loads its e4m3 activations itself; 2:
-    # staged through LDS, "xs=1" in the variant).
+    # staged through LDS, "xs=1" in the variant; 3..6: widened once per wave
+    # into LDS, "xs=2", with 1, 2, 4 or 8 chunks of 16 bytes per lane: the
+    # smallest that holds M tokens x the wave's slice, whose steps of 128
+    # bytes are rounded up to a power of two of at least max(unroll, 2)).
     def kernel_name(M):
         v = dict(kv.split("=") for kv in h.describe(wl.quant, M, wl.N, wl.K).split()[1:])
         rows = int(v["rows"])
         rt = 1 if rows <= 16 else (2 if rows <= 32 else 4)
         am = 2 if v.get("xs") == "1" else 0
+        if v.get("xs") == "2":
+            steps = -(-wl.K // 128)
+            per = -(-steps // int(v["waves"]))
+            wst = max(int(v["unroll"]), 2)
+            while wst < per:
+                wst *= 2
+            rounds = -(-M * wst * 8 // 64)
+            am = 3 + next(i for i, r in enumerate((1, 2, 4, 8)) if rounds <= r)
         return (f"decode_kernel<2, {1 if M <= 16 else 2}, {'true' if v['swap'] == '1' else 'false'}"
                 f", {v['waves']}, {v['unroll']}, {rt}, {am}>")
     groups = {}

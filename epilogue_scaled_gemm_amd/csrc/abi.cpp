@@ -369,8 +369,9 @@ int run_impl(lin_gemm_t h, const void* A, const void* B, const lin_scales_t* sca
   } else if (v.kind == lg::V_PP) {
     e = lg::launch_pp(v, c, split, s);
   } else {
-    e = v.xs && lg::decode_xs_supported(v, c) ? lg::launch_decode_xs(v, c, split, s)
-                                               : lg::launch_decode(v, c, split, s);
+    if (v.xs == 2 && lg::decode_wd_supported(v, c, split)) e = lg::launch_decode_wd(v, c, split, s);
+    else if (v.xs && lg::decode_xs_supported(v, c)) e = lg::launch_decode_xs(v, c, split, s);
+    else e = lg::launch_decode(v, c, split, s);
   }
   if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
   if (std::getenv("LIN_GEMM_LOG")) {
@@ -458,9 +459,12 @@ int lin_gemm_describe(lin_gemm_t h, int quant_mode, int64_t M, int64_t N, int64_
   lg::Call c{};
   c.M = M; c.N = N; c.K = K; c.KB = b_row_bytes(quant_mode, K);
   c.qk = qkind(quant_mode);
-  // Report staged activations only where lin_gemm_run would use them.
-  if (v.xs && !lg::decode_xs_supported(v, c)) v.xs = 0;
-  std::string s = lg::format_variant(v, resolve_split(v, c));
+  // Report staged / widened activations only where lin_gemm_run would use
+  // them (the widened form falls back to staging, then to neither).
+  const int split = resolve_split(v, c);
+  if (v.xs == 2 && !lg::decode_wd_supported(v, c, split)) v.xs = 1;
+  if (v.xs == 1 && !lg::decode_xs_supported(v, c)) v.xs = 0;
+  std::string s = lg::format_variant(v, split);
   std::snprintf(buf, (size_t)buflen, "%s", s.c_str());
   return LIN_OK;
 }

@@ -73,7 +73,10 @@ bool parse_variant(const std::string& spec, Variant* out, std::string* err) {
     else if (k == "unroll") v.unroll = xi;
     else if (k == "rows") v.rows = xi;
     else if (k == "dq") v.dq = xi ? 1 : 0;
-    else if (k == "xs") v.xs = xi ? 1 : 0;
+    else if (k == "xs") {
+      if (xi > 2) { *err = "xs must be 0, 1 or 2: " + spec; return false; }
+      v.xs = xi;
+    }
     else if (k == "sk") v.sk = xi;
     else { *err = "unknown key '" + k + "'"; return false; }
   }
@@ -116,7 +119,7 @@ std::string format_variant(const Variant& v, int split) {
     os << "decode swap=" << v.swap << " split=" << split << " reduce=" << reduce_name(v.reduce)
        << " waves=" << v.waves << " unroll=" << v.unroll << " rows=" << v.rows;
     if (v.dq) os << " dq=1";
-    if (v.xs) os << " xs=1";
+    if (v.xs) os << " xs=" << v.xs;
   }
   return os.str();
 }

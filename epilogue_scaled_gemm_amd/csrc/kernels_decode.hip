@@ -85,6 +85,18 @@ constexpr bool op_wave(bool swap, int w) { return swap && w >= 8 && w < 16; }
 //             redundant global loads per distinct chunk by LDS broadcasts.
 //             Swap orientation.
 //  AM_QUANT   the quantization prologue below.
+//  AM_WIDEN   e4m3 activations, swap, one token tile: each wave widens the
+//             activations of its whole K range once, all M tokens at a
+//             time, to bf16 in its own slice of LDS (the activation loads
+//             are issued before the first weight batch, so they return
+//             first), and the lanes read ready-made bf16 fragments from
+//             there.  With fewer than 16 tokens the 16 lanes of a token tile
+//             hold copies of the same tokens, so per-lane widening repeats
+//             the same conversions up to 16 times; here each activation
+//             byte is widened once per wave.  Chunks outside the wave's
+//             range or past K are stored as zeros, so the weights need no
+//             zeroing: their products with a zero activation add nothing,
+//             and a weight row past N only feeds an output that is dropped.
 //
 // AM_QUANT: A holds bf16 activations X[M][K] instead of codes, and the kernel
 // quantizes them itself in a prologue (swap, one token tile, split 1): the
@@ -94,9 +106,34 @@ constexpr bool op_wave(bool swap, int w) { return swap && w >= 8 && w < 16; }
 // the first weight batch is already in flight.  The K loop then reads its
 // activation fragments from LDS, and the epilogue takes the per-token scale
 // from there.  Codes and scales are those of lin_gemm_quantize.
-enum : int { AM_GLOBAL = 0, AM_QUANT = 1, AM_STAGE = 2 };
+enum : int { AM_GLOBAL = 0, AM_QUANT = 1, AM_STAGE = 2, AM_WIDEN = 3, AM_WIDEN2 = 4,
+             AM_WIDEN4 = 5, AM_WIDEN8 = 6 };
+// AM_WIDEN .. AM_WIDEN8: the widened mode with one, two, four or eight
+// 16-byte activation chunks per lane (the launch picks the smallest that
+// holds the wave's M x slice: a load whose lanes are all out of range still
+// costs a pass through the memory pipeline; the loads stay straight-line, so
+// each chunk is widened as soon as it lands).
+constexpr bool am_widen(int am) { return am >= AM_WIDEN; }
+constexpr int wd_rounds(int am) { return am >= AM_WIDEN ? 1 << (am - AM_WIDEN) : 1; }
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int DQ_CHUNKS = 4;  // 16-byte activation chunks per thread kept in registers
+constexpr int WD_ROUNDS = 8;  // widened mode: 16-byte activation chunks per lane, at most
+
+// AM_WIDEN layout: per wave, per token, WST steps (a power of two) of 256
+// bytes of bf16 (the 128 K values of a step).  A pair of steps is one
+// 512-byte window; 16-byte piece p of step t of token tok sits at window
+// position ((t & 1) * 16 + p) ^ wd_swz(tok).  A fragment read takes the same
+// piece of the same step for 16 tokens and two lane groups (pieces 4 apart):
+// the swizzle keeps bit 2 and spreads the tokens over the other four bits,
+// so the 32 addresses of a half-wave fall in distinct 16-byte bank groups.
+__device__ inline int wd_swz(int tok) { return (tok & 3) | ((tok & 12) << 1); }
+// Steps per wave a slice of `per` steps reserves: the smallest power of two
+// that holds them and at least two steps and one batch (U is a power of two).
+__host__ __device__ inline int wd_steps(int per, int U) {
+  int n = U > 2 ? U : 2;
+  while (n < per) n *= 2;
+  return n;
+}
 
 // The quantization prologue, run by every thread of the workgroup.  X[M][K]
 // is contiguous, so chunk c (8 values) of the M x K region sits at X + 8c, in
@@ -205,6 +242,10 @@ __device__ __forceinline__ void decode_body(
   constexpr int XR = MX ? 4 : 1;
   constexpr bool DQ = AM == AM_QUANT;
   constexpr bool XS = AM == AM_STAGE;
+  constexpr bool WD = am_widen(AM);
+  constexpr int WDR = wd_rounds(AM);
+  static_assert(!WD || (SWAP && NTT == 1 && (QK == QK_FP8 || QK == QK_FP8_BLOCK)),
+                "widened activations: e4m3, swap, one token tile");
   static_assert(!MX || (SWAP && !DQ), "MXFP4 weights use the swap orientation");
   static_assert(!XS || SWAP, "staged activations are for the swap orientation");
   constexpr int NS = SWAP ? 1 : 4;    // block scales per token tile per lane
@@ -285,6 +326,10 @@ __device__ __forceinline__ void decode_body(
   const __amdgpu_buffer_rsrc_t xrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, XS ? (int)(M * KB * XR) : 0, 0x00020000);
   bool xok[U][2];
+  // With AM_WIDEN: this wave's slice, WST steps of 256 bytes per token.
+  const int WST = wd_steps((steps_per_split + W - 1) / W, U);
+  const int wd_sh = 31 - __builtin_clz(WST * 8);  // chunks per token = 1 << wd_sh
+  uint8_t* wdl = dq_lds + (int64_t)wave * M * WST * 256;
 
   // Block scales: sb[n0/128][kb] is uniform over the workgroup; sa[tok][kb]
   // per lane (one token per tile with swap, four without).
@@ -332,14 +377,17 @@ __device__ __forceinline__ void decode_body(
       if (part != 2) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-          wb[u][rt] = cat(ld16(wp[rt] + c0, ok0 && wrow[rt]), ld16(wp[rt] + c1, ok1 && wrow[rt]));
+          wb[u][rt] = WD ? cat(*(const i32x4*)(wp[rt] + c0), *(const i32x4*)(wp[rt] + c1))
+                         : cat(ld16(wp[rt] + c0, ok0 && wrow[rt]), ld16(wp[rt] + c1, ok1 && wrow[rt]));
       }
       if constexpr (MX) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) msc[u][rt] = *(const uint16_t*)(msp[rt] + (int64_t)st * 8);
       }
       if (part == 1) continue;
-      if constexpr (XS) {
+      if constexpr (WD) {
+        // activations come from the wave's widened slice
+      } else if constexpr (XS) {
         // One direct-to-LDS load per 64 chunks: chunk q (token q / (XSB/16),
         // piece q % (XSB/16)) lands at byte 16 q of the step's slice; lanes
         // past the last chunk get an out-of-range offset (no access).
@@ -412,7 +460,18 @@ __device__ __forceinline__ void decode_body(
       }
   };
 
-  auto compute_batch = [&]() {
+  // With AM_WIDEN: the bf16 fragment of piece pair (2c, 2c+1) of lane group
+  // g, step t of the wave's slice, token tok.
+  auto wide_frag = [&](int t, int c, int64_t tok) {
+    const uint8_t* base = wdl + tok * WST * 256 + (t & ~1) * 256;
+    const int sw = wd_swz((int)tok), p0 = (t & 1) * 16 + 4 * g + 2 * c;
+    const i32x4 a = *(const i32x4*)(base + ((p0 ^ sw) << 4));
+    const i32x4 b = *(const i32x4*)(base + (((p0 + 1) ^ sw) << 4));
+    return cat(a, b);
+  };
+
+  auto compute_batch = [&](int t0) {
+    (void)t0;
     if constexpr (XS) read_staged();
     if constexpr (MX) {
 #pragma unroll
@@ -433,8 +492,14 @@ __device__ __forceinline__ void decode_body(
         typename MF::Frag x0[NTT], x1[NTT];
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
-          x0[tt] = MF::prep(lo16(xb[u][tt]));
-          x1[tt] = MF::prep(hi16(xb[u][tt]));
+          if constexpr (WD) {
+            const int64_t tok = min((int64_t)(tt * 16 + l16), M - 1);
+            x0[tt] = wide_frag(t0 + u, 0, tok);
+            x1[tt] = wide_frag(t0 + u, 1, tok);
+          } else {
+            x0[tt] = MF::prep(lo16(xb[u][tt]));
+            x1[tt] = MF::prep(hi16(xb[u][tt]));
+          }
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -471,8 +536,50 @@ __device__ __forceinline__ void decode_body(
     if (!opw) load_batch(0, 1);
     quant_prologue<QK>((const uint16_t*)A, M, KB, sal, dq_lds, LS);
   }
+  // AM_WIDEN: issue this wave's activation loads (chunk q = lane + 64 r:
+  // token q / (8 WST), 16-byte chunk q % (8 WST) of the slice), then the
+  // first weight batch, then widen and store (the activation loads were
+  // issued first, so only they are waited for).  Buffer loads: a lane
+  // without a chunk in range gets an offset past the buffer, which reads
+  // zeros and touches no memory (every wave of the grid reads the same few
+  // activation lines; dummy loads would pile up on one of them).
+  i32x4 wdv[WD ? WDR : 1];
+  const int wd_chunks = WD ? (int)M * WST * 8 : 0;
+  if constexpr (WD) {
+    if (!opw) {
+      const __amdgpu_buffer_rsrc_t ars =
+          __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(M * KB), 0x00020000);
+#pragma unroll
+      for (int r = 0; r < WDR; ++r) {
+        const int q = lane + 64 * r;
+        const int tok = q >> wd_sh, j = q & ((1 << wd_sh) - 1);
+        const int64_t kb = (int64_t)(first) * STEPB + (int64_t)j * 16;
+        const bool ok = q < wd_chunks && j < my * 8 && kb < KB;
+        const int off = ok ? (int)(tok * KB + kb) : 0x7FFFFFF0;
+        wdv[r] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, off, 0, 0));
+      }
+    }
+  }
   if (!opw) {
     load_batch(0, DQ ? 2 : 0);
+    if constexpr (WD) {
+#pragma unroll
+      for (int r = 0; r < WDR; ++r) {
+        const int q = lane + 64 * r;
+        if (q < wd_chunks) {
+          const int tok = q >> wd_sh, j = q & ((1 << wd_sh) - 1);
+          const int t = j >> 3, p = (j & 7) * 2;
+          uint8_t* base = wdl + (int64_t)tok * WST * 256 + (t & ~1) * 256;
+          const int sw = wd_swz(tok), p0 = (t & 1) * 16 + p;
+          const i32x8 f = MF::prep(wdv[r]);
+          *(i32x4*)(base + ((p0 ^ sw) << 4)) = lo16(f);
+          *(i32x4*)(base + (((p0 + 1) ^ sw) << 4)) = hi16(f);
+        }
+      }
+      // the wave reads what its other lanes wrote
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+    }
     if constexpr (SWAP && !OPW) {
       if (fin_here) {
 #pragma unroll
@@ -483,10 +590,10 @@ __device__ __forceinline__ void decode_body(
         }
       }
     }
-    compute_batch();
+    compute_batch(0);
     for (int t0 = U; t0 < my; t0 += U) {
       load_batch(t0);
-      compute_batch();
+      compute_batch(t0);
     }
   } else if (fin_here) {
     // The operand wave: the loads' latency overlaps the weight stream of the
@@ -768,13 +875,30 @@ inline size_t xs_lds_bytes(int qk, int W, int U, const Call& c) {
   return (size_t)W * U * ((chunks + 63) / 64 * 1024);
 }
 
+// Dynamic LDS of the widened-activation mode: W waves x M tokens x the
+// steps a wave's slice reserves x 256 bytes; and whether one lane's share of
+// the widening (M x steps x 8 chunks over 64 lanes) fits WD_ROUNDS chunks.
+inline int wd_slice_steps(int W, int U, const Call& c, int split) {
+  const int total_steps = (int)((c.KB + STEPB - 1) / STEPB);
+  const int sps = (total_steps + split - 1) / split;
+  return wd_steps((sps + W - 1) / W, U);
+}
+inline size_t wd_lds_bytes(int W, int U, const Call& c, int split) {
+  return (size_t)W * (size_t)c.M * (size_t)wd_slice_steps(W, U, c, split) * 256;
+}
+inline bool wd_fits_rounds(int W, int U, const Call& c, int split) {
+  return c.M * wd_slice_steps(W, U, c, split) * 8 <= 64 * WD_ROUNDS;
+}
+
 template <int QK, int NTT, bool SWAP, int W, int U, int RT, int AM = AM_GLOBAL>
 hipError_t launch_d(const Variant& v, const Call& c, int split, hipStream_t s) {
   constexpr bool DQ = AM == AM_QUANT;
   const int groups = (int)((c.N + v.rows - 1) / v.rows);
   const int total_steps = (int)((c.KB + STEPB - 1) / STEPB);
   const int sps = (total_steps + split - 1) / split;
-  const size_t dyn = DQ ? dq_lds_bytes(QK, c) : (AM == AM_STAGE ? xs_lds_bytes(QK, W, U, c) : 0);
+  const size_t dyn = DQ ? dq_lds_bytes(QK, c)
+                        : (AM == AM_STAGE ? xs_lds_bytes(QK, W, U, c)
+                                          : (am_widen(AM) ? wd_lds_bytes(W, U, c, split) : 0));
   hipLaunchKernelGGL((decode_kernel<QK, NTT, SWAP, W, U, RT, AM>), dim3(groups, split),
                      dim3((W + (op_wave(SWAP, W) ? 1 : 0)) * 64),
                      dyn, s, (const uint8_t*)c.A, (const uint8_t*)c.B, c.M, c.N, c.KB, v.rows, split,
@@ -975,6 +1099,43 @@ hipError_t launch_decode_xs(const Variant& v, const Call& c, int split, hipStrea
     return launch_d<q_, nt, true, w, u, rt, AM_STAGE>(v, c, split, s);
   LG_DECODE_XS(LG_XS_TRY)
 #undef LG_XS_TRY
+  return hipErrorInvalidValue;
+}
+
+// Variants with widened activations (AM_WIDEN; swap; one token tile; e4m3
+// activations): (quant, waves, unroll, 16-row tiles).
+#define LG_DECODE_WD(X)                                                                \
+  X(QK_FP8, 8, 1, 1) X(QK_FP8, 8, 2, 1) X(QK_FP8, 8, 4, 1) X(QK_FP8, 12, 1, 1)          \
+  X(QK_FP8, 16, 1, 1) X(QK_FP8, 8, 1, 2) X(QK_FP8, 4, 4, 1) X(QK_FP8_BLOCK, 12, 1, 1)   \
+  X(QK_FP8_BLOCK, 8, 1, 1) X(QK_FP8_BLOCK, 16, 1, 1) X(QK_FP8_BLOCK, 8, 2, 1)
+
+bool decode_wd_supported(const Variant& v, const Call& c, int split) {
+  if (v.kind != V_DECODE || v.swap != 1 || c.M < 1 || c.M > 16 || split < 1) return false;
+  if (c.M * c.KB > 0x7FFFFFF0LL) return false;  // buffer offsets of the activation loads
+  const void* fn = nullptr;
+  int w_ = 0, u_ = 0;
+#define LG_WD_FN(q_, w, u, rt)                                                      \
+  if (c.qk == q_ && v.waves == w && v.unroll == u && tiles_for(v.rows) == rt) {     \
+    fn = reinterpret_cast<const void*>(&decode_kernel<q_, 1, true, w, u, rt, AM_WIDEN8>); \
+    w_ = w; u_ = u;                                                                 \
+  }
+  LG_DECODE_WD(LG_WD_FN)
+#undef LG_WD_FN
+  // (the four forms share their static LDS; the dynamic size is the same)
+  return fn && wd_fits_rounds(w_, u_, c, split) && lds_fits(fn, wd_lds_bytes(w_, u_, c, split));
+}
+
+hipError_t launch_decode_wd(const Variant& v, const Call& c, int split, hipStream_t s) {
+  const int rounds = (int)((c.M * wd_slice_steps(v.waves, v.unroll, c, split) * 8 + 63) / 64);
+#define LG_WD_TRY(q_, w, u, rt)                                                     \
+  if (c.qk == q_ && v.waves == w && v.unroll == u && tiles_for(v.rows) == rt) {     \
+    if (rounds <= 1) return launch_d<q_, 1, true, w, u, rt, AM_WIDEN>(v, c, split, s);  \
+    if (rounds <= 2) return launch_d<q_, 1, true, w, u, rt, AM_WIDEN2>(v, c, split, s); \
+    if (rounds <= 4) return launch_d<q_, 1, true, w, u, rt, AM_WIDEN4>(v, c, split, s); \
+    return launch_d<q_, 1, true, w, u, rt, AM_WIDEN8>(v, c, split, s);              \
+  }
+  LG_DECODE_WD(LG_WD_TRY)
+#undef LG_WD_TRY
   return hipErrorInvalidValue;
 }
 

@@ -34,7 +34,9 @@ struct Variant {
   // separate kernel first (the default: the prologue pays only for one token)
   int dq = 0;
   // decode family: 1 = stage the activations through LDS where the variant
-  // is compiled for it (small M), 0 = every lane loads its own
+  // is compiled for it (small M), 2 = e4m3 activations widened once per
+  // wave into LDS (up to 16 tokens, where compiled; the grouped layer takes
+  // it as 1), 0 = every lane loads its own
   int xs = 0;
 };
 
@@ -93,6 +95,9 @@ bool decode_mx_supported(const Variant& v);
 // it, LDS within the device limit.
 bool decode_xs_supported(const Variant& v, const Call& c);
 hipError_t launch_decode_xs(const Variant& v, const Call& c, int split, hipStream_t s);
+// Whether the widened-activation form (v.xs == 2) runs this call.
+bool decode_wd_supported(const Variant& v, const Call& c, int split);
+hipError_t launch_decode_wd(const Variant& v, const Call& c, int split, hipStream_t s);
 hipError_t launch_decode_dq(const Variant& v, const Call& c, hipStream_t s);
 // Grouped decode (a mixture-of-experts layer): E experts, expert x owning
 // rows [offsets[x], offsets[x+1]) of the [M] rows of c.A / C / residual, the

@@ -45,11 +45,7 @@ DECODE_CANDIDATES = [
     for sp in (1, 2) for w, u, r in DECODE_SHAPES
 ] + ["decode swap=0 split=1 reduce=twopass waves=8 unroll=2",
      "decode swap=1 split=2 reduce=lastwg waves=8 unroll=1 rows=32",
-     "decode swap=1 split=2 reduce=atomic waves=8 unroll=1 rows=32"] + [
-    # wider row groups split over K with the in-kernel reduction: fewer
-    # workgroups re-read each token's activations (larger token counts)
-    f"decode swap=1 split={sp} reduce=lastwg waves={w} unroll=1 rows={r}"
-    for sp in (2, 4) for w, r in ((8, 64), (4, 64), (8, 32))]
+     "decode swap=1 split=2 reduce=atomic waves=8 unroll=1 rows=32"]
 # Staged activations (xs=1), compiled for some shapes per weight format
 # (a shape without it runs unstaged and simply times the same).
 XS_SHAPES = [(8, 1, 12), (8, 1, 16), (8, 2, 16), (8, 4, 12), (8, 4, 24), (12, 1, 16),
@@ -57,6 +53,12 @@ XS_SHAPES = [(8, 1, 12), (8, 1, 16), (8, 2, 16), (8, 4, 12), (8, 4, 24), (12, 1,
              (8, 2, 32)]
 XS_CANDIDATES = [f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} rows={r} xs=1"
                  for w, u, r in XS_SHAPES]
+# Widened e4m3 activations (xs=2; up to 16 tokens; elsewhere the same
+# variant falls back to staging).
+WD_SHAPES = [(8, 1, 12), (8, 2, 12), (8, 4, 12), (8, 1, 16), (8, 2, 16), (12, 1, 12),
+             (12, 1, 16), (16, 1, 16), (8, 1, 24), (8, 1, 32), (4, 4, 16)]
+WD_CANDIDATES = [f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} rows={r} xs=2"
+                 for w, u, r in WD_SHAPES]
 
 TILE_CANDIDATES = ["tile bm=256 bn=256 wm=2 wn=2", "tile bm=128 bn=256 wm=2 wn=2",
                    "tile bm=256 bn=128 wm=2 wn=2", "tile bm=128 bn=128 wm=2 wn=2",
@@ -248,6 +250,8 @@ def sweep(workloads, out_path, reps, log=print, max_m=None, all_m=False, dynamic
             cands = DECODE_CANDIDATES if M <= 32 else TILE_CANDIDATES + SK_CANDIDATES
             if p.quant in ("fp8_dynamic", "mxfp4", "w8a8_int8", "block_fp8", "bf16", "fp16"):
                 cands = cands + XS_CANDIDATES
+            if p.quant in ("fp8_dynamic", "block_fp8") and M <= 16:
+                cands = cands + WD_CANDIDATES
             # Warm every candidate first (the handle's split-K workspace only
             # grows, so it reaches its final size before any graph is
             # captured), then time them in interleaved rounds.

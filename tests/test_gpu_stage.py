@@ -115,3 +115,43 @@ def test_staged_two_token_tiles(handle, case):
         C0 = run(handle, p, spec)
         assert torch.equal(C1, C0), f"staged vs direct differ [{spec}]"
         assert_close(decode_out(C1, quant), ref, f"staged {quant} {M}x{N}x{K} [{spec}]")
+
+
+# Widened e4m3 activations (xs=2): each wave widens its K range's
+# activations once into LDS; the fragments, products and their order are
+# those of the same variant without it, so the outputs must be identical bit
+# for bit.  Ragged K (a 16-byte tail step), ragged N (masked weight rows),
+# one to sixteen tokens, and split-K slices.
+WIDE = [("fp8_dynamic", "none", 1, 1040, 4096, True, False),
+        ("fp8_dynamic", "gelu_tanh", 3, 528, 272, True, True),
+        ("fp8_dynamic", "silu", 8, 6144, 4096, True, False),
+        ("fp8_dynamic", "relu", 16, 272, 1024, False, True),
+        ("fp8_dynamic", "none", 5, 1040, 12304, True, False),
+        ("block_fp8", "none", 3, 512, 3072, False, True),
+        ("block_fp8", "silu", 9, 256, 1024, True, False)]
+WIDE_SHAPES = [(8, 1, 12), (8, 2, 12), (8, 4, 12), (12, 1, 16), (16, 1, 16), (8, 1, 24),
+               (4, 4, 16), (8, 2, 16)]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=[f"{c[0]}-M{c[2]}-N{c[3]}-K{c[4]}" for c in WIDE])
+def test_widened_activations_match(handle, case):
+    quant, act, M, N, K, b, r = case
+    p = synth.make_custom(quant, act, M, N, K, seed=11 * M + N + K, bias=b, residual=r)
+    ref, _ = oracle.linear(quant, act, p.A, p.B, sa=p.sa, sb=p.sb, bias=p.bias,
+                           residual=p.residual, alpha=p.alpha)
+    specs = [f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} rows={rows}"
+             for w, u, rows in WIDE_SHAPES if quant != "block_fp8" or 128 % rows == 0]
+    specs += ["decode swap=1 split=2 reduce=twopass waves=8 unroll=1 rows=16",
+              "decode swap=1 split=4 reduce=lastwg waves=8 unroll=2 rows=16"]
+    widened = 0
+    for spec in specs:
+        handle.set_force(spec + " xs=2")
+        used = "xs=2" in handle.describe(quant, M, N, K)
+        handle.set_force(None)
+        widened += used
+        print(f"[wide] {quant} {M}x{N}x{K} {spec} widened={used}", flush=True)
+        C2 = run(handle, p, spec + " xs=2")
+        C0 = run(handle, p, spec)
+        assert torch.equal(C2, C0), f"widened vs direct differ [{spec}]"
+        assert_close(decode_out(C2, quant), ref, f"widened {quant} {M}x{N}x{K} [{spec}]")
+    assert widened >= 2, "the widened mode was not used"
