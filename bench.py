@@ -335,8 +335,8 @@ def dynamic_quant_rows(torch, h, reps):
     # The headline decode with the quantization in front (a separate kernel,
     # or the decode kernel's own prologue where the table asks for it),
     # interleaved with the pre-quantized call.
-    wl = Workload(torch, HEAD_CFG, [1, 8, 32])
-    for M in (1, 8, 32):
+    wl = Workload(torch, HEAD_CFG, [1, 2, 8, 32])
+    for M in (1, 2, 8, 32):
         R = wl.ncopy
         X = torch.from_numpy(synth.activations16(M, wl.K, seed=M).view(np.int16)).cuda()
         d = wl.dev[M]

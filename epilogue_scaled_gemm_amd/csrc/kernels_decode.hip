@@ -97,6 +97,15 @@ constexpr bool op_wave(bool swap, int w) { return swap && w >= 8 && w < 16; }
 //             range or past K are stored as zeros, so the weights need no
 //             zeroing: their products with a zero activation add nothing,
 //             and a weight row past N only feeds an output that is dropped.
+//  AM_QWIDEN  AM_WIDEN on bf16 activations X[M][K] with per-token dynamic
+//             e4m3 quantization fused in (the prologue fusion of the pages'
+//             input-side transforms): each wave loads the bf16 values of its
+//             K range, takes every token's partial maximum, the workgroup
+//             combines them through LDS (one barrier; the waves together
+//             cover all of K, split 1), and each wave then forms the scale,
+//             the codes (those of lin_gemm_quantize, bit for bit) and their
+//             exact bf16 widening in its slice.  The epilogue takes the
+//             per-token scale from LDS.
 //
 // AM_QUANT: A holds bf16 activations X[M][K] instead of codes, and the kernel
 // quantizes them itself in a prologue (swap, one token tile, split 1): the
@@ -107,14 +116,17 @@ constexpr bool op_wave(bool swap, int w) { return swap && w >= 8 && w < 16; }
 // activation fragments from LDS, and the epilogue takes the per-token scale
 // from there.  Codes and scales are those of lin_gemm_quantize.
 enum : int { AM_GLOBAL = 0, AM_QUANT = 1, AM_STAGE = 2, AM_WIDEN = 3, AM_WIDEN2 = 4,
-             AM_WIDEN4 = 5, AM_WIDEN8 = 6 };
+             AM_WIDEN4 = 5, AM_WIDEN8 = 6, AM_QWIDEN = 7, AM_QWIDEN2 = 8, AM_QWIDEN4 = 9,
+             AM_QWIDEN8 = 10 };
 // AM_WIDEN .. AM_WIDEN8: the widened mode with one, two, four or eight
 // 16-byte activation chunks per lane (the launch picks the smallest that
 // holds the wave's M x slice: a load whose lanes are all out of range still
 // costs a pass through the memory pipeline; the loads stay straight-line, so
-// each chunk is widened as soon as it lands).
+// each chunk is widened as soon as it lands).  AM_QWIDEN .. AM_QWIDEN8: the
+// same with bf16 activations quantized per token in the prologue (below).
 constexpr bool am_widen(int am) { return am >= AM_WIDEN; }
-constexpr int wd_rounds(int am) { return am >= AM_WIDEN ? 1 << (am - AM_WIDEN) : 1; }
+constexpr bool am_qwiden(int am) { return am >= AM_QWIDEN; }
+constexpr int wd_rounds(int am) { return am >= AM_WIDEN ? 1 << ((am - AM_WIDEN) % 4) : 1; }
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int DQ_CHUNKS = 4;  // 16-byte activation chunks per thread kept in registers
 constexpr int WD_ROUNDS = 8;  // widened mode: 16-byte activation chunks per lane, at most
@@ -243,7 +255,9 @@ __device__ __forceinline__ void decode_body(
   constexpr bool DQ = AM == AM_QUANT;
   constexpr bool XS = AM == AM_STAGE;
   constexpr bool WD = am_widen(AM);
+  constexpr bool QW = am_qwiden(AM);
   constexpr int WDR = wd_rounds(AM);
+  static_assert(!QW || QK == QK_FP8, "the fused quantization is per-token e4m3");
   static_assert(!WD || (SWAP && NTT == 1 && (QK == QK_FP8 || QK == QK_FP8_BLOCK)),
                 "widened activations: e4m3, swap, one token tile");
   static_assert(!MX || (SWAP && !DQ), "MXFP4 weights use the swap orientation");
@@ -257,6 +271,9 @@ __device__ __forceinline__ void decode_body(
   constexpr int NOP = 13;
   __shared__ float opnd[OPW ? NTILE : 1][NOP][64];
   __shared__ int arrival;
+  // AM_QWIDEN: per-wave partial maxima and the scales of up to 16 tokens.
+  __shared__ float qw_max[QW ? W : 1][QW ? 16 : 1];
+  __shared__ float qw_scale[QW ? 16 : 1];
   extern __shared__ __align__(16) uint8_t dq_lds[];
   static_assert(!DQ || (SWAP && NTT == 1), "the quantization prologue is for swap, one token tile");
 
@@ -545,7 +562,7 @@ __device__ __forceinline__ void decode_body(
   // activation lines; dummy loads would pile up on one of them).
   i32x4 wdv[WD ? WDR : 1];
   const int wd_chunks = WD ? (int)M * WST * 8 : 0;
-  if constexpr (WD) {
+  if constexpr (WD && !QW) {
     if (!opw) {
       const __amdgpu_buffer_rsrc_t ars =
           __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(M * KB), 0x00020000);
@@ -560,9 +577,79 @@ __device__ __forceinline__ void decode_body(
       }
     }
   }
+  // AM_QWIDEN: bf16 chunks of 8 values, q = lane + 64 r: token q >> qsh,
+  // chunk q & (2^qsh - 1) of the slice (2^qsh = 16 WST chunks per token).
+  const int qsh = 31 - __builtin_clz(WST * 16);
+  const int q_chunks = QW ? (int)M * (1 << qsh) : 0;
+  if constexpr (QW) {
+    if (!opw) {
+      const __amdgpu_buffer_rsrc_t xrs2 =
+          __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(M * KB * 2), 0x00020000);
+#pragma unroll
+      for (int r = 0; r < WDR; ++r) {
+        const int q = lane + 64 * r;
+        const int tok = q >> qsh, j = q & ((1 << qsh) - 1);
+        const int64_t kv = (int64_t)first * STEPB + (int64_t)j * 8;
+        const bool ok = q < q_chunks && j < my * 16 && kv < KB;
+        const int off = ok ? (int)((tok * KB + kv) * 2) : 0x7FFFFFF0;
+        wdv[r] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs2, off, 0, 0));
+      }
+    }
+  }
   if (!opw) {
     load_batch(0, DQ ? 2 : 0);
-    if constexpr (WD) {
+    if constexpr (QW) {
+      // Partial maxima: the lanes of one token within a round are a group of
+      // min(64, 2^qsh) consecutive lanes; its maximum goes to
+      // qw_max[wave][token] (rounds of one token combine in order).
+      if (lane < 16) qw_max[wave][lane] = 0.f;
+      const int gl = qsh >= 6 ? 64 : (1 << qsh);
+#pragma unroll
+      for (int r = 0; r < WDR; ++r) {
+        float v[8];
+        unpack8<false>(wdv[r], v);
+        float am = amax8(v);
+        for (int o = 1; o < gl; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));
+        const int q = lane + 64 * r;
+        const int tok = q >> qsh;
+        if ((lane & (gl - 1)) == 0 && q < q_chunks) qw_max[wave][tok] = fmaxf(qw_max[wave][tok], am);
+      }
+    }
+  }
+  if constexpr (QW) {
+    __syncthreads();  // every wave's partial maxima are in (the operand wave too)
+    if (!opw) {
+#pragma unroll
+      for (int r = 0; r < WDR; ++r) {
+        const int q = lane + 64 * r;
+        if (q < q_chunks) {
+          const int tok = q >> qsh, j = q & ((1 << qsh) - 1);
+          float amax = qw_max[0][tok];
+#pragma unroll
+          for (int w = 1; w < W; ++w) amax = fmaxf(amax, qw_max[w][tok]);
+          const float sc = group_scale(amax, 448.f);
+          if (wave == 0 && j == 0) qw_scale[tok] = sc;
+          float v[8];
+          unpack8<false>(wdv[r], v);
+          const i32x2 c8 = quant8<false>(v, make_div(sc, amax));
+          typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+          i32x4 wide;
+          wide[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)c8[0], 1.0f, false));
+          wide[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)c8[0], 1.0f, true));
+          wide[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)c8[1], 1.0f, false));
+          wide[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)c8[1], 1.0f, true));
+          // chunk j holds values 8 j .. 8 j + 7 of the slice: piece j & 15 of step j >> 4
+          const int t = j >> 4, pc = j & 15;
+          uint8_t* base = wdl + (int64_t)tok * WST * 256 + (t & ~1) * 256;
+          *(i32x4*)(base + ((((t & 1) * 16 + pc) ^ wd_swz(tok)) << 4)) = wide;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave reads what its lanes wrote
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  if (!opw) {
+    if constexpr (WD && !QW) {
 #pragma unroll
       for (int r = 0; r < WDR; ++r) {
         const int q = lane + 64 * r;
@@ -668,6 +755,7 @@ __device__ __forceinline__ void decode_body(
       }
     }
     if constexpr (DQ && !BLOCK) p.sam = sal[min(m, M - 1)];
+    if constexpr (QW) p.sam = qw_scale[min(m, M - 1)];
     epilogue_run4_pre<F16>(e, m, nr, v, p);
   };
   auto reduce_tile = [&](int q, AccT* v) {
@@ -1139,8 +1227,49 @@ hipError_t launch_decode_wd(const Variant& v, const Call& c, int split, hipStrea
   return hipErrorInvalidValue;
 }
 
+// Fused quantization with widened activations (AM_QWIDEN; e4m3 per token,
+// bf16 X, swap, one token tile, split 1): the same shapes as the widened
+// mode, each with one, two, four or eight 8-value chunks per lane.
+#define LG_DECODE_QW(X)                                                                \
+  X(8, 1, 1) X(8, 2, 1) X(8, 4, 1) X(12, 1, 1) X(16, 1, 1) X(8, 1, 2) X(4, 4, 1)
+
+inline int qw_rounds(const Variant& v, const Call& c) {
+  return (int)((c.M * wd_slice_steps(v.waves, v.unroll, c, 1) * 16 + 63) / 64);
+}
+
+bool decode_qw_supported(const Variant& v, const Call& c) {
+  if (v.kind != V_DECODE || v.swap != 1 || v.xs != 2 || c.qk != QK_FP8 || c.M < 1 || c.M > 16)
+    return false;
+  if (c.M * c.KB * 2 > 0x7FFFFFF0LL || qw_rounds(v, c) > WD_ROUNDS) return false;
+  const void* fn = nullptr;
+  int w_ = 0, u_ = 0;
+#define LG_QW_FN(w, u, rt)                                                          \
+  if (v.waves == w && v.unroll == u && tiles_for(v.rows) == rt) {                   \
+    fn = reinterpret_cast<const void*>(&decode_kernel<QK_FP8, 1, true, w, u, rt, AM_QWIDEN8>); \
+    w_ = w; u_ = u;                                                                 \
+  }
+  LG_DECODE_QW(LG_QW_FN)
+#undef LG_QW_FN
+  return fn && lds_fits(fn, wd_lds_bytes(w_, u_, c, 1));
+}
+
+hipError_t launch_decode_qw(const Variant& v, const Call& c, hipStream_t s) {
+  const int rounds = qw_rounds(v, c);
+#define LG_QW_TRY(w, u, rt)                                                         \
+  if (v.waves == w && v.unroll == u && tiles_for(v.rows) == rt) {                   \
+    if (rounds <= 1) return launch_d<QK_FP8, 1, true, w, u, rt, AM_QWIDEN>(v, c, 1, s);  \
+    if (rounds <= 2) return launch_d<QK_FP8, 1, true, w, u, rt, AM_QWIDEN2>(v, c, 1, s); \
+    if (rounds <= 4) return launch_d<QK_FP8, 1, true, w, u, rt, AM_QWIDEN4>(v, c, 1, s); \
+    return launch_d<QK_FP8, 1, true, w, u, rt, AM_QWIDEN8>(v, c, 1, s);              \
+  }
+  LG_DECODE_QW(LG_QW_TRY)
+#undef LG_QW_TRY
+  return hipErrorInvalidValue;
+}
+
 bool decode_dq_supported(const Variant& v, const Call& c, int split) {
   if (v.kind != V_DECODE || v.swap != 1 || split != 1 || c.M < 1 || c.M > 16) return false;
+  if (decode_qw_supported(v, c)) return true;
   const void* fn;
   switch (c.qk) {
     case QK_FP8: return dq_kernel<QK_FP8>(v, c, &fn);
@@ -1151,6 +1280,7 @@ bool decode_dq_supported(const Variant& v, const Call& c, int split) {
 }
 
 hipError_t launch_decode_dq(const Variant& v, const Call& c, hipStream_t s) {
+  if (decode_qw_supported(v, c)) return launch_decode_qw(v, c, s);
   switch (c.qk) {
     case QK_FP8: return launch_dq_prologue<QK_FP8>(v, c, s);
     case QK_I8: return launch_dq_prologue<QK_I8>(v, c, s);

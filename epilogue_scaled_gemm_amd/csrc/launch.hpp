@@ -86,6 +86,8 @@ hipError_t launch_decode(const Variant& v, const Call& c, int split, hipStream_t
 // c.KB = K, c.epi.sa is unused (per-token scales come from the prologue).
 // Supported for swap, split 1, M <= 16, e4m3 / int8 / block e4m3, the
 // variants the library compiles with it, and LDS within the device limit.
+// With v.xs == 2 and per-token e4m3, where it fits, the prologue also widens
+// the codes once per wave into LDS (the widened-activation form).
 bool decode_dq_supported(const Variant& v, const Call& c, int split);
 // Whether the decode variant is compiled for MXFP4 weights (swap, waves /
 // unroll / tiles from a short list).

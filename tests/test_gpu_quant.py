@@ -216,3 +216,62 @@ def test_prologue_falls_back_when_lds_does_not_fit(handle):
     ref, _ = oracle.linear("block_fp8", "none", Qr, p.B, Sr, p.sb, p.bias)
     C = _dyn_run(handle, dev(Xh), p, "decode swap=1 split=1 reduce=twopass waves=8 unroll=1 rows=16 dq=1")
     assert_close(decode_out(C, "block_fp8"), ref, "block fp8 16 x 12288 fallback")
+
+
+# Fused quantization with widened activations ("xs=2 dq=1", e4m3 per token):
+# every wave quantizes its K range after a workgroup-wide maximum and widens
+# the codes once into LDS.  The codes, scales and summation order are those
+# of the two-kernel path with the same variant, so the outputs must be
+# identical bit for bit; also against the oracle.  Includes an all-zero
+# token (scale 1), a token of tiny values (the rescaled division) and a
+# ragged K tail.
+QW_SHAPES = [(8, 2, 12), (8, 1, 12), (8, 4, 12), (12, 1, 16), (16, 1, 16), (8, 1, 24), (4, 4, 16)]
+QW_CASES = [("none", 1, 1040, 4096, True, False), ("gelu_tanh", 3, 528, 272, True, True),
+            ("silu", 5, 1040, 4096, False, True), ("none", 8, 6144, 4096, True, False),
+            ("relu", 2, 272, 12304, True, False), ("none", 4, 256, 1024, False, False)]
+
+
+@pytest.mark.parametrize("case", QW_CASES, ids=[f"M{c[1]}-N{c[2]}-K{c[3]}" for c in QW_CASES])
+def test_fused_quantize_widen_matches_two_kernel_path(handle, case):
+    act, M, N, K, b, r = case
+    p = synth.make_custom("fp8_dynamic", act, M, N, K, seed=13 * M + K, bias=b, residual=r)
+    Xh = synth.activations16(M, K, seed=5 * M + N)
+    if M >= 3:
+        Xh[1] = 0                                             # all-zero token
+        tiny = (np.abs(Xh[2].view(np.int16).astype(np.int32)) & 0x7F) | 0x0100  # ~1e-37
+        Xh[2] = (tiny | (Xh[2] & 0x8000)).astype(np.uint16)
+    Qr, Sr = oracle.dynamic_quant("fp8_token", Xh)
+    ref, _ = oracle.linear("fp8_dynamic", act, Qr, p.B, Sr, p.sb, p.bias, p.residual, p.alpha)
+    X = dev(Xh)
+    for w, u, rows in QW_SHAPES:
+        spec = f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} rows={rows} xs=2"
+        print(f"[qwiden] {M}x{N}x{K} {spec}", flush=True)
+        C1 = _dyn_run(handle, X, p, spec + " dq=1")
+        assert_close(decode_out(C1, "fp8_dynamic"), ref, f"fused {M}x{N}x{K} [{spec}]")
+        C0 = _dyn_run(handle, X, p, spec)
+        assert torch.equal(C1, C0), f"fused vs two-kernel differ [{spec}]"
+        C2 = _dyn_run(handle, X, p, spec.replace(" xs=2", ""))
+        assert torch.equal(C1, C2), f"fused vs plain variant differ [{spec}]"
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_table_fused_quantization_at_decode_shape(handle, M):
+    # The built-in table asks for the fused quantize-widen prologue for one
+    # and two tokens at N = 6144, K = 4096: lin_gemm_run_dynamic through the
+    # default dispatch against the oracle, and bit for bit against the same
+    # variant fed by the separate quantization kernel.
+    N, K = 6144, 4096
+    desc = handle.describe("fp8_dynamic", M, N, K).split()
+    assert "xs=2" in desc and "dq=1" in desc, desc
+    p = synth.make_custom("fp8_dynamic", "silu", M, N, K, seed=17 + M, bias=True, residual=True)
+    Xh = synth.activations16(M, K, seed=23 + M)
+    Qr, Sr = oracle.dynamic_quant("fp8_token", Xh)
+    ref, _ = oracle.linear("fp8_dynamic", "silu", Qr, p.B, Sr, p.sb, p.bias, p.residual, p.alpha)
+    C = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    handle.run_dynamic(dev(Xh), dev(p.B), C, quant="fp8_dynamic", act="silu", sb=dev(p.sb),
+                       alpha=p.alpha, bias=dev(p.bias), residual=dev(p.residual))
+    torch.cuda.synchronize()
+    assert_close(decode_out(C.cpu(), "fp8_dynamic"), ref, f"table fused M={M}")
+    spec = handle.describe("fp8_dynamic", M, N, K).replace(" dq=1", "")
+    C0 = _dyn_run(handle, dev(Xh), p, spec)
+    assert torch.equal(C.cpu(), C0)
