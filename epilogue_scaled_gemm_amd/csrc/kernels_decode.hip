@@ -1007,7 +1007,7 @@ hipError_t launch_d(const Variant& v, const Call& c, int split, hipStream_t s) {
   X(QK, NTT, true, 16, 1, 1) X(QK, NTT, true, 8, 1, 2) X(QK, NTT, true, 4, 2, 2) \
   X(QK, NTT, true, 8, 2, 2) X(QK, NTT, true, 4, 1, 4) X(QK, NTT, true, 8, 1, 4) \
   X(QK, NTT, true, 8, 4, 1) X(QK, NTT, true, 8, 4, 2) X(QK, NTT, true, 12, 1, 1) \
-  X(QK, NTT, false, 8, 2, 1)
+  X(QK, NTT, true, 16, 1, 2) X(QK, NTT, false, 8, 2, 1)
 
 // Tiles per workgroup for a rows-per-workgroup value: 1, 2 or 4.
 inline int tiles_for(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
@@ -1163,7 +1163,9 @@ hipError_t launch_mx(const Variant& v, const Call& c, int split, hipStream_t s) 
   X(QK_BF16, 1, 8, 2, 1) X(QK_BF16, 2, 8, 1, 2) X(QK_FP16, 1, 8, 1, 2)                   \
   X(QK_FP16, 1, 8, 1, 1) X(QK_FP16, 1, 8, 2, 1) X(QK_FP16, 2, 8, 1, 2)                   \
   X(QK_I8, 1, 4, 2, 2) X(QK_I8, 1, 8, 1, 2) X(QK_FP8_BLOCK, 2, 8, 1, 2)                  \
-  X(QK_FP8_BLOCK, 2, 12, 1, 1) X(QK_FP8_BLOCK, 2, 16, 1, 1) X(QK_FP8_BLOCK, 2, 4, 2, 2)
+  X(QK_FP8_BLOCK, 2, 12, 1, 1) X(QK_FP8_BLOCK, 2, 16, 1, 1) X(QK_FP8_BLOCK, 2, 4, 2, 2)   \
+  X(QK_FP8, 2, 16, 1, 2) X(QK_FP8, 1, 16, 1, 2) X(QK_BF16, 2, 16, 1, 2) X(QK_I8, 2, 16, 1, 2) \
+  X(QK_FP8_BLOCK, 2, 16, 1, 2) X(QK_FP16, 2, 16, 1, 2)
 
 bool decode_xs_supported(const Variant& v, const Call& c) {
   if (v.kind != V_DECODE || v.swap != 1 || c.M < 1 || c.M > 32) return false;

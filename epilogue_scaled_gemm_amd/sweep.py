@@ -39,7 +39,8 @@ ROTATION_BYTES = 384 << 20
 # (waves, unroll, rows per workgroup)
 DECODE_SHAPES = [(8, 1, 16), (8, 2, 16), (4, 4, 16), (16, 1, 16), (8, 1, 8), (8, 1, 12),
                  (16, 1, 12), (16, 1, 8), (8, 2, 8), (8, 1, 32), (4, 2, 32), (8, 2, 32),
-                 (8, 1, 24), (4, 1, 64), (8, 1, 64), (8, 4, 12), (8, 4, 24), (12, 1, 12), (12, 1, 16)]
+                 (8, 1, 24), (4, 1, 64), (8, 1, 64), (8, 4, 12), (8, 4, 24), (12, 1, 12), (12, 1, 16),
+                 (16, 1, 24), (16, 1, 32)]
 DECODE_CANDIDATES = [
     f"decode swap=1 split={sp} reduce=twopass waves={w} unroll={u} rows={r}"
     for sp in (1, 2) for w, u, r in DECODE_SHAPES
@@ -50,7 +51,7 @@ DECODE_CANDIDATES = [
 # (a shape without it runs unstaged and simply times the same).
 XS_SHAPES = [(8, 1, 12), (8, 1, 16), (8, 2, 16), (8, 4, 12), (8, 4, 24), (12, 1, 16),
              (8, 1, 24), (8, 2, 12), (4, 4, 16), (16, 1, 16), (4, 2, 32), (8, 1, 32),
-             (8, 2, 32)]
+             (8, 2, 32), (16, 1, 24), (16, 1, 32)]
 XS_CANDIDATES = [f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} rows={r} xs=1"
                  for w, u, r in XS_SHAPES]
 # Widened e4m3 activations (xs=2; up to 16 tokens; elsewhere the same
@@ -213,7 +214,7 @@ def merge_inc(path, new_lines, log=print):
 
 
 def sweep(workloads, out_path, reps, log=print, max_m=None, all_m=False, dynamic=False,
-          emit_inc=None, quant=None, ms=None, merge=False):
+          emit_inc=None, quant=None, ms=None, merge=False, min_m=None):
     import torch
     import synth
     import epilogue_scaled_gemm_amd as lg
@@ -241,7 +242,7 @@ def sweep(workloads, out_path, reps, log=print, max_m=None, all_m=False, dynamic
         if all_m and min(ms_w) <= 32:
             ms_w = sorted(set(ms_w) | set(range(1, 33)))
         for M in ms_w:
-            if max_m is not None and M > max_m:
+            if (max_m is not None and M > max_m) or (min_m is not None and M < min_m):
                 continue
             p = synth.make(cfg, M, quant)
             ops = {k: _dev(torch, v) for k, v in p.operands().items() if k != "alpha"}
@@ -341,6 +342,7 @@ def main():
     ap.add_argument("--workloads", default="1,2,3,4,5")
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--max-m", type=int, default=None, help="only token counts up to this")
+    ap.add_argument("--min-m", type=int, default=None, help="only token counts from this")
     ap.add_argument("--all-m", action="store_true", help="every token count 1..32 (decode)")
     ap.add_argument("--dynamic", action="store_true",
                     help="choose the quantization prologue (dq=1) where it is faster")
@@ -357,7 +359,7 @@ def main():
     sweep([int(x) for x in a.workloads.split(",")], a.out, a.reps,
           log=lambda s: print(s, flush=True), max_m=a.max_m, all_m=a.all_m, dynamic=a.dynamic,
           emit_inc=a.emit_inc, quant=a.quant,
-          ms=[int(x) for x in a.ms.split(",")] if a.ms else None, merge=a.merge)
+          ms=[int(x) for x in a.ms.split(",")] if a.ms else None, merge=a.merge, min_m=a.min_m)
 
 
 if __name__ == "__main__":

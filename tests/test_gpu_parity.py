@@ -161,3 +161,27 @@ def test_large_m_default_path(handle):
     im, inn = sample_positions(p.M, p.N, 4000, seed=17)
     r, _ = reference(p, (im, inn))
     assert_close(decode_out(C, p.quant)[im, inn], r, p.name)
+
+
+# Whole output tiles at full size, in the launch configuration the benchmark
+# times: the kernel's tile (256 x 256 for the bf16 prefill, 256 x 128 for
+# block FP8 at 2048 tokens) is compared element by element at the first, an
+# interior and the last tile position (the last one holds the grid's final
+# rows and columns).
+FULL_TILES = [(5, 4096, 256, 256, [(0, 0), (7, 9), (15, 15)]),
+              (4, 2048, 256, 128, [(0, 0), (3, 17), (7, 31)])]
+
+
+@pytest.mark.parametrize("cfg,M,TM,TN,tiles", FULL_TILES, ids=["prefill-4096", "block_fp8-2048"])
+def test_full_tiles_at_full_size(handle, cfg, M, TM, TN, tiles):
+    p = synth.make(cfg, M)
+    print(f"[tiles] {p.name} variant={handle.describe(p.quant, p.M, p.N, p.K)}", flush=True)
+    C = run(handle, p)
+    g = decode_out(C, p.quant)
+    for tm, tn in tiles:
+        m0, n0 = tm * TM, tn * TN
+        assert m0 + TM <= p.M and n0 + TN <= p.N
+        mm, nn = np.meshgrid(np.arange(m0, m0 + TM), np.arange(n0, n0 + TN), indexing="ij")
+        im, inn = mm.ravel(), nn.ravel()
+        r, _ = reference(p, (im, inn))
+        assert_close(g[im, inn], r, f"{p.name} tile ({tm}, {tn})")
