@@ -264,7 +264,11 @@ __device__ __forceinline__ void decode_body(
   static_assert(!XS || SWAP, "staged activations are for the swap orientation");
   constexpr int NS = SWAP ? 1 : 4;    // block scales per token tile per lane
   constexpr int NTILE = RT * NTT;     // 16x16 output tiles per workgroup
-  __shared__ AccT red[W][NTILE * 4][64];
+  // Partial sums of the W waves for the in-workgroup reduction.  With staged
+  // activations each wave writes its own into its staging slice (done with
+  // it by then), so the static array is not needed.
+  constexpr bool RA = XS;
+  __shared__ AccT red[RA ? 1 : W][NTILE * 4][64];
   // Epilogue operands per tile and lane: sa, sb[4], bias[4], residual[4],
   // staged by the operand wave.
   constexpr bool OPW = op_wave(SWAP, W);
@@ -339,7 +343,9 @@ __device__ __forceinline__ void decode_body(
   constexpr bool XSW = XSB == 128;
   auto xsw = [](int t) { return XSW ? (t & 7) ^ (((t >> 3) & 1) * 7) : 0; };
   const int XSL = (xs_chunks + 63) / 64 * 1024;
-  uint8_t* xsl = dq_lds + (int64_t)wave * U * XSL;
+  // A wave's slice: U steps, and at least its NTILE KiB of partial sums.
+  const int XSS = max(U * XSL, NTILE * 1024);
+  uint8_t* xsl = dq_lds + (int64_t)wave * XSS;
   const __amdgpu_buffer_rsrc_t xrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, XS ? (int)(M * KB * XR) : 0, 0x00020000);
   bool xok[U][2];
@@ -712,7 +718,8 @@ __device__ __forceinline__ void decode_body(
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][(rt * NTT + tt) * 4 + r][lane] = (AccT)acc[rt][tt][r];
+        for (int r = 0; r < 4; ++r)
+          (RA ? (AccT*)xsl : &red[wave][0][0])[((rt * NTT + tt) * 4 + r) * 64 + lane] = (AccT)acc[rt][tt][r];
   }
   __syncthreads();
 
@@ -761,9 +768,12 @@ __device__ __forceinline__ void decode_body(
   auto reduce_tile = [&](int q, AccT* v) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      AccT s = red[0][q * 4 + r][lane];
+      auto part = [&](int w) {
+        return (RA ? (const AccT*)(dq_lds + (int64_t)w * XSS) : &red[w][0][0])[(q * 4 + r) * 64 + lane];
+      };
+      AccT s = part(0);
 #pragma unroll
-      for (int w = 1; w < W; ++w) s += red[w][q * 4 + r][lane];
+      for (int w = 1; w < W; ++w) s += part(w);
       v[r] = s;
     }
   };
@@ -957,10 +967,12 @@ inline size_t dq_lds_bytes(int qk, const Call& c) {
 
 // Dynamic LDS of the staged-activation mode: W waves x U steps x the M
 // tokens' activation bytes of one step, rounded up to whole KiB (the
-// direct-to-LDS loads write 1 KiB each).
-inline size_t xs_lds_bytes(int qk, int W, int U, const Call& c) {
+// direct-to-LDS loads write 1 KiB each), each wave's slice at least the
+// 1 KiB per 16x16 output tile that its partial sums take at the end.
+inline size_t xs_lds_bytes(int qk, int W, int U, int RT, const Call& c) {
   const size_t chunks = (size_t)c.M * STEPB * (qk == QK_MXFP4 ? 4 : 1) / 16;
-  return (size_t)W * U * ((chunks + 63) / 64 * 1024);
+  const size_t ntile = (size_t)RT * (c.M <= 16 ? 1 : 2);
+  return (size_t)W * std::max((size_t)U * ((chunks + 63) / 64 * 1024), ntile * 1024);
 }
 
 // Dynamic LDS of the widened-activation mode: W waves x M tokens x the
@@ -985,7 +997,7 @@ hipError_t launch_d(const Variant& v, const Call& c, int split, hipStream_t s) {
   const int total_steps = (int)((c.KB + STEPB - 1) / STEPB);
   const int sps = (total_steps + split - 1) / split;
   const size_t dyn = DQ ? dq_lds_bytes(QK, c)
-                        : (AM == AM_STAGE ? xs_lds_bytes(QK, W, U, c)
+                        : (AM == AM_STAGE ? xs_lds_bytes(QK, W, U, RT, c)
                                           : (am_widen(AM) ? wd_lds_bytes(W, U, c, split) : 0));
   hipLaunchKernelGGL((decode_kernel<QK, NTT, SWAP, W, U, RT, AM>), dim3(groups, split),
                      dim3((W + (op_wave(SWAP, W) ? 1 : 0)) * 64),
@@ -1007,7 +1019,7 @@ hipError_t launch_d(const Variant& v, const Call& c, int split, hipStream_t s) {
   X(QK, NTT, true, 16, 1, 1) X(QK, NTT, true, 8, 1, 2) X(QK, NTT, true, 4, 2, 2) \
   X(QK, NTT, true, 8, 2, 2) X(QK, NTT, true, 4, 1, 4) X(QK, NTT, true, 8, 1, 4) \
   X(QK, NTT, true, 8, 4, 1) X(QK, NTT, true, 8, 4, 2) X(QK, NTT, true, 12, 1, 1) \
-  X(QK, NTT, true, 16, 1, 2) X(QK, NTT, false, 8, 2, 1)
+  X(QK, NTT, true, 16, 1, 2) X(QK, NTT, true, 16, 2, 2) X(QK, NTT, false, 8, 2, 1)
 
 // Tiles per workgroup for a rows-per-workgroup value: 1, 2 or 4.
 inline int tiles_for(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
@@ -1165,7 +1177,8 @@ hipError_t launch_mx(const Variant& v, const Call& c, int split, hipStream_t s) 
   X(QK_I8, 1, 4, 2, 2) X(QK_I8, 1, 8, 1, 2) X(QK_FP8_BLOCK, 2, 8, 1, 2)                  \
   X(QK_FP8_BLOCK, 2, 12, 1, 1) X(QK_FP8_BLOCK, 2, 16, 1, 1) X(QK_FP8_BLOCK, 2, 4, 2, 2)   \
   X(QK_FP8, 2, 16, 1, 2) X(QK_FP8, 1, 16, 1, 2) X(QK_BF16, 2, 16, 1, 2) X(QK_I8, 2, 16, 1, 2) \
-  X(QK_FP8_BLOCK, 2, 16, 1, 2) X(QK_FP16, 2, 16, 1, 2)
+  X(QK_FP8_BLOCK, 2, 16, 1, 2) X(QK_FP16, 2, 16, 1, 2) X(QK_FP8, 2, 16, 2, 2)             \
+  X(QK_BF16, 2, 16, 2, 2) X(QK_FP16, 2, 16, 2, 2)
 
 bool decode_xs_supported(const Variant& v, const Call& c) {
   if (v.kind != V_DECODE || v.swap != 1 || c.M < 1 || c.M > 32) return false;
@@ -1175,11 +1188,12 @@ bool decode_xs_supported(const Variant& v, const Call& c) {
 #define LG_XS_FN(q_, nt, w, u, rt)                                                  \
   if (c.qk == q_ && ntt == nt && v.waves == w && v.unroll == u && tiles_for(v.rows) == rt) { \
     fn = reinterpret_cast<const void*>(&decode_kernel<q_, nt, true, w, u, rt, AM_STAGE>); \
-    w_ = w; u_ = u;                                                                 \
+    w_ = w; u_ = u; rt_ = rt;                                                       \
   }
+  int rt_ = 1;
   LG_DECODE_XS(LG_XS_FN)
 #undef LG_XS_FN
-  return fn && lds_fits(fn, xs_lds_bytes(c.qk, w_, u_, c));
+  return fn && lds_fits(fn, xs_lds_bytes(c.qk, w_, u_, rt_, c));
 }
 
 hipError_t launch_decode_xs(const Variant& v, const Call& c, int split, hipStream_t s) {
@@ -1347,7 +1361,7 @@ bool grouped_supported(const Variant& v, int qk, int ntt, int64_t KB) {
   if (!v.xs) return true;
   Call c{};
   c.qk = qk; c.M = 16 * ntt; c.KB = KB;
-  return lds_fits(p.fn, xs_lds_bytes(qk, p.w, p.u, c));
+  return lds_fits(p.fn, xs_lds_bytes(qk, p.w, p.u, p.rt, c));
 }
 
 hipError_t launch_grouped(const Variant& v, const Call& c, const int* offsets, int64_t E,
@@ -1361,7 +1375,7 @@ hipError_t launch_grouped(const Variant& v, const Call& c, const int* offsets, i
   const int steps = (int)((c.KB + STEPB - 1) / STEPB);
   Call cm = c;
   cm.M = 16 * ntt;  // staging holds one chunk
-  const size_t dyn = xs ? xs_lds_bytes(c.qk, p.w, p.u, cm) : 0;
+  const size_t dyn = xs ? xs_lds_bytes(c.qk, p.w, p.u, p.rt, cm) : 0;
   const dim3 grid((unsigned)groups, (unsigned)std::min<int64_t>(E, c.M), (unsigned)chunks);
 #define LG_G_TRY(q_, nt, w_, u_, rt_, am)                                               \
   if (p.fn == reinterpret_cast<const void*>(&grouped_decode_kernel<q_, nt, w_, u_, rt_, am>)) { \

@@ -40,7 +40,7 @@ ROTATION_BYTES = 384 << 20
 DECODE_SHAPES = [(8, 1, 16), (8, 2, 16), (4, 4, 16), (16, 1, 16), (8, 1, 8), (8, 1, 12),
                  (16, 1, 12), (16, 1, 8), (8, 2, 8), (8, 1, 32), (4, 2, 32), (8, 2, 32),
                  (8, 1, 24), (4, 1, 64), (8, 1, 64), (8, 4, 12), (8, 4, 24), (12, 1, 12), (12, 1, 16),
-                 (16, 1, 24), (16, 1, 32)]
+                 (16, 1, 24), (16, 1, 32), (16, 2, 24)]
 DECODE_CANDIDATES = [
     f"decode swap=1 split={sp} reduce=twopass waves={w} unroll={u} rows={r}"
     for sp in (1, 2) for w, u, r in DECODE_SHAPES
@@ -51,7 +51,7 @@ DECODE_CANDIDATES = [
 # (a shape without it runs unstaged and simply times the same).
 XS_SHAPES = [(8, 1, 12), (8, 1, 16), (8, 2, 16), (8, 4, 12), (8, 4, 24), (12, 1, 16),
              (8, 1, 24), (8, 2, 12), (4, 4, 16), (16, 1, 16), (4, 2, 32), (8, 1, 32),
-             (8, 2, 32), (16, 1, 24), (16, 1, 32)]
+             (8, 2, 32), (16, 1, 24), (16, 1, 32), (16, 2, 24), (16, 2, 32)]
 XS_CANDIDATES = [f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} rows={r} xs=1"
                  for w, u, r in XS_SHAPES]
 # Widened e4m3 activations (xs=2; up to 16 tokens; elsewhere the same

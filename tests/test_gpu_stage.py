@@ -91,12 +91,12 @@ def test_staged_activations_match(handle, case):
 
 # Two token tiles (17..32 tokens): the variants compiled with staging there.
 TWO_TILE = [("fp8_dynamic", "none", 24, 1040, 4096, True, False,
-             [(8, 1, 24), (8, 1, 32), (8, 4, 24), (16, 1, 24), (16, 1, 32)]),
+             [(8, 1, 24), (8, 1, 32), (8, 4, 24), (16, 1, 24), (16, 1, 32), (16, 2, 24)]),
             ("w8a8_int8", "silu", 32, 528, 1024, False, False, [(4, 2, 32)]),
             ("mxfp4", "gelu_tanh", 20, 272, 512, True, True, [(4, 2, 32), (8, 1, 24)]),
             ("block_fp8", "none", 17, 256, 1024, False, True,
              [(8, 2, 32), (8, 1, 32), (12, 1, 16), (16, 1, 16), (4, 2, 32)]),
-            ("bf16", "relu", 30, 272, 1032, True, True, [(8, 1, 24), (8, 1, 32), (16, 1, 24)]),
+            ("bf16", "relu", 30, 272, 1032, True, True, [(8, 1, 24), (8, 1, 32), (16, 1, 24), (16, 2, 32)]),
             ("w8a8_int8", "none", 20, 528, 4096, True, False, [(16, 1, 32)]),
             ("fp16", "gelu_tanh", 27, 272, 1024, True, True, [(16, 1, 24)])]
 

@@ -33,7 +33,7 @@ def handle():
 DECODE_SHAPES = [(1, 8, 1, 16), (1, 8, 2, 8), (1, 4, 4, 12), (1, 16, 1, 16), (1, 8, 1, 32),
                  (1, 4, 2, 24), (1, 8, 2, 32), (1, 4, 1, 64), (1, 8, 1, 64), (0, 8, 2, 16),
                  (0, 8, 2, 12), (1, 8, 4, 12), (1, 8, 4, 24), (1, 12, 1, 16), (1, 16, 1, 24),
-                 (1, 16, 1, 32)]
+                 (1, 16, 1, 32), (1, 16, 2, 24)]
 SPLITS = [(1, "twopass"), (2, "lastwg"), (4, "atomic"), (8, "twopass"), (16, "lastwg"),
           (4, "twopass"), (2, "atomic")]
 DECODE_SPECS = [f"decode swap={sw} split={sp} reduce={rd} waves={w} unroll={u} rows={r}"
