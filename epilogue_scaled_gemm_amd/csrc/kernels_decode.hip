@@ -265,9 +265,10 @@ __device__ __forceinline__ void decode_body(
   constexpr int NS = SWAP ? 1 : 4;    // block scales per token tile per lane
   constexpr int NTILE = RT * NTT;     // 16x16 output tiles per workgroup
   // Partial sums of the W waves for the in-workgroup reduction.  With staged
-  // activations each wave writes its own into its staging slice (done with
-  // it by then), so the static array is not needed.
-  constexpr bool RA = XS;
+  // or widened activations each wave writes its own into its LDS slice (done
+  // with it by then; slices are sized to hold them), so the static array is
+  // not needed.
+  constexpr bool RA = XS || am_widen(AM);
   __shared__ AccT red[RA ? 1 : W][NTILE * 4][64];
   // Epilogue operands per tile and lane: sa, sb[4], bias[4], residual[4],
   // staged by the operand wave.
@@ -352,7 +353,8 @@ __device__ __forceinline__ void decode_body(
   // With AM_WIDEN: this wave's slice, WST steps of 256 bytes per token.
   const int WST = wd_steps((steps_per_split + W - 1) / W, U);
   const int wd_sh = 31 - __builtin_clz(WST * 8);  // chunks per token = 1 << wd_sh
-  uint8_t* wdl = dq_lds + (int64_t)wave * M * WST * 256;
+  const int64_t WSS = max((int64_t)M * WST * 256, (int64_t)NTILE * 1024);  // slice stride
+  uint8_t* wdl = dq_lds + (int64_t)wave * WSS;
 
   // Block scales: sb[n0/128][kb] is uniform over the workgroup; sa[tok][kb]
   // per lane (one token per tile with swap, four without).
@@ -719,7 +721,8 @@ __device__ __forceinline__ void decode_body(
       for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          (RA ? (AccT*)xsl : &red[wave][0][0])[((rt * NTT + tt) * 4 + r) * 64 + lane] = (AccT)acc[rt][tt][r];
+          (RA ? (AccT*)(XS ? xsl : wdl) : &red[wave][0][0])[((rt * NTT + tt) * 4 + r) * 64 + lane] =
+              (AccT)acc[rt][tt][r];
   }
   __syncthreads();
 
@@ -769,7 +772,8 @@ __device__ __forceinline__ void decode_body(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       auto part = [&](int w) {
-        return (RA ? (const AccT*)(dq_lds + (int64_t)w * XSS) : &red[w][0][0])[(q * 4 + r) * 64 + lane];
+        return (RA ? (const AccT*)(dq_lds + (int64_t)w * (XS ? (int64_t)XSS : WSS)) : &red[w][0][0])
+            [(q * 4 + r) * 64 + lane];
       };
       AccT s = part(0);
 #pragma unroll
@@ -983,8 +987,10 @@ inline int wd_slice_steps(int W, int U, const Call& c, int split) {
   const int sps = (total_steps + split - 1) / split;
   return wd_steps((sps + W - 1) / W, U);
 }
-inline size_t wd_lds_bytes(int W, int U, const Call& c, int split) {
-  return (size_t)W * (size_t)c.M * (size_t)wd_slice_steps(W, U, c, split) * 256;
+inline size_t wd_lds_bytes(int W, int U, const Call& c, int split, int RT = 2) {
+  // each slice also holds the wave's partial sums (1 KiB per 16x16 tile)
+  return (size_t)W * std::max((size_t)c.M * (size_t)wd_slice_steps(W, U, c, split) * 256,
+                              (size_t)RT * 1024);
 }
 inline bool wd_fits_rounds(int W, int U, const Call& c, int split) {
   return c.M * wd_slice_steps(W, U, c, split) * 8 <= 64 * WD_ROUNDS;
@@ -998,7 +1004,7 @@ hipError_t launch_d(const Variant& v, const Call& c, int split, hipStream_t s) {
   const int sps = (total_steps + split - 1) / split;
   const size_t dyn = DQ ? dq_lds_bytes(QK, c)
                         : (AM == AM_STAGE ? xs_lds_bytes(QK, W, U, RT, c)
-                                          : (am_widen(AM) ? wd_lds_bytes(W, U, c, split) : 0));
+                                          : (am_widen(AM) ? wd_lds_bytes(W, U, c, split, RT) : 0));
   hipLaunchKernelGGL((decode_kernel<QK, NTT, SWAP, W, U, RT, AM>), dim3(groups, split),
                      dim3((W + (op_wave(SWAP, W) ? 1 : 0)) * 64),
                      dyn, s, (const uint8_t*)c.A, (const uint8_t*)c.B, c.M, c.N, c.KB, v.rows, split,
@@ -1210,7 +1216,8 @@ hipError_t launch_decode_xs(const Variant& v, const Call& c, int split, hipStrea
 // activations): (quant, waves, unroll, 16-row tiles).
 #define LG_DECODE_WD(X)                                                                \
   X(QK_FP8, 8, 1, 1) X(QK_FP8, 8, 2, 1) X(QK_FP8, 8, 4, 1) X(QK_FP8, 12, 1, 1)          \
-  X(QK_FP8, 16, 1, 1) X(QK_FP8, 8, 1, 2) X(QK_FP8, 4, 4, 1) X(QK_FP8_BLOCK, 12, 1, 1)   \
+  X(QK_FP8, 16, 1, 1) X(QK_FP8, 8, 1, 2) X(QK_FP8, 4, 4, 1) X(QK_FP8, 16, 1, 2)         \
+  X(QK_FP8, 16, 2, 2) X(QK_FP8_BLOCK, 12, 1, 1)                                         \
   X(QK_FP8_BLOCK, 8, 1, 1) X(QK_FP8_BLOCK, 16, 1, 1) X(QK_FP8_BLOCK, 8, 2, 1)
 
 bool decode_wd_supported(const Variant& v, const Call& c, int split) {

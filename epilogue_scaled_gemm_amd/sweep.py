@@ -57,7 +57,7 @@ XS_CANDIDATES = [f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} row
 # Widened e4m3 activations (xs=2; up to 16 tokens; elsewhere the same
 # variant falls back to staging).
 WD_SHAPES = [(8, 1, 12), (8, 2, 12), (8, 4, 12), (8, 1, 16), (8, 2, 16), (12, 1, 12),
-             (12, 1, 16), (16, 1, 16), (8, 1, 24), (8, 1, 32), (4, 4, 16)]
+             (12, 1, 16), (16, 1, 16), (8, 1, 24), (8, 1, 32), (4, 4, 16), (16, 1, 24), (16, 2, 24)]
 WD_CANDIDATES = [f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} rows={r} xs=2"
                  for w, u, r in WD_SHAPES]
 

@@ -133,7 +133,7 @@ WIDE = [("fp8_dynamic", "none", 1, 1040, 4096, True, False),
         ("block_fp8", "none", 3, 512, 3072, False, True),
         ("block_fp8", "silu", 9, 256, 1024, True, False)]
 WIDE_SHAPES = [(8, 1, 12), (8, 2, 12), (8, 4, 12), (12, 1, 16), (16, 1, 16), (8, 1, 24),
-               (4, 4, 16), (8, 2, 16)]
+               (4, 4, 16), (8, 2, 16), (16, 1, 24), (16, 2, 24)]
 
 
 @pytest.mark.parametrize("case", WIDE, ids=[f"{c[0]}-M{c[2]}-N{c[3]}-K{c[4]}" for c in WIDE])
