@@ -196,7 +196,11 @@ __global__ __launch_bounds__(512, 1) void bpp_kernel(const uint8_t* __restrict__
   constexpr int BM = 256, BN = 128, TM = 64, TN = 64, FM = 4, FN = 4;
   constexpr int RB = 128;                 // one 128-wide scale block per stage
   constexpr int NBUF = 3;
-  constexpr int STAGE = (BM + BN) * RB;   // 48 KiB
+  // A stage: the activation and weight tiles of one scale block, then the
+  // block's activation scales of the tile's 256 rows (1 KiB) and its weight
+  // scale (in a 1 KiB slot), all brought by direct-to-LDS loads.
+  constexpr int SA_OFF = (BM + BN) * RB, SB_OFF = SA_OFF + 1024;
+  constexpr int STAGE = SB_OFF + 1024;    // 50 KiB
   constexpr int LA = BM / 8 / 4, LB = BN / 8 / 4;  // loads (8 rows x 128 bytes) per wave per stage
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
@@ -229,8 +233,18 @@ __global__ __launch_bounds__(512, 1) void bpp_kernel(const uint8_t* __restrict__
     off0[q] = row * (int)KB + chk;
   }
   const int ldsdst = ldA ? lw * LA * 1024 : BM * RB + lw * LB * 1024;
+  // Scales: group 0's wave lw brings sa[m0 + 64 lw + lane][kb] (rows past M
+  // read 0 through the bounds and their outputs are never stored); group
+  // 1's wave 4 brings sb[n0 / 128][kb] in its lane 0 (the other lanes' and
+  // waves' offsets lie past the buffer: no access).
+  const __amdgpu_buffer_rsrc_t rss = ldA
+      ? __builtin_amdgcn_make_buffer_rsrc((void*)(e.sa + m0 * KBLK), (short)0, a_rows * KBLK * 4, 0x00020000)
+      : __builtin_amdgcn_make_buffer_rsrc((void*)(e.sb + (n0 / 128) * KBLK), (short)0, KBLK * 4, 0x00020000);
+  const int soff0 = ldA ? (lw * 64 + lane) * KBLK * 4 : ((lw == 0 && lane == 0) ? 0 : 0x7FFFFFF0);
+  const int sdst = ldA ? SA_OFF + lw * 256 : SB_OFF + lw * 256;
   auto dload = [&](int kt) {
-    uint8_t* base = lds + (kt % NBUF) * STAGE + ldsdst;
+    uint8_t* sbase = lds + (kt % NBUF) * STAGE;
+    uint8_t* base = sbase + ldsdst;
     const int koff = (kb0 + kt) * RB;
     const int kill = kt < KT ? 0 : 0x7FFFFFF0;
     if (ldA) {
@@ -242,24 +256,12 @@ __global__ __launch_bounds__(512, 1) void bpp_kernel(const uint8_t* __restrict__
       for (int q = 0; q < LB; ++q)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + q * 1024), 16, (off0[q] + koff) | kill, 0, 0, 0);
     }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (lds_void*)(sbase + sdst), 4,
+                                             (soff0 + (kb0 + kt) * 4) | kill, 0, 0, 0);
   };
-  // Scales: sa varies per token (per lane), sb is uniform over a wave's 64
-  // weight rows (inside one 128-row block).  Rows past M read row M - 1;
-  // their outputs are never stored.
-  // An empty trailing slice (KT == 0) still reads one valid scale.
-  const int kbs = min(kb0, KBLK - 1);
-  const float* sa_base = e.sa + m0 * KBLK + kbs;
-  int sa_off[FM];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-    sa_off[i] = (int)(min(m0 + wave_m * TM + i * 16 + l16, M - 1) - m0) * KBLK;
-  const float* sb_row = e.sb + min((n0 + wave_n * TN) / 128, (N + 127) / 128 - 1) * KBLK + kbs;
-  float sa_nxt[FM], sa_cur[FM], sc_prev[FM];
-  auto sload = [&](int kt) {
-    const int k = min(kt, max(KT - 1, 0));
-#pragma unroll
-    for (int i = 0; i < FM; ++i) sa_nxt[i] = sa_base[sa_off[i] + k];
-  };
+  // The scales of block kt are read from its stage (sa per token, i.e. per
+  // lane; sb uniform: the tile's 128 weight rows are one 128-row block).
+  float sc_prev[FM];
 
   const int sw = swz8(l16);
   const int a_lane = (wave_m * TM + l16) * RB;
@@ -274,10 +276,7 @@ __global__ __launch_bounds__(512, 1) void bpp_kernel(const uint8_t* __restrict__
 
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t) dload(t);
-  sload(0);
   __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll
-  for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i];
   __syncthreads();
   if (grp_w == 1) __builtin_amdgcn_s_barrier();
   for (int kt = 0; kt < KT; ++kt) {
@@ -294,7 +293,6 @@ __global__ __launch_bounds__(512, 1) void bpp_kernel(const uint8_t* __restrict__
       for (int i = 0; i < FM; ++i) ra[i] = *(const i32x4*)(base + a_lane + i * 16 * RB + ch);
       if (h == 0) {
         dload(kt + NBUF - 1);
-        sload(kt + 1);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -308,8 +306,9 @@ __global__ __launch_bounds__(512, 1) void bpp_kernel(const uint8_t* __restrict__
       for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(rw[j]));
 #pragma unroll
       for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(ra[i]));
-      // group 1: weight loads of stage kt + 1 and the scales of block kt landed
-      if (h == 1 && grp_w == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LB + FM));
+      // group 1: the loads of stage kt + 1 have landed (the LB + 1 of stage
+      // kt + 2 may still be in flight)
+      if (h == 1 && grp_w == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LB + 1));
       __builtin_amdgcn_s_barrier();
       // ---- compute phase: widen just in time, MFMA into the block partial
       Frag xa[FM];
@@ -322,14 +321,12 @@ __global__ __launch_bounds__(512, 1) void bpp_kernel(const uint8_t* __restrict__
         for (int i = 0; i < FM; ++i) p[i][j] = MF::mma(w, xa[i], h == 0 ? f32x4{0, 0, 0, 0} : p[i][j]);
       }
       if (h == 1) {
-        // group 0: activation loads of stage kt + 1 and the scales of block kt landed
-        if (grp_w == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LA + FM));
-        const float sbv = sb_row[kt];
+        // group 0: the loads of stage kt + 1 have landed
+        if (grp_w == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LA + 1));
+        const float sbv = *(const float*)(base + SB_OFF);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          sc_prev[i] = sa_cur[i] * sbv;
-          sa_cur[i] = sa_nxt[i];
-        }
+        for (int i = 0; i < FM; ++i)
+          sc_prev[i] = *(const float*)(base + SA_OFF + (wave_m * TM + i * 16 + l16) * 4) * sbv;
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -417,7 +414,7 @@ hipError_t launch_pp(const Variant& v, const Call& c, int split, hipStream_t s) 
     case QK_FP16: return launch_pp_q<QK_FP16>(v, c, s);
     case QK_I8: return launch_pp_q<QK_I8>(v, c, s);
     case QK_FP8_BLOCK: {
-      constexpr size_t lds = 3 * (256 + 128) * 128;
+      constexpr size_t lds = 3 * ((256 + 128) * 128 + 2048);
       hipError_t err = opt_in_lds((const void*)bpp_kernel, lds);
       if (err != hipSuccess) return err;
       const int tiles_m = (int)((c.M + 255) / 256), tiles_n = (int)((c.N + 127) / 128);
