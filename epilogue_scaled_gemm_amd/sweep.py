@@ -84,7 +84,9 @@ def _dev(torch, a):
 
 def capture_variant(torch, h, p, ops, Bs, spec):
     """A HIP graph of one call of `spec` per weight copy (rotating B), and its
-    output buffer.  Raises LinGemmError if the variant does not apply."""
+    output buffer (keep it while the graph is replayed: entering another
+    capture empties the allocator cache, which would release it).  Raises
+    LinGemmError if the variant does not apply."""
     h.set_force(spec)
     try:
         C = torch.empty((p.M, p.N), dtype=torch.int16, device="cuda")
@@ -124,12 +126,14 @@ def time_interleaved(torch, graphs, rounds):
 
 def time_variant(torch, h, p, ops, Bs, spec, reps=10):
     """Seconds per call of one variant (graph replay, rotating B)."""
-    g, _ = capture_variant(torch, h, p, ops, Bs, spec)
+    g, C = capture_variant(torch, h, p, ops, Bs, spec)  # C: the graph writes it
     return time_interleaved(torch, [g], reps)[0] / len(Bs)
 
 
 def capture_dynamic(torch, h, p, ops, Bs, X, spec):
-    """A HIP graph of lin_gemm_run_dynamic calls (rotating B) under `spec`."""
+    """A HIP graph of lin_gemm_run_dynamic calls (rotating B) under `spec`, and
+    its output buffer (keep it while the graph is replayed: entering another
+    capture empties the allocator cache, which would release it)."""
     h.set_force(spec)
     try:
         C = torch.empty((p.M, p.N), dtype=torch.int16, device="cuda")
@@ -146,7 +150,7 @@ def capture_dynamic(torch, h, p, ops, Bs, X, spec):
                 call(i)
     finally:
         h.set_force(None)
-    return g
+    return g, C
 
 
 def merge_ranges(entries):
@@ -289,7 +293,8 @@ def sweep(workloads, out_path, reps, log=print, max_m=None, all_m=False, dynamic
                 try:
                     gd = [capture_dynamic(torch, h, p, ops, Bs, X, spec),
                           capture_dynamic(torch, h, p, ops, Bs, X, spec + " dq=1")]
-                    t0, t1 = (t / len(Bs) for t in time_interleaved(torch, gd, reps))
+                    t0, t1 = (t / len(Bs) for t in
+                              time_interleaved(torch, [g for g, _ in gd], reps))
                     log(f"DYNAMIC {c['name']} M={M}: separate kernel {t0 * 1e6:.2f} us, "
                         f"prologue {t1 * 1e6:.2f} us")
                     if t1 < 0.98 * t0:
