@@ -126,6 +126,9 @@ enum : int { AM_GLOBAL = 0, AM_QUANT = 1, AM_STAGE = 2, AM_WIDEN = 3, AM_WIDEN2 
 // same with bf16 activations quantized per token in the prologue (below).
 constexpr bool am_widen(int am) { return am >= AM_WIDEN; }
 constexpr bool am_qwiden(int am) { return am >= AM_QWIDEN; }
+
+// s_waitcnt immediate for "vmcnt <= n" (expcnt and lgkmcnt not waited).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 constexpr int wd_rounds(int am) { return am >= AM_WIDEN ? 1 << ((am - AM_WIDEN) % 4) : 1; }
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int DQ_CHUNKS = 4;  // 16-byte activation chunks per thread kept in registers
@@ -384,7 +387,60 @@ __device__ __forceinline__ void decode_body(
   // step.  Each activation slice feeds RT weight tiles.
   // part: 0 = weights and activations, 1 = weights only, 2 = activations
   // (and block scales) only.
+  // Weight (and MXFP4 scale) loads of step u.
+  auto load_weights = [&](int t0, int u) {
+    const int t = t0 + u;
+    const bool live = t < my;
+    const int st = min(first + (live ? t : 0), total_steps - 1);
+    const int64_t o0 = (int64_t)st * STEPB + g * 32, o1 = o0 + 16;
+    const int64_t c0 = (o0 < KB ? o0 : KB - 16) - g * 32;
+    const int64_t c1 = (o1 < KB ? o1 : KB - 16) - g * 32;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+      wb[u][rt] = cat(ld16(wp[rt] + c0, live && o0 < KB && wrow[rt]),
+                      ld16(wp[rt] + c1, live && o1 < KB && wrow[rt]));
+    if constexpr (MX) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) msc[u][rt] = *(const uint16_t*)(msp[rt] + (int64_t)st * 8);
+    }
+  };
+  // Direct-to-LDS activation loads of step u: one per 64 chunks, chunk q
+  // (token q / (XSB/16), piece q % (XSB/16)) landing at byte 16 q of the
+  // step's slice; lanes past the last chunk get an out-of-range offset (no
+  // access).
+  auto stage_step = [&](int t0, int u) {
+    const int t = t0 + u;
+    const bool live = t < my;
+    const int st = min(first + (live ? t : 0), total_steps - 1);
+    const int64_t o0 = (int64_t)st * STEPB + g * 32;
+    xok[u][0] = live && (o0 < KB);
+    xok[u][1] = live && (o0 + 16 < KB);
+    for (int i = 0; i * 64 < xs_chunks; ++i) {
+      const int q = i * 64 + lane;
+      const int tq = q / (XSB / 16), pq = (q - tq * (XSB / 16)) ^ xsw(tq);
+      const int voff = q < xs_chunks ? (int)(tq * KB * XR + (int64_t)st * XSB + pq * 16)
+                                     : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xrs, (lds_void*)(xsl + (int64_t)u * XSL + i * 1024), 16, voff, 0, 0, 0);
+    }
+  };
   auto load_batch = [&](int t0, int part = 0) {
+    if constexpr (XS) {
+      // A one-step batch issues its activation loads before its weights:
+      // loads complete in issue order, so the staged fragments are read
+      // while the weights are still in flight.  Longer batches keep
+      // step order (weights, then activations, per step) and wait for all.
+      if constexpr (U == 1) {
+        stage_step(t0, 0);
+        load_weights(t0, 0);
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          load_weights(t0, u);
+          stage_step(t0, u);
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u;
@@ -399,33 +455,19 @@ __device__ __forceinline__ void decode_body(
       const bool ok1 = live && (o1 < KB);
       const int64_t c0 = (o0 < KB ? o0 : KB - 16) - g * 32;
       const int64_t c1 = (o1 < KB ? o1 : KB - 16) - g * 32;
-      if (part != 2) {
+      if (part != 2 && !XS) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
           wb[u][rt] = WD ? cat(*(const i32x4*)(wp[rt] + c0), *(const i32x4*)(wp[rt] + c1))
                          : cat(ld16(wp[rt] + c0, ok0 && wrow[rt]), ld16(wp[rt] + c1, ok1 && wrow[rt]));
       }
-      if constexpr (MX) {
+      if constexpr (MX && !XS) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) msc[u][rt] = *(const uint16_t*)(msp[rt] + (int64_t)st * 8);
       }
       if (part == 1) continue;
-      if constexpr (WD) {
-        // activations come from the wave's widened slice
-      } else if constexpr (XS) {
-        // One direct-to-LDS load per 64 chunks: chunk q (token q / (XSB/16),
-        // piece q % (XSB/16)) lands at byte 16 q of the step's slice; lanes
-        // past the last chunk get an out-of-range offset (no access).
-        xok[u][0] = ok0;
-        xok[u][1] = ok1;
-        for (int i = 0; i * 64 < xs_chunks; ++i) {
-          const int q = i * 64 + lane;
-          const int tq = q / (XSB / 16), pq = (q - tq * (XSB / 16)) ^ xsw(tq);
-          const int voff = q < xs_chunks ? (int)(tq * KB * XR + (int64_t)st * XSB + pq * 16)
-                                         : 0x7FFFFFF0;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              xrs, (lds_void*)(xsl + (int64_t)u * XSL + i * 1024), 16, voff, 0, 0, 0);
-        }
+      if constexpr (WD || XS) {
+        // activations come from LDS (the widened slice, or staged above)
       } else if constexpr (MX) {
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt)
@@ -461,28 +503,34 @@ __device__ __forceinline__ void decode_body(
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) acc[rt][tt] = C{0, 0, 0, 0};
 
-  // With AM_STAGE: the step's fragments from the wave's LDS slice, once the
-  // direct-to-LDS loads have landed (vmcnt 0; the weight loads of the batch
-  // are needed now anyway).
-  auto read_staged = [&]() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // With AM_STAGE: step u's fragments from the wave's LDS slice, once its
+  // direct-to-LDS loads have landed.
+  auto read_staged = [&](int u) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int tt = 0; tt < NTT; ++tt) {
+      const int64_t tok = min((int64_t)(tt * 16 + l16), M - 1);
+      if constexpr (MX) {
+        const uint8_t* xr = xsl + (int64_t)u * XSL + tok * XSB + g * 32 * XR;
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
-        const int64_t tok = min((int64_t)(tt * 16 + l16), M - 1);
-        if constexpr (MX) {
-          const uint8_t* xr = xsl + (int64_t)u * XSL + tok * XSB + g * 32 * XR;
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            xb[u][tt].v[j] = ld16(xr + 16 * j, j < 4 ? xok[u][0] : xok[u][1]);
-        } else {
-          const uint8_t* xt = xsl + (int64_t)u * XSL + tok * XSB;
-          const int sw = xsw((int)tok);
-          xb[u][tt] = cat(ld16(xt + (((2 * g) ^ sw) << 4), xok[u][0]),
-                          ld16(xt + (((2 * g + 1) ^ sw) << 4), xok[u][1]));
-        }
+        for (int j = 0; j < 8; ++j)
+          xb[u][tt].v[j] = ld16(xr + 16 * j, j < 4 ? xok[u][0] : xok[u][1]);
+      } else {
+        const uint8_t* xt = xsl + (int64_t)u * XSL + tok * XSB;
+        const int sw = xsw((int)tok);
+        xb[u][tt] = cat(ld16(xt + (((2 * g) ^ sw) << 4), xok[u][0]),
+                        ld16(xt + (((2 * g + 1) ^ sw) << 4), xok[u][1]));
       }
+    }
+  };
+  // A staged batch: its fragments once its direct-to-LDS loads have landed
+  // (one-step batches: with at most the step's weight loads, two per row
+  // tile plus the MXFP4 scale load, still in flight behind them).
+  auto stage_batch = [&]() {
+    if constexpr (XS) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(U == 1 ? (MX ? 3 : 2) * RT : 0));
+#pragma unroll
+      for (int u = 0; u < U; ++u) read_staged(u);
+    }
   };
 
   // With AM_WIDEN: the bf16 fragment of piece pair (2c, 2c+1) of lane group
@@ -497,10 +545,10 @@ __device__ __forceinline__ void decode_body(
 
   auto compute_batch = [&](int t0) {
     (void)t0;
-    if constexpr (XS) read_staged();
+    stage_batch();
     if constexpr (MX) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const float s0 = e8m0_to_f32(msc[u][rt] & 0xFFu), s1 = e8m0_to_f32(msc[u][rt] >> 8);
@@ -511,6 +559,7 @@ __device__ __forceinline__ void decode_body(
             for (int tt = 0; tt < NTT; ++tt) acc[rt][tt] = MF::mma(w, xb[u][tt].v[j], acc[rt][tt]);
           }
         }
+      }
     } else {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
