@@ -1151,15 +1151,6 @@ hipError_t launch_dq_prologue(const Variant& v, const Call& c, hipStream_t s) {
 
 }  // namespace
 
-bool decode_supported(int swap, int waves, int unroll, int rows) {
-  if (rows < 4 || rows > 64 || rows % 4 != 0) return false;
-#define LG_DECODE_HAS(qk, ntt, sw, w, u, rt) \
-  if (swap == (sw ? 1 : 0) && waves == w && unroll == u && tiles_for(rows) == rt) return true;
-  LG_DECODE_SWAP(LG_DECODE_HAS, 0, 1)
-#undef LG_DECODE_HAS
-  return false;
-}
-
 int decode_auto_split(const Call& c, const Variant& v) {
   const int64_t groups = (c.N + v.rows - 1) / v.rows;
   const int64_t steps = (c.KB + STEPB - 1) / STEPB;
@@ -1233,7 +1224,24 @@ hipError_t launch_mx(const Variant& v, const Call& c, int split, hipStream_t s) 
   X(QK_FP8_BLOCK, 2, 12, 1, 1) X(QK_FP8_BLOCK, 2, 16, 1, 1) X(QK_FP8_BLOCK, 2, 4, 2, 2)   \
   X(QK_FP8, 2, 16, 1, 2) X(QK_FP8, 1, 16, 1, 2) X(QK_BF16, 2, 16, 1, 2) X(QK_I8, 2, 16, 1, 2) \
   X(QK_FP8_BLOCK, 2, 16, 1, 2) X(QK_FP16, 2, 16, 1, 2) X(QK_FP8, 2, 16, 2, 2)             \
-  X(QK_BF16, 2, 16, 2, 2) X(QK_FP16, 2, 16, 2, 2)
+  X(QK_BF16, 2, 16, 2, 2) X(QK_FP16, 2, 16, 2, 2) X(QK_FP8_BLOCK, 2, 16, 2, 1)          \
+  X(QK_FP8_BLOCK, 2, 12, 2, 1)
+
+// Whether some build of this decode shape exists (a plain one for every
+// weight format, or a staged one for some formats only: forcing the latter
+// elsewhere fails at the call).
+bool decode_supported(int swap, int waves, int unroll, int rows) {
+  if (rows < 4 || rows > 64 || rows % 4 != 0) return false;
+#define LG_DECODE_HAS(qk, ntt, sw, w, u, rt) \
+  if (swap == (sw ? 1 : 0) && waves == w && unroll == u && tiles_for(rows) == rt) return true;
+  LG_DECODE_SWAP(LG_DECODE_HAS, 0, 1)
+#undef LG_DECODE_HAS
+#define LG_DECODE_XS_HAS(q_, nt, w, u, rt) \
+  if (swap == 1 && waves == w && unroll == u && tiles_for(rows) == rt) return true;
+  LG_DECODE_XS(LG_DECODE_XS_HAS)
+#undef LG_DECODE_XS_HAS
+  return false;
+}
 
 bool decode_xs_supported(const Variant& v, const Call& c) {
   if (v.kind != V_DECODE || v.swap != 1 || c.M < 1 || c.M > 32) return false;

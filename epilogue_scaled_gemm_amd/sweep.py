@@ -51,7 +51,8 @@ DECODE_CANDIDATES = [
 # (a shape without it runs unstaged and simply times the same).
 XS_SHAPES = [(8, 1, 12), (8, 1, 16), (8, 2, 16), (8, 4, 12), (8, 4, 24), (12, 1, 16),
              (8, 1, 24), (8, 2, 12), (4, 4, 16), (16, 1, 16), (4, 2, 32), (8, 1, 32),
-             (8, 2, 32), (16, 1, 24), (16, 1, 32), (16, 2, 24), (16, 2, 32)]
+             (8, 2, 32), (16, 1, 24), (16, 1, 32), (16, 2, 24), (16, 2, 32), (16, 2, 16),
+             (12, 2, 16)]
 XS_CANDIDATES = [f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} rows={r} xs=1"
                  for w, u, r in XS_SHAPES]
 # Widened e4m3 activations (xs=2; up to 16 tokens; elsewhere the same
