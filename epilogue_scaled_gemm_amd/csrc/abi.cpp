@@ -354,6 +354,11 @@ int run_impl(lin_gemm_t h, const void* A, const void* B, const lin_scales_t* sca
   lg::Variant v;
   rc = select_variant(h, quant_mode, M, N, K, &v);
   if (rc != LIN_OK) return rc;
+  if (v.kind == lg::V_DECODE && !lg::decode_plain_supported(v.swap, v.waves, v.unroll, v.rows) &&
+      !(v.xs == 2 && lg::decode_wd_supported(v, c, resolve_split(v, c))) &&
+      !(v.xs && lg::decode_xs_supported(v, c)))
+    return fail(h, LIN_ERR_UNSUPPORTED,
+                "decode shape compiled only with staged activations, which do not apply to this call");
   hipError_t e;
   const int split = resolve_split(v, c);
   if (noalloc) {

@@ -1227,15 +1227,23 @@ hipError_t launch_mx(const Variant& v, const Call& c, int split, hipStream_t s) 
   X(QK_BF16, 2, 16, 2, 2) X(QK_FP16, 2, 16, 2, 2) X(QK_FP8_BLOCK, 2, 16, 2, 1)          \
   X(QK_FP8_BLOCK, 2, 12, 2, 1)
 
-// Whether some build of this decode shape exists (a plain one for every
-// weight format, or a staged one for some formats only: forcing the latter
-// elsewhere fails at the call).
-bool decode_supported(int swap, int waves, int unroll, int rows) {
+// Whether the plain build of this decode shape exists (for every weight
+// format).
+bool decode_plain_supported(int swap, int waves, int unroll, int rows) {
   if (rows < 4 || rows > 64 || rows % 4 != 0) return false;
 #define LG_DECODE_HAS(qk, ntt, sw, w, u, rt) \
   if (swap == (sw ? 1 : 0) && waves == w && unroll == u && tiles_for(rows) == rt) return true;
   LG_DECODE_SWAP(LG_DECODE_HAS, 0, 1)
 #undef LG_DECODE_HAS
+  return false;
+}
+
+// Whether some build of this decode shape exists: the plain one, or a staged
+// one for some formats and token tiles only (forcing the latter where it does
+// not apply fails at the call).
+bool decode_supported(int swap, int waves, int unroll, int rows) {
+  if (decode_plain_supported(swap, waves, unroll, rows)) return true;
+  if (rows < 4 || rows > 64 || rows % 4 != 0) return false;
 #define LG_DECODE_XS_HAS(q_, nt, w, u, rt) \
   if (swap == 1 && waves == w && unroll == u && tiles_for(rows) == rt) return true;
   LG_DECODE_XS(LG_DECODE_XS_HAS)

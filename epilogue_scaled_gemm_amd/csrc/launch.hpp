@@ -79,6 +79,7 @@ hipError_t launch_pp(const Variant& v, const Call& c, int split, hipStream_t s);
 
 // Decode family (kernels_decode.hip).
 bool decode_supported(int swap, int waves, int unroll, int rows);
+bool decode_plain_supported(int swap, int waves, int unroll, int rows);
 int decode_auto_split(const Call& c, const Variant& v);
 size_t decode_ws_bytes(const Variant& v, const Call& c, int split);
 hipError_t launch_decode(const Variant& v, const Call& c, int split, hipStream_t s);

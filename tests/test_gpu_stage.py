@@ -164,3 +164,12 @@ def test_widened_activations_match(handle, case):
         assert torch.equal(C2, C0), f"widened vs direct differ [{spec}]"
         assert_close(decode_out(C2, quant), ref, f"widened {quant} {M}x{N}x{K} [{spec}]")
     assert widened >= 2, "the widened mode was not used"
+
+
+def test_staged_only_shape_rejected_where_staging_does_not_apply(handle):
+    # The two-step block e4m3 shapes exist only staged for two token tiles:
+    # forcing one at a single-tile token count fails with an error, and
+    # launches nothing.
+    p = synth.make_custom("block_fp8", "none", 8, 256, 1024, seed=1, bias=False, residual=False)
+    with pytest.raises(lg.LinGemmError, match="staged"):
+        run(handle, p, "decode swap=1 split=1 reduce=twopass waves=16 unroll=2 rows=16 xs=1")
