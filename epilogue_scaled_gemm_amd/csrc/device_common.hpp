@@ -402,11 +402,18 @@ __device__ inline void epilogue_one(const Epi& e, int64_t m, int64_t n, AccT v) 
 
 // The epilogue operands of a 4-column run C[m][n0 .. n0+4), loaded ahead of
 // time (at kernel start) so the loads' latency overlaps the K loop instead of
-// following it.
+// following it.  Bias and residual stay as raw 16-bit pairs (low half first)
+// until the epilogue widens them: widening at load time would make the wave
+// wait for the loads right there.
 struct EpiPre4 {
   float sam;
-  float sb[4], bias[4], res[4];
+  float sb[4];
+  uint32_t bias[2], res[2];
 };
+// Value i of a raw pair array (bias or residual).
+template <bool F16> __device__ inline float pre_h(const uint32_t* w, int i) {
+  return h_to_f32<F16>((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+}
 
 template <bool F16>
 __device__ inline void epilogue_prefetch4(const Epi& e, int64_t m, int64_t n0, EpiPre4& p) {
@@ -414,7 +421,8 @@ __device__ inline void epilogue_prefetch4(const Epi& e, int64_t m, int64_t n0, E
   const bool full = (n0 + 4 <= e.N) && (e.N % 4 == 0) && (n0 % 4 == 0);
   p.sam = 1.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) p.sb[i] = 1.f, p.bias[i] = 0.f, p.res[i] = 0.f;
+  for (int i = 0; i < 4; ++i) p.sb[i] = 1.f;
+  p.bias[0] = p.bias[1] = p.res[0] = p.res[1] = 0u;  // +0
   if (e.raw) return;
   if (e.scale_mode == 1) {
     if (e.sa) p.sam = e.sa[mm];  // (no sa: the kernel derives it from its activations)
@@ -426,15 +434,18 @@ __device__ inline void epilogue_prefetch4(const Epi& e, int64_t m, int64_t n0, E
       for (int i = 0; i < 4; ++i) if (n0 + i < e.N) p.sb[i] = e.sb[n0 + i];
     }
   }
-  if (e.bias) {
-    if (full) load_h<4, F16>(e.bias + n0, p.bias);
-    else for (int i = 0; i < 4; ++i) if (n0 + i < e.N) p.bias[i] = h_to_f32<F16>(e.bias[n0 + i]);
-  }
-  if (e.residual) {
-    const uint16_t* rrow = e.residual + mm * e.N;
-    if (full) load_h<4, F16>(rrow + n0, p.res);
-    else for (int i = 0; i < 4; ++i) if (n0 + i < e.N) p.res[i] = h_to_f32<F16>(rrow[n0 + i]);
-  }
+  auto raw4 = [&](const uint16_t* row, uint32_t* w) {
+    if (full) {
+      const i32x2 b = *(const i32x2*)(row + n0);
+      w[0] = (uint32_t)b[0];
+      w[1] = (uint32_t)b[1];
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (n0 + i < e.N) w[i >> 1] |= (uint32_t)row[n0 + i] << (16 * (i & 1));
+    }
+  };
+  if (e.bias) raw4(e.bias, p.bias);
+  if (e.residual) raw4(e.residual + mm * e.N, p.res);
 }
 
 // Epilogue of a 4-column run from prefetched operands (same arithmetic and
@@ -454,8 +465,8 @@ __device__ inline void epilogue_run4_pre(const Epi& e, int64_t m, int64_t n0, co
   for (int i = 0; i < 4; ++i) {
     y[i] = (float)v[i];
     if (e.scale_mode == 1) y[i] *= p.sam * p.sb[i];
-    y[i] += p.bias[i];
-    y[i] = act_apply(e.act, y[i]) * e.alpha + p.res[i];
+    y[i] += pre_h<F16>(p.bias, i);
+    y[i] = act_apply(e.act, y[i]) * e.alpha + pre_h<F16>(p.res, i);
   }
   uint16_t* crow = (uint16_t*)e.C + m * e.N;
   if ((n0 + 4 <= e.N) && (e.N % 4 == 0) && (n0 % 4 == 0)) {

@@ -94,9 +94,7 @@ constexpr bool op_wave(bool swap, int w) { return swap && w >= 8 && w < 16; }
 //             hold copies of the same tokens, so per-lane widening repeats
 //             the same conversions up to 16 times; here each activation
 //             byte is widened once per wave.  Chunks outside the wave's
-//             range or past K are stored as zeros, so the weights need no
-//             zeroing: their products with a zero activation add nothing,
-//             and a weight row past N only feeds an output that is dropped.
+//             range or past K are stored as zeros.
 //  AM_QWIDEN  AM_WIDEN on bf16 activations X[M][K] with per-token dynamic
 //             e4m3 quantization fused in (the prologue fusion of the pages'
 //             input-side transforms): each wave loads the bf16 values of its
@@ -273,10 +271,10 @@ __device__ __forceinline__ void decode_body(
   // not needed.
   constexpr bool RA = XS || am_widen(AM);
   __shared__ AccT red[RA ? 1 : W][NTILE * 4][64];
-  // Epilogue operands per tile and lane: sa, sb[4], bias[4], residual[4],
-  // staged by the operand wave.
+  // Epilogue operands per tile and lane: sa, sb[4], then bias and residual
+  // as two raw 16-bit pairs each, staged by the operand wave.
   constexpr bool OPW = op_wave(SWAP, W);
-  constexpr int NOP = 13;
+  constexpr int NOP = 9;
   __shared__ float opnd[OPW ? NTILE : 1][NOP][64];
   __shared__ int arrival;
   // AM_QWIDEN: per-wave partial maxima and the scales of up to 16 tokens.
@@ -305,16 +303,24 @@ __device__ __forceinline__ void decode_body(
   const int first = beg + wave * per;
   const int my = max(0, min(per, end - first));  // steps of this wave
 
-  // Masked rows load a row this workgroup reads anyway (a cache hit, no
-  // extra HBM traffic) and are zeroed.
-  const uint8_t* wp[RT];
-  bool wrow[RT];
+  // Weight loads are buffer loads over this workgroup's rows [n0, nend)
+  // (at most 64 rows of at most 8 MiB): a lane's 16-byte chunk sits at
+  // wlb[rt] + st * STEPB (+16); rows past nend are out of range, and chunks
+  // past the end of a row and steps past the wave's range are given an
+  // out-of-range offset, so all of them read zeros without a memory access.
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(B + n0 * KB), (short)0, (int)((nend - n0) * KB), 0x00020000);
+  int wlb[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int64_t row = n0 + rt * 16 + l16;
-    wrow[rt] = row < nend;
-    wp[rt] = B + (wrow[rt] ? row : n0) * KB + g * 32;
-  }
+  for (int rt = 0; rt < RT; ++rt) wlb[rt] = (rt * 16 + l16) * (int)KB + g * 32;
+  auto wload = [&](int rt, int st, bool live) {
+    const int o0 = st * STEPB + g * 32;
+    const int b = wlb[rt] + st * STEPB;
+    const int off0 = live && o0 < KB ? b : 0x7FFFFFF0;
+    const int off1 = live && o0 + 16 < KB ? b + 16 : 0x7FFFFFF0;
+    return cat(__builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, off0, 0, 0)),
+               __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, off1, 0, 0)));
+  };
   const uint8_t* xp[NTT];
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt)
@@ -392,13 +398,8 @@ __device__ __forceinline__ void decode_body(
     const int t = t0 + u;
     const bool live = t < my;
     const int st = min(first + (live ? t : 0), total_steps - 1);
-    const int64_t o0 = (int64_t)st * STEPB + g * 32, o1 = o0 + 16;
-    const int64_t c0 = (o0 < KB ? o0 : KB - 16) - g * 32;
-    const int64_t c1 = (o1 < KB ? o1 : KB - 16) - g * 32;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-      wb[u][rt] = cat(ld16(wp[rt] + c0, live && o0 < KB && wrow[rt]),
-                      ld16(wp[rt] + c1, live && o1 < KB && wrow[rt]));
+    for (int rt = 0; rt < RT; ++rt) wb[u][rt] = wload(rt, st, live);
     if constexpr (MX) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) msc[u][rt] = *(const uint16_t*)(msp[rt] + (int64_t)st * 8);
@@ -407,7 +408,16 @@ __device__ __forceinline__ void decode_body(
   // Direct-to-LDS activation loads of step u: one per 64 chunks, chunk q
   // (token q / (XSB/16), piece q % (XSB/16)) landing at byte 16 q of the
   // step's slice; lanes past the last chunk get an out-of-range offset (no
-  // access).
+  // access).  XSB / 16 divides 64, so chunk 64 i + lane is token
+  // i * 64 / (XSB/16) + lane / (XSB/16), piece lane % (XSB/16), and the
+  // piece's swizzled position depends on i only through its parity: the lane
+  // part of the offset is computed once, for even and for odd i.
+  constexpr int CPT = XSB / 16, TPI = 64 / CPT;
+  static_assert(64 % CPT == 0 && (!XSW || TPI == 8), "staged chunk layout");
+  int xlb[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+    xlb[p] = (lane / CPT) * (int)(KB * XR) + (((lane % CPT) ^ xsw(lane / CPT + p * TPI)) << 4);
   auto stage_step = [&](int t0, int u) {
     const int t = t0 + u;
     const bool live = t < my;
@@ -416,10 +426,9 @@ __device__ __forceinline__ void decode_body(
     xok[u][0] = live && (o0 < KB);
     xok[u][1] = live && (o0 + 16 < KB);
     for (int i = 0; i * 64 < xs_chunks; ++i) {
-      const int q = i * 64 + lane;
-      const int tq = q / (XSB / 16), pq = (q - tq * (XSB / 16)) ^ xsw(tq);
-      const int voff = q < xs_chunks ? (int)(tq * KB * XR + (int64_t)st * XSB + pq * 16)
-                                     : 0x7FFFFFF0;
+      const int voff = i * 64 + lane < xs_chunks
+                           ? xlb[i & 1] + i * TPI * (int)(KB * XR) + st * XSB
+                           : 0x7FFFFFF0;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xrs, (lds_void*)(xsl + (int64_t)u * XSL + i * 1024), 16, voff, 0, 0, 0);
     }
@@ -445,9 +454,10 @@ __device__ __forceinline__ void decode_body(
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u;
       const bool live = t < my;
-      // Steps past this wave's range re-read a step inside the row (its
-      // first, clamped to the last step of K) and are zeroed; chunks past the
-      // end of the row re-read the row's last 16 bytes and are zeroed.
+      // Per-lane activation loads: steps past this wave's range re-read a
+      // step inside the row (its first, clamped to the last step of K) and
+      // are zeroed; chunks past the end of the row re-read the row's last 16
+      // bytes and are zeroed.
       const int st = min(first + (live ? t : 0), total_steps - 1);
       const int64_t off = (int64_t)st * STEPB;
       const int64_t o0 = off + g * 32, o1 = o0 + 16;
@@ -457,9 +467,7 @@ __device__ __forceinline__ void decode_body(
       const int64_t c1 = (o1 < KB ? o1 : KB - 16) - g * 32;
       if (part != 2 && !XS) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          wb[u][rt] = WD ? cat(*(const i32x4*)(wp[rt] + c0), *(const i32x4*)(wp[rt] + c1))
-                         : cat(ld16(wp[rt] + c0, ok0 && wrow[rt]), ld16(wp[rt] + c1, ok1 && wrow[rt]));
+        for (int rt = 0; rt < RT; ++rt) wb[u][rt] = wload(rt, st, live);
       }
       if constexpr (MX && !XS) {
 #pragma unroll
@@ -752,10 +760,11 @@ __device__ __forceinline__ void decode_body(
         epilogue_prefetch4<F16>(e, (q % NTT) * 16 + l16, nr, p);
         opnd[q][0][lane] = p.sam;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          opnd[q][1 + i][lane] = p.sb[i];
-          opnd[q][5 + i][lane] = p.bias[i];
-          opnd[q][9 + i][lane] = p.res[i];
+        for (int i = 0; i < 4; ++i) opnd[q][1 + i][lane] = p.sb[i];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          opnd[q][5 + i][lane] = __uint_as_float(p.bias[i]);
+          opnd[q][7 + i][lane] = __uint_as_float(p.res[i]);
         }
       }
     }
@@ -807,10 +816,11 @@ __device__ __forceinline__ void decode_body(
     } else {
       p.sam = opnd[q][0][lane];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p.sb[j] = opnd[q][1 + j][lane];
-        p.bias[j] = opnd[q][5 + j][lane];
-        p.res[j] = opnd[q][9 + j][lane];
+      for (int j = 0; j < 4; ++j) p.sb[j] = opnd[q][1 + j][lane];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        p.bias[j] = __float_as_uint(opnd[q][5 + j][lane]);
+        p.res[j] = __float_as_uint(opnd[q][7 + j][lane]);
       }
     }
     if constexpr (DQ && !BLOCK) p.sam = sal[min(m, M - 1)];
