@@ -270,7 +270,10 @@ __device__ __forceinline__ void decode_body(
   // with it by then; slices are sized to hold them), so the static array is
   // not needed.
   constexpr bool RA = XS || am_widen(AM);
-  __shared__ AccT red[RA ? 1 : W][NTILE * 4][64];
+  __shared__ __align__(16) AccT red[RA ? 1 : W][NTILE * 64 * 4];
+  // A lane's four partial sums of a tile sit together (one 16-byte LDS
+  // access each way): element r of tile q, lane l at (q * 64 + l) * 4 + r.
+  typedef AccT AccT4 __attribute__((ext_vector_type(4)));
   // Epilogue operands per tile and lane: sa, sb[4], then bias and residual
   // as two raw 16-bit pairs each, staged by the operand wave.
   constexpr bool OPW = op_wave(SWAP, W);
@@ -773,14 +776,15 @@ __device__ __forceinline__ void decode_body(
   // In-workgroup reduction, in wave order; wave w then owns tiles
   // q = w, w + W, ... (q = rt * NTT + tt) for the rest of the kernel.
   if (!opw) {
+    AccT* mine = RA ? (AccT*)(XS ? xsl : wdl) : &red[wave][0];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          (RA ? (AccT*)(XS ? xsl : wdl) : &red[wave][0][0])[((rt * NTT + tt) * 4 + r) * 64 + lane] =
-              (AccT)acc[rt][tt][r];
+      for (int tt = 0; tt < NTT; ++tt) {
+        const C& a = acc[rt][tt];
+        *(AccT4*)(mine + ((rt * NTT + tt) * 64 + lane) * 4) =
+            AccT4{(AccT)a[0], (AccT)a[1], (AccT)a[2], (AccT)a[3]};
+      }
   }
   __syncthreads();
 
@@ -828,17 +832,16 @@ __device__ __forceinline__ void decode_body(
     epilogue_run4_pre<F16>(e, m, nr, v, p);
   };
   auto reduce_tile = [&](int q, AccT* v) {
+    auto part = [&](int w) {
+      return *(const AccT4*)((RA ? (const AccT*)(dq_lds + (int64_t)w * (XS ? (int64_t)XSS : WSS))
+                                 : &red[w][0]) +
+                             (q * 64 + lane) * 4);
+    };
+    AccT4 s = part(0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      auto part = [&](int w) {
-        return (RA ? (const AccT*)(dq_lds + (int64_t)w * (XS ? (int64_t)XSS : WSS)) : &red[w][0][0])
-            [(q * 4 + r) * 64 + lane];
-      };
-      AccT s = part(0);
+    for (int w = 1; w < W; ++w) s += part(w);
 #pragma unroll
-      for (int w = 1; w < W; ++w) s += part(w);
-      v[r] = s;
-    }
+    for (int r = 0; r < 4; ++r) v[r] = s[r];
   };
 
   if (split == 1) {
