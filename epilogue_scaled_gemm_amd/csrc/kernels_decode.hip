@@ -13,8 +13,8 @@
 //  * A workgroup owns 16*rows weight rows and a slice of K; its W waves split
 //    that slice into contiguous runs of 128-byte steps (in-workgroup
 //    split-K), so each weight byte is loaded by exactly one lane, straight
-//    from HBM into registers (no LDS staging: there is no reuse to stage
-//    for).  Every lane loads 32 contiguous bytes per step; 4 lanes cover a
+//    from HBM into registers with buffer loads over the workgroup's rows (no
+//    LDS staging: there is no reuse to stage for).  Every lane loads 32 contiguous bytes per step; 4 lanes cover a
 //    128-byte line; each activation slice feeds all 16*rows weight rows.
 //  * A wave issues the loads of up to U steps at once (U * 2 KiB of weight),
 //    then consumes them; with the wave counts used, every weight byte of the
@@ -609,8 +609,8 @@ __device__ __forceinline__ void decode_body(
   };
 
   // The first batch is issued before anything else, so the weight stream
-  // starts at once (a wave with no steps loads zeroed re-reads, which add
-  // nothing).
+  // starts at once (a wave with no steps issues out-of-range weight loads,
+  // which read zeros and add nothing).
   // Without the operand wave, each swap wave prefetches the operands of the
   // tiles it will finish (q = wave, wave + W, ...) right behind its first
   // batch.
