@@ -1014,11 +1014,29 @@ __global__ __launch_bounds__(256) void splitk_reduce(const void* __restrict__ ws
   const int64_t n = (idx - m * nq) * 4;
   if (m >= e.M) return;
   AccT v[4] = {0, 0, 0, 0};
-  for (int q = 0; q < split; ++q) {
-    const AccT* row = wsa + ((int64_t)q * e.M + m) * e.N;
+  const int64_t slice = e.M * e.N;
+  const AccT* col = wsa + m * e.N + n;
+  if (n + 4 <= e.N && e.N % 4 == 0) {
+    // 16-byte loads, four slices in flight at a time; the sums still run in
+    // slice order.
+    typedef AccT AccT4 __attribute__((ext_vector_type(4)));
+    AccT4 s = {0, 0, 0, 0};
+    int q = 0;
+    for (; q + 4 <= split; q += 4) {
+      AccT4 p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (n + i < e.N) v[i] += row[n + i];
+      for (int k = 0; k < 4; ++k) p[k] = *(const AccT4*)(col + (q + k) * slice);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s += p[k];
+    }
+    for (; q < split; ++q) s += *(const AccT4*)(col + q * slice);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = s[i];
+  } else {
+    for (int q = 0; q < split; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (n + i < e.N) v[i] += col[q * slice + i];
   }
   epilogue_run<4, QTraits<QK>::out_f16>(e, m, n, v);
 }
