@@ -166,7 +166,11 @@ const char *lin_gemm_last_error(lin_gemm_t h);
 /* Force a variant for every following lin_gemm_run on h (testing and the
  * offline sweep); NULL or "" returns to the table.  Spec syntax, e.g.
  *   "tile bm=128 bn=128"   "decode swap=1 split=4 reduce=lastwg waves=4"
- * Returns LIN_ERR_CONFIG if the spec does not parse. */
+ * Returns LIN_ERR_CONFIG if the spec does not parse or names a shape that
+ * is not compiled.  A variant that does not apply to a later call's sizes
+ * or quant mode (for example a decode shape compiled only with staged
+ * activations, forced at a token count those builds do not cover) makes
+ * that call fail with LIN_ERR_UNSUPPORTED before anything is enqueued. */
 int lin_gemm_set_force(lin_gemm_t h, const char *spec);
 
 /* Write into buf (NUL-terminated, at most buflen bytes) the variant that
