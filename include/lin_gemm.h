@@ -170,7 +170,7 @@ const char *lin_gemm_last_error(lin_gemm_t h);
  * is not compiled.  A variant that does not apply to a later call's sizes
  * or quant mode (for example a decode shape compiled only with staged
  * activations, forced at a token count those builds do not cover) makes
- * that call fail with LIN_ERR_UNSUPPORTED before anything is enqueued. */
+ * that call fail, with LIN_ERR_UNSUPPORTED and no kernel launched. */
 int lin_gemm_set_force(lin_gemm_t h, const char *spec);
 
 /* Write into buf (NUL-terminated, at most buflen bytes) the variant that
