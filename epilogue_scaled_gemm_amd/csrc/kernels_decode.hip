@@ -1256,7 +1256,7 @@ hipError_t launch_mx(const Variant& v, const Call& c, int split, hipStream_t s) 
   X(QK_FP8, 2, 16, 1, 2) X(QK_FP8, 1, 16, 1, 2) X(QK_BF16, 2, 16, 1, 2) X(QK_I8, 2, 16, 1, 2) \
   X(QK_FP8_BLOCK, 2, 16, 1, 2) X(QK_FP16, 2, 16, 1, 2) X(QK_FP8, 2, 16, 2, 2)             \
   X(QK_BF16, 2, 16, 2, 2) X(QK_FP16, 2, 16, 2, 2) X(QK_FP8_BLOCK, 2, 16, 2, 1)          \
-  X(QK_FP8_BLOCK, 2, 12, 2, 1)
+  X(QK_FP8_BLOCK, 2, 12, 2, 1) X(QK_FP8_BLOCK, 2, 8, 1, 4)
 
 // Whether the plain build of this decode shape exists (for every weight
 // format).

@@ -55,6 +55,11 @@ XS_SHAPES = [(8, 1, 12), (8, 1, 16), (8, 2, 16), (8, 4, 12), (8, 4, 24), (12, 1,
              (12, 2, 16)]
 XS_CANDIDATES = [f"decode swap=1 split=1 reduce=twopass waves={w} unroll={u} rows={r} xs=1"
                  for w, u, r in XS_SHAPES]
+# Staged activations with K split across workgroups: 64-row workgroups
+# read a quarter of the tokens' activation bytes each, which pays where K
+# is long (block e4m3 at K = 12288, 17-32 tokens); swept where K >= 8192.
+XS_SPLIT_CANDIDATES = [f"decode swap=1 split={sp} reduce=twopass waves={w} unroll={u} rows={r} xs=1"
+                       for sp in (2, 4) for w, u, r in ((8, 1, 64), (16, 1, 32), (8, 1, 32))]
 # Widened e4m3 activations (xs=2; up to 16 tokens; elsewhere the same
 # variant falls back to staging).
 WD_SHAPES = [(8, 1, 12), (8, 2, 12), (8, 4, 12), (8, 1, 16), (8, 2, 16), (12, 1, 12),
@@ -256,6 +261,8 @@ def sweep(workloads, out_path, reps, log=print, max_m=None, all_m=False, dynamic
             cands = DECODE_CANDIDATES if M <= 32 else TILE_CANDIDATES + SK_CANDIDATES
             if p.quant in ("fp8_dynamic", "mxfp4", "w8a8_int8", "block_fp8", "bf16", "fp16"):
                 cands = cands + XS_CANDIDATES
+                if p.K >= 8192:
+                    cands = cands + XS_SPLIT_CANDIDATES
             if p.quant in ("fp8_dynamic", "block_fp8") and M <= 16:
                 cands = cands + WD_CANDIDATES
             # Warm every candidate first (the handle's split-K workspace only

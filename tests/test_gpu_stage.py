@@ -126,6 +126,43 @@ def test_staged_two_token_tiles(handle, case):
         assert_close(decode_out(C1, quant), ref, f"staged {quant} {M}x{N}x{K} [{spec}]")
 
 
+# Staged activations with K split across workgroups (17..32 tokens): the
+# products and their order are those of the unstaged variant with the same
+# split and reduction, so the outputs must be identical bit for bit (except
+# under the atomic reduction, whose order of arrival is not fixed).  Block
+# e4m3 at the workload's own size (N = 4096, K = 12288) and a small ragged
+# one; fp8 per-channel and bf16 with a K tail.
+SPLIT = [("block_fp8", "none", 32, 4096, 12288, False, True),
+         ("block_fp8", "silu", 19, 384, 3072, True, False),
+         ("fp8_dynamic", "gelu_tanh", 25, 528, 4112, True, True),
+         ("bf16", "none", 17, 272, 8200, True, False)]
+SPLIT_SPECS = [f"decode swap=1 split={sp} reduce={red} waves=8 unroll=1 rows=64"
+               for sp in (2, 4) for red in ("twopass", "lastwg", "atomic")] + \
+              ["decode swap=1 split=2 reduce=twopass waves=16 unroll=1 rows=32",
+               "decode swap=1 split=4 reduce=twopass waves=8 unroll=1 rows=32"]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=[f"{c[0]}-M{c[2]}-N{c[3]}-K{c[4]}" for c in SPLIT])
+def test_staged_split_k_two_token_tiles(handle, case):
+    quant, act, M, N, K, b, r = case
+    p = synth.make_custom(quant, act, M, N, K, seed=13 * M + N, bias=b, residual=r)
+    ref, _ = oracle.linear(quant, act, p.A, p.B, sa=p.sa, sb=p.sb, bias=p.bias,
+                           residual=p.residual, alpha=p.alpha)
+    staged = 0
+    for spec in SPLIT_SPECS:
+        handle.set_force(spec + " xs=1")
+        used = "xs=1" in handle.describe(quant, M, N, K)
+        handle.set_force(None)
+        staged += used
+        print(f"[stage-split] {quant} {M}x{N}x{K} {spec} staged={used}", flush=True)
+        C1 = run(handle, p, spec + " xs=1")
+        if "atomic" not in spec:
+            C0 = run(handle, p, spec)
+            assert torch.equal(C1, C0), f"staged vs direct differ [{spec}]"
+        assert_close(decode_out(C1, quant), ref, f"staged {quant} {M}x{N}x{K} [{spec}]")
+    assert staged >= 2, "the staged mode was not used"
+
+
 # Widened e4m3 activations (xs=2): each wave widens its K range's
 # activations once into LDS; the fragments, products and their order are
 # those of the same variant without it, so the outputs must be identical bit
