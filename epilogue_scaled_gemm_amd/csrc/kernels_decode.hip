@@ -438,20 +438,13 @@ __device__ __forceinline__ void decode_body(
   };
   auto load_batch = [&](int t0, int part = 0) {
     if constexpr (XS) {
-      // A one-step batch issues its activation loads before its weights:
+      // A batch issues its steps' activation loads before their weights:
       // loads complete in issue order, so the staged fragments are read
-      // while the weights are still in flight.  Longer batches keep
-      // step order (weights, then activations, per step) and wait for all.
-      if constexpr (U == 1) {
-        stage_step(t0, 0);
-        load_weights(t0, 0);
-      } else {
+      // while the weights are still in flight.
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          load_weights(t0, u);
-          stage_step(t0, u);
-        }
-      }
+      for (int u = 0; u < U; ++u) stage_step(t0, u);
+#pragma unroll
+      for (int u = 0; u < U; ++u) load_weights(t0, u);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -533,12 +526,13 @@ __device__ __forceinline__ void decode_body(
       }
     }
   };
-  // A staged batch: its fragments once its direct-to-LDS loads have landed
-  // (one-step batches: with at most the step's weight loads, two per row
-  // tile plus the MXFP4 scale load, still in flight behind them).
+  // A staged batch: its fragments once its direct-to-LDS loads have landed,
+  // with at most the batch's weight loads (two per row tile and step, plus
+  // the MXFP4 scale load) still in flight behind them.
   auto stage_batch = [&]() {
     if constexpr (XS) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(U == 1 ? (MX ? 3 : 2) * RT : 0));
+      static_assert(U * (MX ? 3 : 2) * RT <= 63, "vmcnt range");
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(U * (MX ? 3 : 2) * RT));
 #pragma unroll
       for (int u = 0; u < U; ++u) read_staged(u);
     }

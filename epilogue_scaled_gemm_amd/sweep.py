@@ -90,9 +90,11 @@ def _dev(torch, a):
 
 def capture_variant(torch, h, p, ops, Bs, spec):
     """A HIP graph of one call of `spec` per weight copy (rotating B), and its
-    output buffer (keep it while the graph is replayed: entering another
-    capture empties the allocator cache, which would release it).  Raises
-    LinGemmError if the variant does not apply."""
+    output buffer.  Keep the output and every operand (ops, Bs) alive while
+    the graph is replayed: entering another capture empties the allocator
+    cache, which would hand their memory back to the driver, and a replay
+    would then access freed memory.  Raises LinGemmError if the variant does
+    not apply."""
     h.set_force(spec)
     try:
         C = torch.empty((p.M, p.N), dtype=torch.int16, device="cuda")
