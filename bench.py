@@ -548,8 +548,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU; collectives and multi-GPU runs are not "
-              f"part of it (asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no collectives or multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
 
     import torch
