@@ -15,8 +15,9 @@ over a rotation of weight copies larger than the 256 MB MALL.
 
 --all-m sweeps every token count 1..32 of the decode workloads (not only the
 workloads' own list); --ms sweeps a given token list instead (each swept count
-then covers the counts above the previous one up to itself); --merge with --emit-inc replaces only the overlapping entries of the
-existing include; --dynamic also times lin_gemm_run_dynamic with the
+then covers the counts above the previous one up to itself); --merge with
+--emit-inc cuts the existing include's entries of the same shape around the
+new token ranges and keeps the rest; --dynamic also times lin_gemm_run_dynamic with the
 winning decode variant with and without the quantization prologue (dq=1)
 and keeps the prologue where it is faster; --emit-inc writes the measured
 entries as the C++ include that the library compiles in as its built-in
@@ -195,34 +196,66 @@ def sparse_ranges(entries):
     return out
 
 
-def merge_inc(path, new_lines, log=print):
-    """Rewrite the table include at `path`: the new entries replace existing
-    ones of the same (quant, N, K) whose token ranges overlap them; the
-    other existing entries stay, in their order, before the new ones."""
+def merge_lines(old, new_lines):
+    """Table lines after merging: an existing entry of the same (quant, N, K)
+    keeps the token counts no new entry covers (its range is cut, or split in
+    two, around the new ranges, so coverage never shrinks); the new entries
+    follow the kept ones."""
     def key(line):
         f = line.split("#", 1)[0].split()
         if len(f) < 6:
             return None
         hi = 1 << 40 if f[2] == "*" else int(f[2])
-        return f[0], int(f[1]), hi, f[3], f[4]
-    text = open(path).read() if os.path.exists(path) else ""
-    body = text.split('R"TABLE(', 1)[1].split(')TABLE"', 1)[0] if 'R"TABLE(' in text else ""
-    old = [l for l in body.splitlines() if l.strip() and not l.lstrip().startswith("#")]
+        return f[0], int(f[1]), hi, f[3], f[4], f
+
     new_keys = [key(l) for l in new_lines]
     kept = []
     for l in old:
         k = key(l)
-        if k and any(k[0] == n[0] and k[3] == n[3] and k[4] == n[4] and k[1] <= n[2] and n[1] <= k[2]
-                     for n in new_keys):
+        if not k:
+            kept.append(l)
             continue
-        kept.append(l)
+        pieces = [(k[1], k[2])]
+        for n in new_keys:
+            if not n or (n[0], n[3], n[4]) != (k[0], k[3], k[4]):
+                continue
+            cut = []
+            for lo, hi in pieces:
+                if n[2] < lo or n[1] > hi:
+                    cut.append((lo, hi))
+                    continue
+                if lo < n[1]:
+                    cut.append((lo, n[1] - 1))
+                if n[2] < hi:
+                    cut.append((n[2] + 1, hi))
+            pieces = cut
+        f = k[5]
+        rest = l.split("#", 1)
+        spec = " ".join(f[5:])
+        note = ("   #" + rest[1]) if len(rest) > 1 else ""
+        for lo, hi in pieces:
+            if (lo, hi) == (k[1], k[2]):
+                kept.append(l)
+            else:
+                hs = "*" if hi == 1 << 40 else str(hi)
+                kept.append(f"{f[0]:<12} {lo:<5} {hs:<5} {f[3]:<6} {f[4]:<6} {spec}{note}")
+    return kept + list(new_lines)
+
+
+def merge_inc(path, new_lines, log=print):
+    """Rewrite the table include at `path` with `merge_lines` of its entries
+    and the new ones."""
+    text = open(path).read() if os.path.exists(path) else ""
+    body = text.split('R"TABLE(', 1)[1].split(')TABLE"', 1)[0] if 'R"TABLE(' in text else ""
+    old = [l for l in body.splitlines() if l.strip() and not l.lstrip().startswith("#")]
+    lines = merge_lines(old, new_lines)
     with open(path, "w") as f:
         f.write("// Measured entries of the built-in variant table, written by\n"
                 "// epilogue_scaled_gemm_amd.sweep (graph replay over rotating weight\n"
                 "// copies on an MI355X); microseconds per call in the comments.\n"
                 "R\"TABLE(\n# quant        m_lo  m_hi  N      K      variant\n"
-                + "\n".join(kept + list(new_lines)) + "\n)TABLE\"\n")
-    log(f"merged {len(new_lines)} entries into {path} ({len(kept)} kept)")
+                + "\n".join(lines) + "\n)TABLE\"\n")
+    log(f"merged {len(new_lines)} entries into {path} ({len(lines) - len(new_lines)} kept or cut)")
 
 
 def sweep(workloads, out_path, reps, log=print, max_m=None, all_m=False, dynamic=False,
@@ -365,8 +398,8 @@ def main():
     ap.add_argument("--quant", default=None,
                     help="run the workloads in this quant mode (same draws), e.g. fp16")
     ap.add_argument("--merge", action="store_true",
-                    help="with --emit-inc: replace only the overlapping entries of the existing "
-                         "include, keep the rest")
+                    help="with --emit-inc: cut the existing include's entries of the same shape "
+                         "around the new token ranges, keep the rest")
     ap.add_argument("--ms", default=None,
                     help="token counts to sweep instead of each workload's own list, e.g. "
                          "64,128,256,512,1024,2048")
