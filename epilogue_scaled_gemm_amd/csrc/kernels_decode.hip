@@ -354,6 +354,7 @@ __device__ __forceinline__ void decode_body(
   // the 32 lanes of two lane groups) then hit distinct bank groups instead
   // of the same few (token rows are 128 bytes apart).
   constexpr bool XSW = XSB == 128;
+  constexpr bool XS_FIRST = U == 1 || W >= 8;  // activation loads first (below)
   auto xsw = [](int t) { return XSW ? (t & 7) ^ (((t >> 3) & 1) * 7) : 0; };
   const int XSL = (xs_chunks + 63) / 64 * 1024;
   // A wave's slice: U steps, and at least its NTILE KiB of partial sums.
@@ -440,11 +441,22 @@ __device__ __forceinline__ void decode_body(
     if constexpr (XS) {
       // A batch issues its steps' activation loads before their weights:
       // loads complete in issue order, so the staged fragments are read
-      // while the weights are still in flight.
+      // while the weights are still in flight.  With 4 waves a batch spans
+      // more of K, and its first weights would wait behind all of its
+      // activation loads (1-2% slower for int8 at 4-16 tokens): those
+      // batches keep step order and wait for everything.
+      if constexpr (XS_FIRST) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) stage_step(t0, u);
+        for (int u = 0; u < U; ++u) stage_step(t0, u);
 #pragma unroll
-      for (int u = 0; u < U; ++u) load_weights(t0, u);
+        for (int u = 0; u < U; ++u) load_weights(t0, u);
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          load_weights(t0, u);
+          stage_step(t0, u);
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -526,13 +538,14 @@ __device__ __forceinline__ void decode_body(
       }
     }
   };
-  // A staged batch: its fragments once its direct-to-LDS loads have landed,
-  // with at most the batch's weight loads (two per row tile and step, plus
-  // the MXFP4 scale load) still in flight behind them.
+  // A staged batch: its fragments once its direct-to-LDS loads have landed;
+  // issued first, they leave at most the batch's weight loads (two per row
+  // tile and step, plus the MXFP4 scale load) in flight behind them, else
+  // the batch waits for all of its loads.
   auto stage_batch = [&]() {
     if constexpr (XS) {
-      static_assert(U * (MX ? 3 : 2) * RT <= 63, "vmcnt range");
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(U * (MX ? 3 : 2) * RT));
+      static_assert(!XS_FIRST || U * (MX ? 3 : 2) * RT <= 63, "vmcnt range");
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(XS_FIRST ? U * (MX ? 3 : 2) * RT : 0));
 #pragma unroll
       for (int u = 0; u < U; ++u) read_staged(u);
     }
